@@ -1,0 +1,265 @@
+// full_decode.hip -- full-attention decode over the contiguous pool, split
+// over key chunks, with a log-sum-exp combine (bf16 storage, MFMA).
+//
+// colibri "MiMo-V2.6 (Xiaomi)", "System One mode and prompt reuse": full
+// layers keep K/V rows by position.  gaudi-cookbook "MiMo-V2.6-Flash on
+// Gaudi 2", "What was built" and "What it taught about Gaudi": decode runs as
+// per-block partials, and a sink must count once per sequence, not once per
+// block -- so partials carry no sink and the combine adds it exactly once.
+// Full layers of MiMo have no sink (colibri "What the engine implements"),
+// but one may be passed.
+//
+// Pass 1: one workgroup per (sequence, KV head, chunk of `chunk` keys); wave
+// w takes a contiguous quarter of the chunk in steps of 32 keys.  The G query
+// heads of the group are the 16 B columns of S^T = K Q^T
+// (v_mfma_f32_16x16x32_bf16, K rows loaded from HBM straight into the A
+// operand); an online softmax in log2 units; O^T += V^T P^T
+// (v_mfma_f32_16x16x16_bf16, P as bf16 hi + lo, V transposed through a
+// per-wave LDS tile).  The four waves merge in LDS and write one
+// (m, l, acc[128]) fp32 partial per (sequence, head, chunk).
+// Pass 2: one wave per (sequence, head) merges the chunks:
+//   M = max m_c,  Z = sum 2^(m_c - M) l_c (+ 2^(sink - M) once),
+//   o = value_scale * sum 2^(m_c - M) acc_c / Z.
+// HBM-bound: every K/V row is read exactly once.
+#include "hsw_device.h"
+#include "hsw_launch.h"
+
+namespace hsw {
+namespace {
+
+constexpr int DQK = 192, DV = 128;
+constexpr int STEPS = DQK / 32;
+constexpr int DT = DV / 16;
+constexpr int KS = 32;                 // keys per wave step
+constexpr int VT_STRIDE = KS + 4;      // bf16 per transposed V row
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int full = (total / 8) * 8;
+    if (bid >= full) return bid;
+    return (bid % 8) * (total / 8) + bid / 8;
+}
+
+struct StepRegs {
+    u32x4 k[2][STEPS];
+    u32x4 v[8];
+};
+
+template <int G>
+__global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vt[4 * DV * VT_STRIDE];
+    __shared__ float red_m[4][16], red_l[4][16];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int quad = lane >> 4, col = lane & 15;
+    const int total = a.n_seqs * a.hkv * a.n_chunks;
+    const int bid = xcd_remap(blockIdx.x, total);
+    const int c = bid % a.n_chunks;
+    const int g = (bid / a.n_chunks) % a.hkv;
+    const int s = bid / (a.n_chunks * a.hkv);
+
+    const int64_t L = a.ctx_len[s];
+    const int64_t c0 = (int64_t)c * a.chunk;
+    if (c0 >= L) return;
+    const int64_t base = a.seq_base[s];
+    const int per_wave = a.chunk / 4;
+    const int64_t w0 = c0 + (int64_t)w * per_wave;
+    int64_t w1 = w0 + per_wave;
+    if (w1 > L) w1 = L;
+    if (base + w1 > a.pool_rows) w1 = a.pool_rows - base;  // never read past the pool
+    if (base < 0) w1 = w0;                                   // nor before it
+    const int nsteps = w1 > w0 ? (int)((w1 - w0 + KS - 1) / KS) : 0;
+
+    const uint16_t *Q = (const uint16_t *)a.q + ((int64_t)s * a.hq + g * G) * DQK;
+    const uint16_t *Kp = (const uint16_t *)a.k_main;
+    const uint16_t *Vp = (const uint16_t *)a.v_main;
+    u32x4 qb[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st)
+        qb[st] = col < G ? ld16(Q + col * DQK + 32 * st + 8 * quad) : u32x4{0, 0, 0, 0};
+
+    auto load_step = [&](int i, StepRegs &r) {
+        const int64_t k0 = w0 + (int64_t)i * KS;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            int64_t key = k0 + 16 * kt + col;
+            bool ok = key < w1;
+            const uint16_t *src = Kp + ((base + key) * a.hkv + g) * (int64_t)DQK + 8 * quad;
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) r.k[kt][st] = ok ? ld16(src + 32 * st) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int cc = it * 64 + lane;
+            int64_t key = k0 + (cc >> 4);
+            r.v[it] = key < w1 ? ld16(Vp + ((base + key) * a.hkv + g) * (int64_t)DV + 8 * (cc & 15))
+                               : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    uint16_t *vtw = vt + w * DV * VT_STRIDE;
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0, 0, 0, 0};
+    float m = -INFINITY, l = 0.0f;
+    const float scale2 = a.scale * kLog2e;
+
+    StepRegs cur;
+    for (int i = 0; i < nsteps; ++i) {
+        load_step(i, cur);
+        const int64_t k0 = w0 + (int64_t)i * KS;
+        f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) sacc[kt] = mfma_16x16x32_bf16(cur.k[kt][st], qb[st], sacc[kt]);
+        // V^T of this step into the wave's LDS tile (DS ops of one wave run
+        // in order, so the reads below see these writes and the writes of the
+        // next step come after these reads).
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int cc = it * 64 + lane, key = cc >> 4, dv0 = 8 * (cc & 15);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                uint32_t word = cur.v[it][e >> 1];
+                vtw[(dv0 + e) * VT_STRIDE + key] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        float sv[8], mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int64_t key = k0 + 16 * kt + 4 * quad + j;
+                float v = key < w1 ? sacc[kt][j] * scale2 : -INFINITY;
+                sv[4 * kt + j] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = quad_max(mx);
+        float mn = fmaxf(m, mx);
+        float mu = mn == -INFINITY ? 0.0f : mn;
+        float corr = exp2f(m - mu);
+        float pv[8], ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pv[e] = exp2f(sv[e] - mu);
+            ps += pv[e];
+        }
+        ps = quad_sum(ps);
+        l = l * corr + ps;
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= corr;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            u32x2 hi, lo;
+            split_hi_lo(pv + 4 * kt, hi, lo);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                u32x2 av = *reinterpret_cast<const u32x2 *>(vtw + (16 * dt + col) * VT_STRIDE + 16 * kt + 4 * quad);
+                oacc[dt] = mfma_16x16x16_bf16(av, hi, oacc[dt]);
+                oacc[dt] = mfma_16x16x16_bf16(av, lo, oacc[dt]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // Merge the four waves of this chunk.
+    if (quad == 0) {
+        red_m[w][col] = m;
+        red_l[w][col] = l;
+    }
+    __syncthreads();  // all waves done with their V tiles: reuse vt for partials
+    float *opart = reinterpret_cast<float *>(vt);  // [4][16][DV]
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4 *>(opart + (w * 16 + col) * DV + 16 * dt + 4 * quad) = oacc[dt];
+    __syncthreads();
+    float *ws_ml = (float *)a.ws;
+    float *ws_acc = ws_ml + ((2 * (int64_t)a.n_seqs * a.hq * a.n_chunks + 3) & ~(int64_t)3);
+    for (int idx = threadIdx.x; idx < G * DV / 4; idx += kThreads) {
+        int h = idx / (DV / 4), d4 = 4 * (idx % (DV / 4));
+        float mc = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+        float mu = mc == -INFINITY ? 0.0f : mc;
+        f32x4 o = f32x4{0, 0, 0, 0};
+        float lc = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            float f = exp2f(red_m[ww][h] - mu);
+            o += f * *reinterpret_cast<const f32x4 *>(opart + (ww * 16 + h) * DV + d4);
+            lc += f * red_l[ww][h];
+        }
+        int64_t slot = ((int64_t)s * a.hq + g * G + h) * a.n_chunks + c;
+        *reinterpret_cast<f32x4 *>(ws_acc + slot * DV + d4) = o;
+        if (d4 == 0) {
+            ws_ml[2 * slot] = mc;
+            ws_ml[2 * slot + 1] = lc;
+        }
+    }
+}
+
+// One wave per (sequence, q head); lane owns value dims 2*lane, 2*lane+1.
+__global__ __launch_bounds__(kThreads) void full_decode_combine_kernel(AttnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (wid >= (int64_t)a.n_seqs * a.hq) return;
+    const int s = (int)(wid / a.hq), h = (int)(wid % a.hq);
+    const int64_t L = a.ctx_len[s];
+    int64_t nc64 = (L + a.chunk - 1) / a.chunk;
+    const int nc = (int)(nc64 < a.n_chunks ? nc64 : a.n_chunks);  // ctx_len beyond max_ctx is clipped
+    const float *ws_ml = (const float *)a.ws;
+    const float *ws_acc = ws_ml + ((2 * (int64_t)a.n_seqs * a.hq * a.n_chunks + 3) & ~(int64_t)3);
+    const int64_t slot0 = wid * a.n_chunks;
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, ws_ml[2 * (slot0 + c)]);
+    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+    M = fmaxf(M, sink2);
+    const float mu = M == -INFINITY ? 0.0f : M;
+    float z = a.sinks ? exp2f(sink2 - mu) : 0.0f;
+    float o0 = 0.0f, o1 = 0.0f;
+    for (int c = 0; c < nc; ++c) {
+        float f = exp2f(ws_ml[2 * (slot0 + c)] - mu);
+        z += f * ws_ml[2 * (slot0 + c) + 1];
+        const float *acc = ws_acc + (slot0 + c) * DV + 2 * lane;
+        o0 += f * acc[0];
+        o1 += f * acc[1];
+    }
+    float r = z > 0.0f ? a.value_scale / z : 0.0f;
+    uint16_t *out = (uint16_t *)a.out + wid * DV + 2 * lane;
+    *reinterpret_cast<uint32_t *>(out) = (uint32_t)f2bf(o0 * r) | ((uint32_t)f2bf(o1 * r) << 16);
+}
+
+}  // namespace
+
+bool full_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
+    int G = a.hq / a.hkv;
+    return dtype == 0 && out_dtype == 0 && a.dqk == DQK && a.dv == DV && a.chunk % 128 == 0 &&
+           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+hipError_t launch_full_decode(const AttnArgs &a, hipStream_t s) {
+    dim3 grid((unsigned)(a.n_seqs * a.hkv * a.n_chunks)), block(kThreads);
+    switch (a.hq / a.hkv) {
+        case 1: hipLaunchKernelGGL(full_decode_partial_kernel<1>, grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(full_decode_partial_kernel<2>, grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL(full_decode_partial_kernel<4>, grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL(full_decode_partial_kernel<8>, grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL(full_decode_partial_kernel<16>, grid, block, 0, s, a); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t waves = (int64_t)a.n_seqs * a.hq;
+    dim3 grid2((unsigned)((waves + 3) / 4));
+    hipLaunchKernelGGL(full_decode_combine_kernel, grid2, block, 0, s, a);
+    return hipGetLastError();
+}
+
+// Workspace: (m, l) pairs then acc[DV] per (sequence, head, chunk), fp32.
+size_t full_decode_ws_bytes(int64_t n_seqs, int64_t hq, int64_t n_chunks, int64_t dv) {
+    int64_t ml = (2 * n_seqs * hq * n_chunks + 3) & ~(int64_t)3;
+    return (size_t)(ml + n_seqs * hq * n_chunks * dv) * sizeof(float);
+}
+
+}  // namespace hsw

@@ -1,0 +1,278 @@
+// hsw_abi.hip -- the C ABI of libhsw: host-side argument checks and dispatch.
+//
+// Every entry point validates its arguments before any launch; on failure it
+// returns an HSW_E_* code, records a message for hsw_last_error() and
+// launches nothing.  Zero-sized calls return HSW_OK without a launch.  No C++
+// exception crosses the boundary.  Device-resident values (positions,
+// lengths, bases) are never read here: the kernels bound their own accesses.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/hsw.h"
+#include "hsw_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hsw_status fail(hsw_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == HSW_BF16 ? 2 : 4; }
+
+// Shape checks shared by all calls.  want_window: 1 = windowed (> 0),
+// 0 = full (== 0), -1 = either.
+hsw_status check_shape(const hsw_attn_shape *sh, int want_window) {
+    if (!sh) return fail(HSW_E_NULL, "shape pointer is NULL");
+    if (sh->n_q_heads <= 0 || sh->n_kv_heads <= 0 || sh->n_q_heads % sh->n_kv_heads != 0)
+        return fail(HSW_E_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                    sh->n_q_heads, sh->n_kv_heads);
+    if (sh->d_qk < 8 || sh->d_qk > 256 || sh->d_qk % 8 != 0)
+        return fail(HSW_E_SHAPE, "d_qk (%d) must be a multiple of 8 in [8, 256]", sh->d_qk);
+    if (sh->d_v < 8 || sh->d_v > 256 || sh->d_v % 8 != 0)
+        return fail(HSW_E_SHAPE, "d_v (%d) must be a multiple of 8 in [8, 256]", sh->d_v);
+    if (sh->rope_dim < 0 || sh->rope_dim > sh->d_qk || sh->rope_dim % 16 != 0)
+        return fail(HSW_E_SHAPE, "rope_dim (%d) must be a multiple of 16 in [0, d_qk]", sh->rope_dim);
+    if (sh->window < 0) return fail(HSW_E_SHAPE, "window (%d) must be >= 0", sh->window);
+    if (want_window == 1 && sh->window == 0)
+        return fail(HSW_E_SHAPE, "a windowed call needs window > 0");
+    if (want_window == 0 && sh->window != 0)
+        return fail(HSW_E_SHAPE, "a full-attention call needs window == 0");
+    if (sh->dtype != HSW_BF16 && sh->dtype != HSW_F32)
+        return fail(HSW_E_DTYPE, "dtype %d is not HSW_BF16 or HSW_F32", sh->dtype);
+    if (sh->out_dtype != HSW_BF16 && sh->out_dtype != HSW_F32)
+        return fail(HSW_E_DTYPE, "out_dtype %d is not HSW_BF16 or HSW_F32", sh->out_dtype);
+    if (!(sh->softmax_scale > 0.0f) || !isfinite(sh->softmax_scale) || !isfinite(sh->value_scale))
+        return fail(HSW_E_SHAPE, "softmax_scale must be finite and > 0, value_scale finite");
+    if (sh->rope_dim > 0 && !(sh->rope_theta > 0.0))
+        return fail(HSW_E_SHAPE, "rope_theta must be > 0");
+    return HSW_OK;
+}
+
+#define REQUIRE_PTR(p) \
+    do { if (!(p)) return fail(HSW_E_NULL, "%s is NULL", #p); } while (0)
+#define REQUIRE_ALIGN(p, n) \
+    do { if ((p) && !aligned((p), (n))) return fail(HSW_E_ALIGN, "%s is not %d-byte aligned", #p, (int)(n)); } while (0)
+
+hsw_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return HSW_OK;
+}
+
+hsw::AttnArgs base_args(const hsw_attn_shape *sh) {
+    hsw::AttnArgs a;
+    memset(&a, 0, sizeof a);
+    a.hq = sh->n_q_heads;
+    a.hkv = sh->n_kv_heads;
+    a.dqk = sh->d_qk;
+    a.dv = sh->d_v;
+    a.window = sh->window;
+    a.scale = sh->softmax_scale;
+    a.value_scale = sh->value_scale;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hsw_status_str(hsw_status s) {
+    switch (s) {
+        case HSW_OK: return "HSW_OK";
+        case HSW_E_NULL: return "HSW_E_NULL: a required pointer is NULL";
+        case HSW_E_SHAPE: return "HSW_E_SHAPE: inconsistent or unsupported sizes";
+        case HSW_E_ALIGN: return "HSW_E_ALIGN: a tensor pointer is misaligned";
+        case HSW_E_DTYPE: return "HSW_E_DTYPE: unsupported dtype";
+        case HSW_E_WORKSPACE: return "HSW_E_WORKSPACE: workspace too small";
+        case HSW_E_LAUNCH: return "HSW_E_LAUNCH: kernel launch failed";
+        default: return "unknown hsw_status";
+    }
+}
+
+const char *hsw_last_error(void) { return g_err; }
+
+const char *hsw_version(void) { return "hsw 0.1 gfx950"; }
+
+hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens, const void *q,
+                                     const void *k, const void *v, const int64_t *pos,
+                                     const int32_t *seq, int32_t dst_kind, void *k_dst, void *v_dst,
+                                     int64_t dst_capacity, const int64_t *seq_base, void *q_rot,
+                                     int64_t *dst_index_out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, -1);
+    if (st) return st;
+    if (n_tokens < 0) return fail(HSW_E_SHAPE, "n_tokens (%lld) < 0", (long long)n_tokens);
+    if (dst_kind != HSW_DST_RING && dst_kind != HSW_DST_POOL && dst_kind != HSW_DST_STAGING)
+        return fail(HSW_E_SHAPE, "dst_kind %d is not RING, POOL or STAGING", dst_kind);
+    if (dst_kind == HSW_DST_RING && sh->window <= 0)
+        return fail(HSW_E_SHAPE, "a ring destination needs window > 0");
+    if (dst_capacity < 0) return fail(HSW_E_SHAPE, "dst_capacity < 0");
+    if (sh->rope_dim / 2 > 128) return fail(HSW_E_SHAPE, "rope_dim > 256 is not supported");
+    if (n_tokens > 0x7fffffffLL) return fail(HSW_E_SHAPE, "n_tokens exceeds 2^31 - 1");
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(pos);
+    REQUIRE_PTR(k_dst); REQUIRE_PTR(v_dst); REQUIRE_PTR(q_rot);
+    if (dst_kind != HSW_DST_STAGING) REQUIRE_PTR(seq);
+    if (dst_kind == HSW_DST_POOL) REQUIRE_PTR(seq_base);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(k_dst, 16);
+    REQUIRE_ALIGN(v_dst, 16); REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(pos, 8);
+    REQUIRE_ALIGN(seq, 4); REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(dst_index_out, 8);
+    if (n_tokens == 0) return HSW_OK;
+    hsw::RopeArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.pos = pos; a.seq = seq; a.seq_base = seq_base;
+    a.k_dst = k_dst; a.v_dst = v_dst; a.q_rot = q_rot; a.dst_index_out = dst_index_out;
+    a.n_tokens = n_tokens; a.dst_capacity = dst_capacity; a.theta = sh->rope_theta;
+    a.hq = sh->n_q_heads; a.hkv = sh->n_kv_heads; a.dqk = sh->d_qk; a.dv = sh->d_v;
+    a.rope_dim = sh->rope_dim; a.window = sh->window; a.dst_kind = dst_kind;
+    return launched(hsw::launch_rope(a, sh->dtype, (hipStream_t)stream), "rope_partial_kv_write");
+}
+
+hsw_status hsw_swa_prefill(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                           const int64_t *cu_seqlens, const int64_t *start_pos, const void *q_rot,
+                           const void *k_stage, const void *v_stage, void *k_ring, void *v_ring,
+                           const float *sinks, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, 1);
+    if (st) return st;
+    if (n_seqs < 0 || max_seqlen < 0) return fail(HSW_E_SHAPE, "n_seqs and max_seqlen must be >= 0");
+    if ((int64_t)n_seqs * max_seqlen * sh->n_q_heads > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "n_seqs * max_seqlen * n_q_heads exceeds 2^31 - 1");
+    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(start_pos); REQUIRE_PTR(q_rot); REQUIRE_PTR(k_stage);
+    REQUIRE_PTR(v_stage); REQUIRE_PTR(k_ring); REQUIRE_PTR(v_ring); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(k_stage, 16); REQUIRE_ALIGN(v_stage, 16);
+    REQUIRE_ALIGN(k_ring, 16); REQUIRE_ALIGN(v_ring, 16); REQUIRE_ALIGN(out, 16);
+    REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(start_pos, 8); REQUIRE_ALIGN(sinks, 4);
+    if (n_seqs == 0 || max_seqlen == 0) return HSW_OK;
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kSwaPrefill;
+    a.q = q_rot; a.k_main = k_stage; a.v_main = v_stage; a.k_ring = k_ring; a.v_ring = v_ring;
+    a.sinks = sinks; a.cu_seqlens = cu_seqlens; a.start_pos = start_pos; a.out = out;
+    a.n_seqs = n_seqs; a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hsw::swa_prefill_fast_ok(a, sh->dtype, sh->out_dtype)
+                       ? hsw::launch_swa_prefill(a, s)
+                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
+    if ((st = launched(e, "swa_prefill"))) return st;
+    // The ring commit overwrites slots the attention above read, so it is a
+    // second launch, ordered after it on the same stream.
+    return launched(hsw::launch_ring_commit(a, sh->dtype, s), "swa_prefill ring commit");
+}
+
+hsw_status hsw_swa_decode(const hsw_attn_shape *sh, int32_t n_seqs, const int64_t *pos,
+                          const void *q_rot, const void *k_ring, const void *v_ring,
+                          const float *sinks, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, 1);
+    if (st) return st;
+    if (n_seqs < 0) return fail(HSW_E_SHAPE, "n_seqs < 0");
+    if ((int64_t)n_seqs * sh->n_q_heads > 0x7fffffffLL) return fail(HSW_E_SHAPE, "n_seqs * n_q_heads exceeds 2^31 - 1");
+    REQUIRE_PTR(pos); REQUIRE_PTR(q_rot); REQUIRE_PTR(k_ring); REQUIRE_PTR(v_ring); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(k_ring, 16); REQUIRE_ALIGN(v_ring, 16);
+    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(pos, 8); REQUIRE_ALIGN(sinks, 4);
+    if (n_seqs == 0) return HSW_OK;
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kSwaDecode;
+    a.q = q_rot; a.k_main = k_ring; a.v_main = v_ring; a.sinks = sinks; a.pos = pos; a.out = out;
+    a.n_seqs = n_seqs; a.n_rows = n_seqs;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hsw::swa_decode_fast_ok(a, sh->dtype, sh->out_dtype)
+                       ? hsw::launch_swa_decode(a, s)
+                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
+    return launched(e, "swa_decode");
+}
+
+size_t hsw_full_decode_workspace_bytes(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                       int32_t chunk) {
+    if (!sh || n_seqs < 0 || max_ctx < 0 || chunk <= 0) return 0;
+    int64_t nc = (max_ctx + chunk - 1) / chunk;
+    return hsw::full_decode_ws_bytes(n_seqs, sh->n_q_heads, nc, sh->d_v);
+}
+
+hsw_status hsw_full_decode_splitk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                  const int64_t *ctx_len, const int64_t *seq_base,
+                                  const void *q_rot, const void *k_pool, const void *v_pool,
+                                  int64_t pool_rows, const float *sinks, int32_t chunk, void *ws,
+                                  size_t ws_bytes, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, 0);
+    if (st) return st;
+    if (n_seqs < 0 || max_ctx < 0 || pool_rows < 0)
+        return fail(HSW_E_SHAPE, "n_seqs, max_ctx and pool_rows must be >= 0");
+    if (chunk <= 0 || chunk % 128 != 0) return fail(HSW_E_SHAPE, "chunk (%d) must be a positive multiple of 128", chunk);
+    REQUIRE_PTR(ctx_len); REQUIRE_PTR(seq_base); REQUIRE_PTR(q_rot); REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(k_pool, 16); REQUIRE_ALIGN(v_pool, 16);
+    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(ws, 16); REQUIRE_ALIGN(ctx_len, 8);
+    REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(sinks, 4);
+    if (n_seqs == 0) return HSW_OK;
+    size_t need = hsw_full_decode_workspace_bytes(sh, n_seqs, max_ctx, chunk);
+    if (!ws || ws_bytes < need)
+        return fail(HSW_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
+    if (max_ctx == 0) return HSW_OK;
+    int64_t nc = (max_ctx + chunk - 1) / chunk;
+    if ((int64_t)n_seqs * sh->n_kv_heads * nc > 0x7fffffffLL || (int64_t)n_seqs * sh->n_q_heads > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "grid too large");
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kFullDecode;
+    a.q = q_rot; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.ctx_len = ctx_len;
+    a.seq_base = seq_base; a.out = out; a.ws = ws; a.n_seqs = n_seqs; a.n_rows = n_seqs;
+    a.max_seqlen = max_ctx; a.pool_rows = pool_rows; a.chunk = chunk; a.n_chunks = (int)nc;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hsw::full_decode_fast_ok(a, sh->dtype, sh->out_dtype)
+                       ? hsw::launch_full_decode(a, s)
+                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
+    return launched(e, "full_decode_splitk");
+}
+
+hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                                  const int64_t *cu_seqlens, const int64_t *start_pos,
+                                  const int64_t *seq_base, const void *q_rot, const void *k_pool,
+                                  const void *v_pool, int64_t pool_rows, const float *sinks,
+                                  void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, 0);
+    if (st) return st;
+    if (n_seqs < 0 || max_seqlen < 0 || pool_rows < 0)
+        return fail(HSW_E_SHAPE, "n_seqs, max_seqlen and pool_rows must be >= 0");
+    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(start_pos); REQUIRE_PTR(seq_base); REQUIRE_PTR(q_rot);
+    REQUIRE_PTR(k_pool); REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(k_pool, 16); REQUIRE_ALIGN(v_pool, 16);
+    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(start_pos, 8);
+    REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(sinks, 4);
+    if (n_seqs == 0 || max_seqlen == 0) return HSW_OK;
+    if ((int64_t)n_seqs * max_seqlen * sh->n_q_heads > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "n_seqs * max_seqlen * n_q_heads exceeds 2^31 - 1");
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kFullPrefill;
+    a.q = q_rot; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
+    a.start_pos = start_pos; a.seq_base = seq_base; a.out = out; a.n_seqs = n_seqs;
+    a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen; a.pool_rows = pool_rows;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hsw::full_prefill_fast_ok(a, sh->dtype, sh->out_dtype)
+                       ? hsw::launch_full_prefill(a, s)
+                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
+    return launched(e, "full_prefill_chunk");
+}
+
+int64_t hsw_kv_bytes(int32_t kind, int64_t n_seqs, int64_t ctx, int32_t window, int32_t n_kv_heads,
+                     int32_t d_qk, int32_t d_v_stored, int32_t elem_bytes, int32_t n_layers) {
+    if (n_seqs < 0 || ctx < 0 || n_kv_heads < 0 || d_qk < 0 || d_v_stored < 0 || elem_bytes <= 0 ||
+        n_layers < 0)
+        return -1;
+    int64_t positions;
+    if (kind == HSW_DST_RING) {
+        if (window <= 0) return -1;
+        positions = window;
+    } else if (kind == HSW_DST_POOL) {
+        positions = ctx;
+    } else {
+        return -1;
+    }
+    return (int64_t)n_layers * n_seqs * positions * n_kv_heads * (int64_t)(d_qk + d_v_stored) * elem_bytes;
+}
+
+}  // extern "C"

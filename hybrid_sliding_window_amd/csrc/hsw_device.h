@@ -1,0 +1,104 @@
+// hsw_device.h -- device-side helpers shared by the gfx950 kernels of libhsw.
+//
+// Vector types for MFMA operands, bf16 <-> fp32 conversions, 16-byte global
+// loads/stores and wave-level reductions.  gfx950 only: wave64, MFMA
+// v_mfma_f32_16x16x32_bf16 (8 bf16 per lane per operand) and
+// v_mfma_f32_16x16x16_{bf16,f16} (4 per lane).
+//
+// Lane layout of the 16x16 MFMA family used throughout (wave64, lane l,
+// quad q = l / 16, column c = l % 16):
+//   A (16 x K):  lane l holds row c, K-slots of quad q;
+//   B (K x 16):  lane l holds column c, K-slots of quad q;
+//   D (16 x 16): lane l holds column c, rows 4q .. 4q+3.
+// Which K index each (quad, slot) pair denotes only has to agree between A
+// and B, since the product sums over K; every kernel loads A and B with the
+// same (quad, slot) -> K mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hsw {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, u32x4 v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x16_bf16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(u16x4, a),
+                                                     __builtin_bit_cast(u16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x16_f16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Split four fp32 values into bf16 hi = bf16(p) and lo = bf16(p - hi) so that
+// hi + lo carries about 16 significant bits of p.
+__device__ __forceinline__ void split_hi_lo(const float p[4], u32x2 &hi, u32x2 &lo) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = f2bf(p[i]);
+        l[i] = f2bf(p[i] - bf2f(h[i]));
+    }
+    hi = u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    lo = u32x2{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) {
+    return v + __shfl_xor(v, mask, kWave);
+}
+
+// Reduce over the four quads (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float quad_max(float v) {
+    v = wave_max_xor(v, 16);
+    return wave_max_xor(v, 32);
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    v = wave_sum_xor(v, 16);
+    return wave_sum_xor(v, 32);
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t *p) { return bf2f(*p); }
+    static __device__ __forceinline__ void store(uint16_t *p, float f) { *p = f2bf(f); }
+};
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float *p) { return *p; }
+    static __device__ __forceinline__ void store(float *p, float f) { *p = f; }
+};
+
+}  // namespace hsw

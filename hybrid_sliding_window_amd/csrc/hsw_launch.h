@@ -1,0 +1,60 @@
+// hsw_launch.h -- internal launch interface between the C ABI (hsw_abi.hip)
+// and the kernels.  Argument structs are passed to kernels by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hsw {
+
+struct RopeArgs {
+    const void *q, *k, *v;
+    const int64_t *pos;
+    const int32_t *seq;
+    const int64_t *seq_base;
+    void *k_dst, *v_dst, *q_rot;
+    int64_t *dst_index_out;
+    int64_t n_tokens, dst_capacity;
+    double theta;
+    int hq, hkv, dqk, dv, rope_dim, window, dst_kind;
+};
+
+// Attention call kinds served by the generic (any dtype / shape) kernel.
+enum AttnKind { kSwaPrefill = 0, kSwaDecode = 1, kFullPrefill = 2, kFullDecode = 3 };
+
+struct AttnArgs {
+    const void *q;             // q_rot
+    const void *k_main;        // staging (SWA prefill) / ring (SWA decode) / pool (full)
+    const void *v_main;
+    const void *k_ring;        // ring (SWA prefill only)
+    const void *v_ring;
+    const float *sinks;        // [Hq] or null
+    const int64_t *cu_seqlens; // prefill kinds
+    const int64_t *start_pos;  // prefill kinds
+    const int64_t *pos;        // SWA decode: position of the new token
+    const int64_t *ctx_len;    // full decode
+    const int64_t *seq_base;   // full kinds
+    void *out;
+    void *ws;                  // full decode partials
+    int64_t n_rows;            // query rows (tokens or sequences)
+    int64_t max_seqlen;        // prefill: bound on chunk length; full decode: max_ctx
+    int64_t pool_rows;         // full kinds: rows in the pool
+    int n_seqs, hq, hkv, dqk, dv, window, chunk, n_chunks;
+    float scale, value_scale;
+    int kind;
+};
+
+hipError_t launch_rope(const RopeArgs &a, int dtype, hipStream_t s);
+hipError_t launch_generic_attn(const AttnArgs &a, int dtype, int out_dtype, hipStream_t s);
+hipError_t launch_ring_commit(const AttnArgs &a, int dtype, hipStream_t s);
+bool swa_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
+hipError_t launch_swa_decode(const AttnArgs &a, hipStream_t s);
+bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
+hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s);
+bool full_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
+hipError_t launch_full_decode(const AttnArgs &a, hipStream_t s);
+size_t full_decode_ws_bytes(int64_t n_seqs, int64_t hq, int64_t n_chunks, int64_t dv);
+bool full_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
+hipError_t launch_full_prefill(const AttnArgs &a, hipStream_t s);
+
+}  // namespace hsw

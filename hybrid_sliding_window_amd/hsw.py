@@ -1,0 +1,156 @@
+"""Thin ctypes binding of libhsw.so (include/hsw.h).
+
+Argument marshalling only: every function takes torch tensors for device
+memory, passes their data pointers and the current HIP stream to the C entry
+point of the same name, and raises HswError on a non-zero status.  All
+arithmetic happens in the library's kernels; there is no CPU fallback, and
+importing this module fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhsw.so")
+
+HSW_BF16, HSW_F32 = 0, 1
+HSW_DST_RING, HSW_DST_POOL, HSW_DST_STAGING = 0, 1, 2
+STATUS = {0: "HSW_OK", 1: "HSW_E_NULL", 2: "HSW_E_SHAPE", 3: "HSW_E_ALIGN", 4: "HSW_E_DTYPE",
+          5: "HSW_E_WORKSPACE", 6: "HSW_E_LAUNCH"}
+
+
+class HswError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("value_scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+_DT = {torch.bfloat16: HSW_BF16, torch.float32: HSW_F32}
+
+
+def make_shape(s) -> AttnShape:
+    """From any object with the fields of workloads.Shape."""
+    return AttnShape(s.n_q_heads, s.n_kv_heads, s.d_qk, s.d_v, s.rope_dim, s.window,
+                     s.softmax_scale, s.value_scale, s.rope_theta, _DT[s.dtype], _DT[s.out_dtype])
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m hybrid_sliding_window_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SH = ctypes.POINTER(AttnShape)
+    lib.hsw_status_str.restype = ctypes.c_char_p
+    lib.hsw_status_str.argtypes = [I32]
+    lib.hsw_last_error.restype = ctypes.c_char_p
+    lib.hsw_version.restype = ctypes.c_char_p
+    lib.hsw_rope_partial_kv_write.argtypes = [SH, I64, P, P, P, P, P, I32, P, P, I64, P, P, P, P]
+    lib.hsw_swa_prefill.argtypes = [SH, I32, I64, P, P, P, P, P, P, P, P, P, P]
+    lib.hsw_swa_decode.argtypes = [SH, I32, P, P, P, P, P, P, P]
+    lib.hsw_full_decode_workspace_bytes.argtypes = [SH, I32, I64, I32]
+    lib.hsw_full_decode_workspace_bytes.restype = SZ
+    lib.hsw_full_decode_splitk.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, SZ, P, P]
+    lib.hsw_full_prefill_chunk.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
+    lib.hsw_kv_bytes.argtypes = [I32, I64, I64, I32, I32, I32, I32, I32, I32]
+    lib.hsw_kv_bytes.restype = I64
+    for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode",
+              "hsw_full_decode_splitk", "hsw_full_prefill_chunk"):
+        getattr(lib, f).restype = I32
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_rope_partial_kv_write",
+            "hsw_swa_prefill", "hsw_swa_decode", "hsw_full_decode_workspace_bytes",
+            "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_kv_bytes")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise HswError(rc, what, lib.hsw_last_error().decode())
+
+
+def _sh(shape):
+    return ctypes.byref(shape if isinstance(shape, AttnShape) else make_shape(shape))
+
+
+def hsw_rope_partial_kv_write(shape, n_tokens, q, k, v, pos, seq, dst_kind, k_dst, v_dst,
+                              dst_capacity, seq_base, q_rot, dst_index_out=None, stream=None):
+    _check(lib.hsw_rope_partial_kv_write(_sh(shape), int(n_tokens), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(pos), _ptr(seq), int(dst_kind), _ptr(k_dst),
+                                         _ptr(v_dst), int(dst_capacity), _ptr(seq_base),
+                                         _ptr(q_rot), _ptr(dst_index_out), _stream(stream)),
+           "hsw_rope_partial_kv_write")
+
+
+def hsw_swa_prefill(shape, n_seqs, max_seqlen, cu_seqlens, start_pos, q_rot, k_stage, v_stage,
+                    k_ring, v_ring, sinks, out, stream=None):
+    _check(lib.hsw_swa_prefill(_sh(shape), int(n_seqs), int(max_seqlen), _ptr(cu_seqlens),
+                               _ptr(start_pos), _ptr(q_rot), _ptr(k_stage), _ptr(v_stage),
+                               _ptr(k_ring), _ptr(v_ring), _ptr(sinks), _ptr(out), _stream(stream)),
+           "hsw_swa_prefill")
+
+
+def hsw_swa_decode(shape, n_seqs, pos, q_rot, k_ring, v_ring, sinks, out, stream=None):
+    _check(lib.hsw_swa_decode(_sh(shape), int(n_seqs), _ptr(pos), _ptr(q_rot), _ptr(k_ring),
+                              _ptr(v_ring), _ptr(sinks), _ptr(out), _stream(stream)),
+           "hsw_swa_decode")
+
+
+def hsw_full_decode_workspace_bytes(shape, n_seqs, max_ctx, chunk) -> int:
+    return int(lib.hsw_full_decode_workspace_bytes(_sh(shape), int(n_seqs), int(max_ctx), int(chunk)))
+
+
+def hsw_full_decode_splitk(shape, n_seqs, max_ctx, ctx_len, seq_base, q_rot, k_pool, v_pool,
+                           pool_rows, sinks, chunk, ws, ws_bytes, out, stream=None):
+    _check(lib.hsw_full_decode_splitk(_sh(shape), int(n_seqs), int(max_ctx), _ptr(ctx_len),
+                                      _ptr(seq_base), _ptr(q_rot), _ptr(k_pool), _ptr(v_pool),
+                                      int(pool_rows), _ptr(sinks), int(chunk), _ptr(ws),
+                                      int(ws_bytes), _ptr(out), _stream(stream)),
+           "hsw_full_decode_splitk")
+
+
+def hsw_full_prefill_chunk(shape, n_seqs, max_seqlen, cu_seqlens, start_pos, seq_base, q_rot,
+                           k_pool, v_pool, pool_rows, sinks, out, stream=None):
+    _check(lib.hsw_full_prefill_chunk(_sh(shape), int(n_seqs), int(max_seqlen), _ptr(cu_seqlens),
+                                      _ptr(start_pos), _ptr(seq_base), _ptr(q_rot), _ptr(k_pool),
+                                      _ptr(v_pool), int(pool_rows), _ptr(sinks), _ptr(out),
+                                      _stream(stream)),
+           "hsw_full_prefill_chunk")
+
+
+def hsw_kv_bytes(kind, n_seqs, ctx, window, n_kv_heads, d_qk, d_v_stored, elem_bytes, n_layers) -> int:
+    return int(lib.hsw_kv_bytes(int(kind), int(n_seqs), int(ctx), int(window), int(n_kv_heads),
+                                int(d_qk), int(d_v_stored), int(elem_bytes), int(n_layers)))
+
+
+def hsw_version() -> str:
+    return lib.hsw_version().decode()

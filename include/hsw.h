@@ -1,0 +1,228 @@
+/*
+ * hsw.h -- C ABI of the hybrid sliding-window attention core (libhsw.so),
+ * hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The method (MiMo-V2.6 Flash/Pro attention, as described on the pages):
+ *  - colibri "MiMo-V2.6 (Xiaomi)", section "What the engine implements":
+ *    layers are windowed (128-position ring, 8 KV heads on Flash, RoPE theta
+ *    1e4, a per-head sink logit that joins the softmax denominator only) or
+ *    full attention (4 KV heads on Flash, theta 1e7, no sink); partial
+ *    rotate-half RoPE on the first 64 of 192 q/k dims; values 128 wide; the
+ *    value scale (0.707 Flash, 0.612 Pro) multiplies values before attention.
+ *  - colibri, section "System One mode and prompt reuse": position p lives in
+ *    ring slot p mod 128; full layers keep K/V rows by position.
+ *  - gaudi-cookbook "MiMo-V2.6-Flash on Gaudi 2", section "What was built":
+ *    the decode window is exactly the last 128 positions; the sink must count
+ *    once per sequence, not once per KV block; section "Tiled global-attention
+ *    prefill": softmax is per query row, so query tiles need no merge.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked "host".  Scalars are host
+ *    values.  Tensor pointers must be 16-byte aligned.
+ *  - All tensors are dense, row-major (last index fastest), in `dtype`
+ *    (HSW_BF16 or HSW_F32) unless stated.  Positions and lengths are int64.
+ *  - The caller allocates and owns every buffer; the library allocates and
+ *    frees nothing.  Every output element of a call is overwritten (nothing is
+ *    accumulated into).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise.  They are re-entrant and may be issued
+ *    from several host threads on different streams.
+ *  - Errors: arguments are validated on the host before any launch.  A
+ *    failure returns an HSW_E_* code, launches nothing and writes nothing;
+ *    hsw_last_error() then describes it (thread-local).  Sizes of zero return
+ *    HSW_OK without a launch.  A launch failure reported by the runtime gives
+ *    HSW_E_LAUNCH.  Device-resident values (positions, lengths, bases) are not
+ *    read on the host; kernels skip, without writing, any K/V row whose
+ *    destination or source falls outside the capacities passed in.
+ *  - Positions are 0-based.  A window of W positions at position p holds
+ *    p-W+1 .. p (the token itself and the W-1 before it).
+ *  - Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef HSW_H_
+#define HSW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hsw_stream_t; /* identical to hipStream_t */
+
+typedef int32_t hsw_status;
+enum {
+    HSW_OK = 0,
+    HSW_E_NULL = 1,      /* a required pointer is NULL */
+    HSW_E_SHAPE = 2,     /* inconsistent or unsupported sizes */
+    HSW_E_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
+    HSW_E_DTYPE = 4,     /* unsupported dtype combination */
+    HSW_E_WORKSPACE = 5, /* workspace smaller than required */
+    HSW_E_LAUNCH = 6     /* the HIP runtime rejected a launch */
+};
+
+enum { HSW_BF16 = 0, HSW_F32 = 1 };
+
+/* Destination of K/V rows written by hsw_rope_partial_kv_write. */
+enum {
+    HSW_DST_RING = 0,    /* k_dst [n_seqs][Hkv][window][d_qk], slot = pos mod window */
+    HSW_DST_POOL = 1,    /* k_dst [rows][Hkv][d_qk], row = seq_base[seq] + pos      */
+    HSW_DST_STAGING = 2  /* k_dst [n_tokens][Hkv][d_qk], row = token index          */
+};
+
+/* Per-layer attention shape.
+ *   n_q_heads, n_kv_heads: GQA; n_q_heads % n_kv_heads == 0 (MFMA kernels
+ *   take groups of 1, 2, 4, 8 or 16; other groups use a generic kernel).
+ *   d_qk: q/k head width (192; multiple of 8, <= 256).  d_v: value width
+ *   (128; multiple of 8, <= 256).  rope_dim: rotated leading dims of each
+ *   q/k head (64; multiple of 16, <= d_qk).  The MFMA kernels take
+ *   d_qk = 192, d_v = 128 (and window 128 on windowed layers) in bf16; other
+ *   shapes and fp32 storage run on a generic wave-per-row kernel.  window: ring / window length in
+ *   positions (128) for windowed layers, 0 for full attention.
+ *   softmax_scale: multiplies q.k (1/sqrt(192) for these heads).
+ *   value_scale: multiplies values before attention (0.707 Flash).
+ *   rope_theta: 1e4 windowed, 1e7 full.
+ *   dtype: storage type of q, k, v, q_rot and the K/V caches.
+ *   out_dtype: type of attention outputs. */
+typedef struct hsw_attn_shape {
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t d_qk;
+    int32_t d_v;
+    int32_t rope_dim;
+    int32_t window;
+    float softmax_scale;
+    float value_scale;
+    double rope_theta;
+    int32_t dtype;
+    int32_t out_dtype;
+} hsw_attn_shape;
+
+const char *hsw_status_str(hsw_status s);
+const char *hsw_last_error(void);
+const char *hsw_version(void);
+
+/*
+ * Partial rotate-half RoPE on q and k, plus the K/V write.
+ * Follows colibri "What the engine implements" (rotate-half on the first
+ * rope_dim dims, theta per layer kind) and gaudi-cookbook "The RoPE fix for
+ * large positions" (angles must stay exact at large positions: each angle
+ * pos * theta^(-2i/rope_dim) is formed and reduced in double precision, then
+ * rotated in fp32).  Values are written unscaled: the value scale is applied
+ * to the attention output, which equals scaling values first by linearity.
+ *
+ *   q [n_tokens][Hq][d_qk], k [n_tokens][Hkv][d_qk], v [n_tokens][Hkv][d_v]
+ *      in dtype; pos [n_tokens] int64 (>= 0); seq [n_tokens] int32 (the
+ *      token's sequence; may be NULL for HSW_DST_STAGING; for HSW_DST_POOL
+ *      every seq[t] must index seq_base).
+ *   dst_kind: HSW_DST_RING / POOL / STAGING (see the enum for layouts; V is
+ *      the same with d_v).  dst_capacity: sequences in the ring, rows in the
+ *      pool, or rows in staging.  seq_base [n_seqs] int64: POOL only.
+ *   q_rot [n_tokens][Hq][d_qk] in dtype (written).
+ *   dst_index_out [n_tokens] int64 or NULL: the slot / row written for each
+ *      token, or -1 when its destination was outside dst_capacity.
+ */
+hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens,
+                                     const void *q, const void *k, const void *v,
+                                     const int64_t *pos, const int32_t *seq,
+                                     int32_t dst_kind, void *k_dst, void *v_dst,
+                                     int64_t dst_capacity, const int64_t *seq_base,
+                                     void *q_rot, int64_t *dst_index_out,
+                                     hsw_stream_t stream);
+
+/*
+ * Banded sliding-window prefill with a per-head sink, then the ring commit.
+ * Follows gaudi-cookbook "What was built" (banded tiles, fp32 softmax that
+ * includes the sink) and colibri "What the engine implements" (window of
+ * sh->window positions, sink in the denominator only, value scale).
+ *
+ *   Sequence s owns chunk tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 at
+ *   positions start_pos[s] + t.  Keys at positions < start_pos[s] come from
+ *   the ring (slot = pos mod window), which must hold positions
+ *   start_pos[s]-window+1 .. start_pos[s]-1 (those >= 0); keys inside the
+ *   chunk come from the staging buffers.
+ *   cu_seqlens [n_seqs+1], start_pos [n_seqs] int64; max_seqlen (host) bounds
+ *   every chunk length.  q_rot [T][Hq][d_qk]; k_stage [T][Hkv][d_qk];
+ *   v_stage [T][Hkv][d_v]; k_ring [n_seqs][Hkv][window][d_qk];
+ *   v_ring [n_seqs][Hkv][window][d_v]; sinks [Hq] fp32 or NULL;
+ *   out [T][Hq][d_v] in out_dtype.
+ *   After the attention, the last min(len, window) chunk rows of each
+ *   sequence are copied into their ring slots (a second, stream-ordered
+ *   launch), so the ring then holds the chunk's final positions.
+ */
+hsw_status hsw_swa_prefill(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                           const int64_t *cu_seqlens, const int64_t *start_pos,
+                           const void *q_rot, const void *k_stage, const void *v_stage,
+                           void *k_ring, void *v_ring, const float *sinks, void *out,
+                           hsw_stream_t stream);
+
+/*
+ * Sliding-window decode of one new token per sequence over its ring.
+ * Follows colibri "System One mode and prompt reuse" (slot t holds position
+ * P - ((P - t) mod window); slots holding positions < 0 are skipped) and
+ * gaudi-cookbook "What was built" (exactly the last `window` positions, the
+ * sink counted once).
+ *
+ *   pos [n_seqs] int64: the new token's position (already in the ring).
+ *   q_rot [n_seqs][Hq][d_qk]; k_ring / v_ring as in hsw_swa_prefill;
+ *   sinks [Hq] fp32 or NULL; out [n_seqs][Hq][d_v] in out_dtype.
+ */
+hsw_status hsw_swa_decode(const hsw_attn_shape *sh, int32_t n_seqs, const int64_t *pos,
+                          const void *q_rot, const void *k_ring, const void *v_ring,
+                          const float *sinks, void *out, hsw_stream_t stream);
+
+/*
+ * Full-attention decode, split over key chunks with a log-sum-exp combine.
+ * Follows colibri "System One mode and prompt reuse" (rows by position) and
+ * gaudi-cookbook "What was built" / "What it taught about Gaudi" (per-block
+ * decode partials; a sink, if given, is added exactly once, in the combine).
+ *
+ *   ctx_len [n_seqs] int64 (keys 0 .. ctx_len-1, the new token last, at
+ *   row seq_base[s] + ctx_len - 1); seq_base [n_seqs] int64; max_ctx (host)
+ *   bounds every ctx_len (keys past max_ctx are not read).  q_rot [n_seqs][Hq][d_qk];
+ *   k_pool [pool_rows][Hkv][d_qk], v_pool [pool_rows][Hkv][d_v] with
+ *   pool_rows (host) rows; sinks [Hq] fp32 or NULL; chunk: keys per split
+ *   (multiple of 64, e.g. 2048).  ws: device workspace of ws_bytes bytes,
+ *   at least hsw_full_decode_workspace_bytes(...).  out [n_seqs][Hq][d_v].
+ */
+size_t hsw_full_decode_workspace_bytes(const hsw_attn_shape *sh, int32_t n_seqs,
+                                       int64_t max_ctx, int32_t chunk);
+hsw_status hsw_full_decode_splitk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                  const int64_t *ctx_len, const int64_t *seq_base,
+                                  const void *q_rot, const void *k_pool, const void *v_pool,
+                                  int64_t pool_rows, const float *sinks, int32_t chunk,
+                                  void *ws, size_t ws_bytes, void *out, hsw_stream_t stream);
+
+/*
+ * Full-attention chunked prefill over prior rows plus the chunk (causal).
+ * Follows gaudi-cookbook "Tiled global-attention prefill" (query tiles, no
+ * materialised mask, no cross-tile merge since softmax is per row) and
+ * colibri "System One mode and prompt reuse" (rows by position).
+ *
+ *   Sequence s: chunk tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 at positions
+ *   start_pos[s] + t; its rows seq_base[s] + 0 .. seq_base[s] + start_pos[s]
+ *   + len - 1 are already in the pool (RoPE appended the chunk).
+ *   q_rot [T][Hq][d_qk]; pools as in hsw_full_decode_splitk; sinks [Hq] or
+ *   NULL; out [T][Hq][d_v] in out_dtype.
+ */
+hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                                  const int64_t *cu_seqlens, const int64_t *start_pos,
+                                  const int64_t *seq_base, const void *q_rot,
+                                  const void *k_pool, const void *v_pool, int64_t pool_rows,
+                                  const float *sinks, void *out, hsw_stream_t stream);
+
+/*
+ * KV-cache bytes (host arithmetic).  kind HSW_DST_RING: every sequence holds
+ * `window` positions whatever ctx is (the O(W) ring of colibri "What the
+ * engine implements"); HSW_DST_POOL: ctx positions.  Per position and layer:
+ * n_kv_heads * (d_qk + d_v_stored) * elem_bytes.  Returns -1 on bad input.
+ */
+int64_t hsw_kv_bytes(int32_t kind, int64_t n_seqs, int64_t ctx, int32_t window,
+                     int32_t n_kv_heads, int32_t d_qk, int32_t d_v_stored,
+                     int32_t elem_bytes, int32_t n_layers);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSW_H_ */

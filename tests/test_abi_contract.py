@@ -1,0 +1,137 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/hsw.h declares, rejects bad arguments on the host with the
+documented status (launching nothing), treats empty calls as no-ops, and its
+host-side layout arithmetic reproduces byte counts the pages print.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsw.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_values.json")
+
+hsw = pytest.importorskip("hybrid_sliding_window_amd.hsw",
+                          reason="libhsw.so not built (python -m hybrid_sliding_window_amd.build)")
+from hybrid_sliding_window_amd import workloads as wl  # noqa: E402
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails or is empty
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(hsw_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", hsw.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hsw_[a-z0-9_]+)\b", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(hsw.lib, n)
+    assert set(hsw.EXPORTED) == set(names)
+
+
+def test_status_strings():
+    for code in range(7):
+        assert hsw.lib.hsw_status_str(code).decode().startswith(hsw.STATUS[code])
+    assert "gfx950" in hsw.hsw_version()
+
+
+def swa():
+    return hsw.make_shape(wl.swa_shape())
+
+
+def full():
+    return hsw.make_shape(wl.full_shape())
+
+
+def expect(status, fn, *args, **kw):
+    with pytest.raises(hsw.HswError) as e:
+        fn(*args, **kw)
+    assert e.value.status == status, str(e.value)
+
+
+def test_rope_argument_errors():
+    sh = swa()
+    args = dict(n_tokens=4, q=FAKE, k=FAKE, v=FAKE, pos=FAKE, seq=FAKE, dst_kind=hsw.HSW_DST_RING,
+                k_dst=FAKE, v_dst=FAKE, dst_capacity=4, seq_base=None, q_rot=FAKE)
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "q": None})
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "seq": None})
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "dst_kind": hsw.HSW_DST_POOL})  # no seq_base
+    expect(3, hsw.hsw_rope_partial_kv_write, sh, **{**args, "k": FAKE + 2})
+    expect(2, hsw.hsw_rope_partial_kv_write, sh, **{**args, "dst_kind": 7})
+    expect(2, hsw.hsw_rope_partial_kv_write, sh, **{**args, "n_tokens": -1})
+    bad = swa()
+    bad.rope_dim = 24
+    expect(2, hsw.hsw_rope_partial_kv_write, bad, **args)
+    bad = swa()
+    bad.n_kv_heads = 3
+    expect(2, hsw.hsw_rope_partial_kv_write, bad, **args)
+    bad = swa()
+    bad.dtype = 9
+    expect(4, hsw.hsw_rope_partial_kv_write, bad, **args)
+    ring_full = full()
+    expect(2, hsw.hsw_rope_partial_kv_write, ring_full, **args)  # ring needs a window
+    # empty call: nothing launched, nothing touched
+    hsw.hsw_rope_partial_kv_write(sh, **{**args, "n_tokens": 0})
+
+
+def test_attention_argument_errors():
+    sh, fs = swa(), full()
+    expect(2, hsw.hsw_swa_prefill, fs, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(1, hsw.hsw_swa_prefill, sh, 1, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(3, hsw.hsw_swa_prefill, sh, 1, 8, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    hsw.hsw_swa_prefill(sh, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(2, hsw.hsw_swa_decode, fs, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(1, hsw.hsw_swa_decode, sh, 2, FAKE, FAKE, None, FAKE, None, FAKE)
+    hsw.hsw_swa_decode(sh, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    need = hsw.hsw_full_decode_workspace_bytes(fs, 4, 10000, 2048)
+    assert need > 0
+    expect(5, hsw.hsw_full_decode_splitk, fs, 4, 10000, FAKE, FAKE, FAKE, FAKE, FAKE, 40000, None,
+           2048, FAKE, need - 16, FAKE)
+    expect(2, hsw.hsw_full_decode_splitk, fs, 4, 10000, FAKE, FAKE, FAKE, FAKE, FAKE, 40000, None,
+           100, FAKE, need, FAKE)
+    expect(2, hsw.hsw_full_decode_splitk, sh, 4, 10000, FAKE, FAKE, FAKE, FAKE, FAKE, 40000, None,
+           2048, FAKE, need, FAKE)
+    expect(2, hsw.hsw_full_prefill_chunk, sh, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE)
+    expect(1, hsw.hsw_full_prefill_chunk, fs, 1, 8, FAKE, FAKE, None, FAKE, FAKE, FAKE, 100, None, FAKE)
+    hsw.hsw_full_prefill_chunk(fs, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE)
+
+
+def test_workspace_size_formula():
+    fs = full()
+    for S, L, C in [(64, 131072, 2048), (3, 1, 2048), (1, 4097, 1024)]:
+        nc = math.ceil(L / C)
+        ml = (2 * S * 64 * nc + 3) // 4 * 4
+        assert hsw.hsw_full_decode_workspace_bytes(fs, S, L, C) == 4 * (ml + S * 64 * nc * 128)
+
+
+def test_p10_kv_bytes_reproduce_page_values():
+    """Layout arithmetic against byte counts the pages print (golden file)."""
+    g = json.load(open(GOLDEN))
+    RING, POOL = hsw.HSW_DST_RING, hsw.HSW_DST_POOL
+    # 9 full layers, TP8 -> 1 KV head per card, V zero-padded to 192, bf16
+    assert hsw.hsw_kv_bytes(POOL, 1, 1, 0, 1, 192, 192, 2, 9) == g["full_kv_bytes_per_token_per_card_windowed_kv"]["value"]
+    # stock: all 48 layers keep full-length KV
+    assert hsw.hsw_kv_bytes(POOL, 1, 1, 0, 1, 192, 192, 2, 48) == g["full_kv_bytes_per_token_per_card_stock"]["value"]
+    # colibri snapshot: 39 rings x 128 slots x 8 heads x (192+128) f32 ~ 50 MB, whatever the context
+    snap = hsw.hsw_kv_bytes(RING, 1, 123456, 128, 8, 192, 128, 4, 39)
+    assert snap == hsw.hsw_kv_bytes(RING, 1, 7, 128, 8, 192, 128, 4, 39) == 51_118_080
+    assert round(snap / 1e6, -1) == g["ring_snapshot_bytes_flash"]["value_approx_mb"]
+    # Pro: 10 full layers x 8192 positions x 8 KV heads x (192+128) f32 = 0.78 GiB
+    pro = hsw.hsw_kv_bytes(POOL, 1, 8192, 0, 8, 192, 128, 4, 10)
+    assert round(pro / 2 ** 30, 2) == g["pro_full_kv_bytes_8k"]["value_gib_approx"]
+    assert hsw.hsw_kv_bytes(7, 1, 1, 0, 1, 1, 1, 1, 1) == -1
+    assert hsw.hsw_kv_bytes(RING, 1, 1, 0, 1, 1, 1, 1, 1) == -1

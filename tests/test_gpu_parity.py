@@ -1,0 +1,456 @@
+"""GPU parity: every C-ABI call on cuda:0 against the fp64 oracle fed the exact
+tensors that call consumed ("bf16 in"), element by element.
+
+Bars: max_abs <= 2e-2 and mean_rel <= 2e-3 for floating outputs (mean_rel is
+the L1 ratio sum|y - r| / sum|r| over a call's outputs); slot / row indices
+bit-exact; K written by RoPE within one bf16 ulp of the rounded fp64 value;
+pass-through dims, V and untouched cache rows bitwise unchanged; the fp32
+workload (logits near -25, sinks near +1) to mean_rel <= 1e-5.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, bf16_ulp, f64, linear_kv_from_ring, note, shape_kw
+from parity import assert_close, errors
+
+pytestmark = pytest.mark.gpu
+
+hsw = pytest.importorskip("hybrid_sliding_window_amd.hsw")
+from hybrid_sliding_window_amd import workloads as wl  # noqa: E402
+
+RING, POOL, STAGING = hsw.HSW_DST_RING, hsw.HSW_DST_POOL, hsw.HSW_DST_STAGING
+SENTINEL = -7.25  # exactly representable in bf16 and fp32
+
+
+def dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def check_rope_values(x_in, y_gpu, pos, theta, rope_dim=64, what=""):
+    """y_gpu against the fp64 rotation of exactly the input x_in: rotated dims
+    within one bf16 ulp (+ fp32 slack), pass-through dims bitwise."""
+    x = f64(x_in)
+    ref = oracle.rope(x, pos, theta, rope_dim)
+    y = f64(y_gpu)
+    assert np.array_equal(y[..., rope_dim:], x[..., rope_dim:]), f"{what}: pass-through dims changed"
+    half = rope_dim // 2
+    mag = np.abs(x[..., :half]) + np.abs(x[..., half:rope_dim])
+    mag = np.concatenate([mag, mag], axis=-1)
+    d = np.abs(y[..., :rope_dim] - ref[..., :rope_dim])
+    tol = bf16_ulp(ref[..., :rope_dim]) + 1e-6 * mag
+    bad = d > tol
+    assert not bad.any(), f"{what}: {bad.sum()} rotated values off by more than 1 bf16 ulp (max {d.max():.3e})"
+    return float((d == 0).mean())
+
+
+# ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("kind", [RING, POOL, STAGING])
+def test_rope_kv_write(kind):
+    note(f"rope kind={kind}")
+    shape = wl.full_shape() if kind == POOL else wl.swa_shape()
+    hq, hkv = shape.n_q_heads, shape.n_kv_heads
+    g = wl.gen(21 + kind)
+    special = [0, 1, 127, 128, 196608, 200000, 205000, 262143, 524287, 524288]
+    if kind == RING:
+        T = 300
+        pos = torch.cat([torch.tensor(special), torch.randint(0, 524289, (T - len(special),), generator=g)])
+        seq = torch.arange(T, dtype=torch.int32)
+        seq[-1] = T + 5                      # outside the ring: must be skipped, index -1
+        cap = T
+        seq_base = None
+        kdst = torch.full((cap, hkv, 128, 192), SENTINEL, dtype=torch.bfloat16)
+        vdst = torch.full((cap, hkv, 128, 128), SENTINEL, dtype=torch.bfloat16)
+    elif kind == POOL:
+        starts = [0, 130000, 199960, 524288 - 74]
+        T = 75 * len(starts)
+        pos = torch.cat([torch.arange(b, b + 75) for b in starts])
+        seq = torch.repeat_interleave(torch.arange(len(starts), dtype=torch.int32), 75)
+        seq_base = torch.tensor([75 * i - b for i, b in enumerate(starts)], dtype=torch.int64)
+        cap = T + 10
+        kdst = torch.full((cap, hkv, 192), SENTINEL, dtype=torch.bfloat16)
+        vdst = torch.full((cap, hkv, 128), SENTINEL, dtype=torch.bfloat16)
+    else:
+        T = 333
+        pos = torch.randint(0, 524289, (T,), generator=g)
+        pos[:len(special)] = torch.tensor(special)
+        seq = None
+        seq_base = None
+        cap = T + 7
+        kdst = torch.full((cap, hkv, 192), SENTINEL, dtype=torch.bfloat16)
+        vdst = torch.full((cap, hkv, 128), SENTINEL, dtype=torch.bfloat16)
+    pos = pos.to(torch.int64)
+    q = wl.randn((T, hq, 192), g)
+    k = wl.randn((T, hkv, 192), g)
+    v = wl.randn((T, hkv, 128), g)
+    d_q, d_k, d_v, d_pos = dev(q), dev(k), dev(v), dev(pos)
+    d_seq, d_base = dev(seq), dev(seq_base)
+    d_kdst, d_vdst = dev(kdst), dev(vdst)
+    q_rot = torch.empty_like(d_q)
+    idx = torch.full((T,), -99, dtype=torch.int64, device=DEV)
+    hsw.hsw_rope_partial_kv_write(shape, T, d_q, d_k, d_v, d_pos, d_seq, kind, d_kdst, d_vdst, cap,
+                                  d_base, q_rot, idx)
+    torch.cuda.synchronize()
+    P = pos.numpy()
+    # indices: exact
+    want = []
+    for t in range(T):
+        if kind == RING:
+            s = int(seq[t])
+            want.append(oracle.dst_index(oracle.RING, t, int(P[t])) if s < cap else -1)
+        elif kind == POOL:
+            want.append(oracle.dst_index(oracle.POOL, t, int(P[t]), int(seq_base[int(seq[t])])))
+        else:
+            want.append(oracle.dst_index(oracle.STAGING, t, int(P[t])))
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, np.array(want)), "destination indices differ"
+    frac_q = check_rope_values(q, q_rot, P, shape.rope_theta, what="q_rot")
+    kd, vd = kdst.clone(), vdst.clone()
+    gk, gv = d_kdst.cpu(), d_vdst.cpu()
+    written = np.zeros(gk.shape[:-1], bool)
+    for t in range(T):
+        if want[t] < 0:
+            continue
+        if kind == RING:
+            s = int(seq[t])
+            sel_k, sel_v = gk[s, :, want[t]], gv[s, :, want[t]]
+            written[s, :, want[t]] = True
+        else:
+            sel_k, sel_v = gk[want[t]], gv[want[t]]
+            written[want[t]] = True
+        check_rope_values(k[t:t + 1], sel_k[None], P[t:t + 1], shape.rope_theta, what=f"k[{t}]")
+        assert torch.equal(sel_v, v[t]), f"v[{t}] not copied bit-exactly"
+    # everything not written keeps the sentinel bytes
+    assert torch.equal(gk[torch.from_numpy(~written)], kd[torch.from_numpy(~written)])
+    assert torch.equal(gv[torch.from_numpy(~written)], vd[torch.from_numpy(~written)])
+    print(f"rope kind={kind}: q_rot bitwise-equal fraction {frac_q:.3f}")
+
+
+def test_rope_fp32_logit_shift_layer():
+    """fp32 storage (the logit-shift workload): rotation within fp32 rounding."""
+    note("rope fp32")
+    d = wl.logit_shift_layer()
+    shape = d["shape"]
+    T = d["q"].shape[0]
+    q_rot = torch.empty_like(dev(d["q"]))
+    kst = torch.empty_like(dev(d["k"]))
+    vst = torch.empty_like(dev(d["v"]))
+    hsw.hsw_rope_partial_kv_write(shape, T, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["pos"]), None,
+                                  STAGING, kst, vst, T, None, q_rot)
+    torch.cuda.synchronize()
+    P = d["pos"].numpy()
+    for x, y in ((d["q"], q_rot), (d["k"], kst)):
+        ref = oracle.rope(f64(x), P, shape.rope_theta)
+        assert np.abs(f64(y) - ref).max() <= 2e-6 * np.abs(ref).max()
+    assert torch.equal(vst.cpu(), d["v"])
+
+
+# ------------------------------------------------------------ SWA decode
+def run_swa_decode(batch):
+    shape = batch["shape"]
+    S = batch["pos"].shape[0]
+    kring, vring = dev(batch["kring"]), dev(batch["vring"])
+    q_rot = torch.empty_like(dev(batch["q"]))
+    idx = torch.empty(S, dtype=torch.int64, device=DEV)
+    hsw.hsw_rope_partial_kv_write(shape, S, dev(batch["q"]), dev(batch["k"]), dev(batch["v"]),
+                                  dev(batch["pos"]), dev(batch["seq"]), RING, kring, vring, S, None,
+                                  q_rot, idx)
+    out = torch.empty((S, shape.n_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+    sinks = dev(batch["sinks"])
+    hsw.hsw_swa_decode(shape, S, dev(batch["pos"]), q_rot, kring, vring, sinks, out)
+    torch.cuda.synchronize()
+    return q_rot, kring, vring, out, idx
+
+
+@pytest.mark.parametrize("case", ["small_positions", "decode_256_seqs"])
+def test_swa_decode(case):
+    if case == "small_positions":
+        positions = [0, 1, 2, 5, 63, 126, 127, 128, 129, 255, 1000, 524288]
+        batch = wl.swa_decode_batch(seed=31, n_seqs=len(positions), positions=positions)
+    else:
+        batch = wl.swa_decode_batch(seed=3)   # 256 sequences at positions U{128..524288}
+    note(f"swa_decode {case}")
+    shape = batch["shape"]
+    ring_before = batch["kring"].clone()
+    q_rot, kring, vring, out, idx = run_swa_decode(batch)
+    P = batch["pos"].numpy()
+    assert np.array_equal(idx.cpu().numpy(), P % 128)
+    # only slot P mod 128 of each sequence changed
+    kr = kring.cpu()
+    for s in range(len(P)):
+        other = torch.ones(128, dtype=torch.bool)
+        other[int(P[s]) % 128] = False
+        assert torch.equal(kr[s][:, other], ring_before[s][:, other])
+    ref = oracle.ring_decode(f64(q_rot), P, f64(kring), f64(vring), sinks=f64(batch["sinks"]), **shape_kw(shape))
+    ma, mr = assert_close(f64(out), ref, what=f"swa_decode {case}")
+    # chain from the raw inputs (reported, not gated)
+    qr = oracle.rope(f64(batch["q"]), P, shape.rope_theta)
+    kn = oracle.rope(f64(batch["k"]), P, shape.rope_theta)
+    kring64, vring64 = f64(batch["kring"]), f64(batch["vring"])
+    for s in range(len(P)):
+        kring64[s, :, P[s] % 128] = kn[s]
+        vring64[s, :, P[s] % 128] = f64(batch["v"])[s]
+    chain = oracle.ring_decode(qr, P, kring64, vring64, sinks=f64(batch["sinks"]), **shape_kw(shape))
+    cma, cmr = errors(f64(out), chain)
+    print(f"swa_decode {case}: bf16-in max_abs={ma:.2e} mean_rel={mr:.2e}; chain max_abs={cma:.2e} mean_rel={cmr:.2e}")
+
+
+def test_swa_decode_batch_order_bitwise():
+    """A row depends only on its own inputs: permuting the batch permutes the
+    output bytes (colibri 'System One mode': rows must not depend on others)."""
+    note("swa_decode batch order")
+    batch = wl.swa_decode_batch(seed=33, n_seqs=40)
+    _, _, _, out, _ = run_swa_decode(batch)
+    perm = torch.randperm(40, generator=wl.gen(34))
+    pb = {k: (v[perm] if isinstance(v, torch.Tensor) and v.shape[:1] == (40,) else v) for k, v in batch.items()}
+    pb["seq"] = torch.arange(40, dtype=torch.int32)
+    _, _, _, out_p, _ = run_swa_decode(pb)
+    assert torch.equal(out_p.cpu(), out.cpu()[perm])
+
+
+# ----------------------------------------------------------- SWA prefill
+def run_swa_prefill(batch):
+    shape = batch["shape"]
+    T = batch["q"].shape[0]
+    S = batch["start_pos"].shape[0]
+    lens = (batch["cu_seqlens"][1:] - batch["cu_seqlens"][:-1])
+    q_rot = torch.empty_like(dev(batch["q"]))
+    kst = torch.empty_like(dev(batch["k"]))
+    vst = torch.empty_like(dev(batch["v"]))
+    hsw.hsw_rope_partial_kv_write(shape, T, dev(batch["q"]), dev(batch["k"]), dev(batch["v"]),
+                                  dev(batch["pos"]), None, STAGING, kst, vst, T, None, q_rot)
+    kring, vring = dev(batch["kring"]), dev(batch["vring"])
+    kring_before, vring_before = kring.cpu(), vring.cpu()
+    out = torch.full((T, shape.n_q_heads, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_swa_prefill(shape, S, int(lens.max()) + 3, dev(batch["cu_seqlens"]), dev(batch["start_pos"]),
+                        q_rot, kst, vst, kring, vring, dev(batch["sinks"]), out)
+    torch.cuda.synchronize()
+    return q_rot, kst, vst, kring_before, vring_before, kring, vring, out
+
+
+def check_ring_commit(batch, kst, vst, kring_before, vring_before, kring, vring):
+    cu = batch["cu_seqlens"].tolist()
+    st = batch["start_pos"].tolist()
+    kr, vr, ks, vs = kring.cpu(), vring.cpu(), kst.cpu(), vst.cpu()
+    for s in range(len(st)):
+        n = cu[s + 1] - cu[s]
+        written = torch.zeros(128, dtype=torch.bool)
+        for t in range(max(0, n - 128), n):
+            slot = (st[s] + t) % 128
+            written[slot] = True
+            assert torch.equal(kr[s, :, slot], ks[cu[s] + t]) and torch.equal(vr[s, :, slot], vs[cu[s] + t])
+        assert torch.equal(kr[s][:, ~written], kring_before[s][:, ~written])
+        assert torch.equal(vr[s][:, ~written], vring_before[s][:, ~written])
+
+
+def oracle_swa_prefill_rows(batch, q_rot, kst, vst, kring_before, vring_before, rows=None):
+    """Oracle outputs for chunk rows (all, or a per-sequence sample)."""
+    shape = batch["shape"]
+    cu = batch["cu_seqlens"].tolist()
+    st = batch["start_pos"].tolist()
+    kr0, vr0 = f64(kring_before), f64(vring_before)
+    sinks = f64(batch["sinks"])
+    outs = []
+    for s in range(len(st)):
+        sel = np.arange(cu[s], cu[s + 1]) if rows is None else np.asarray(rows[s])
+        ks, vs = f64(kst[cu[s]:cu[s + 1]]), f64(vst[cu[s]:cu[s + 1]])
+        k, v, kpos0 = linear_kv_from_ring(kr0[s], vr0[s], st[s], ks, vs)
+        qpos = st[s] + (sel - cu[s])
+        qsel = f64(q_rot[torch.from_numpy(sel).to(q_rot.device)])
+        outs.append((sel, oracle.attn_linear(qsel, qpos, k, v, kpos0, window=128, sinks=sinks,
+                                             **shape_kw(shape))))
+    return outs
+
+
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (128, 8), (32, 8)])
+def test_swa_prefill_ragged(hq, hkv):
+    note(f"swa_prefill ragged hq={hq} hkv={hkv}")
+    batch = wl.swa_prefill_batch(seed=41, n_seqs=3, seqlens=(300, 17, 1000), start_pos=(0, 5000, 130),
+                                 hq=hq, hkv=hkv)
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
+    got = f64(out)
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb)])
+    ma, mr = assert_close(got, ref, what="swa_prefill ragged")
+    print(f"swa_prefill ragged hq={hq}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_swa_prefill_full_size_sampled():
+    """4 x 8192 from position 0: every head of sampled rows (the first 130,
+    the last 2 and 124 random per sequence), plus the ring commit."""
+    note("swa_prefill 4x8192 sampled")
+    batch = wl.swa_prefill_batch(seed=2)
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
+    cu = batch["cu_seqlens"].tolist()
+    g = np.random.default_rng(2)
+    rows = []
+    for s in range(4):
+        r = list(range(cu[s], cu[s] + 130)) + [cu[s + 1] - 2, cu[s + 1] - 1]
+        r += list(g.choice(np.arange(cu[s] + 130, cu[s + 1] - 2), 124, replace=False))
+        rows.append(np.array(sorted(r)))
+    outs = oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb, rows)
+    got = np.concatenate([f64(out[torch.from_numpy(sel)]) for sel, _ in outs])
+    ref = np.concatenate([o for _, o in outs])
+    ma, mr = assert_close(got, ref, what="swa_prefill 4x8192")
+    print(f"swa_prefill 4x8192 sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_logit_shift_layer_fp32_chain():
+    """One windowed layer in fp32 (1 x 512, 4/1 heads, logits ~ -25, sinks ~ +1):
+    rope + windowed prefill against the oracle from the raw inputs."""
+    note("fp32 logit-shift layer")
+    d = wl.logit_shift_layer()
+    shape = d["shape"]
+    T = 512
+    q_rot = torch.empty_like(dev(d["q"]))
+    kst = torch.empty_like(dev(d["k"]))
+    vst = torch.empty_like(dev(d["v"]))
+    hsw.hsw_rope_partial_kv_write(shape, T, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["pos"]), None,
+                                  STAGING, kst, vst, T, None, q_rot)
+    kring = torch.zeros((1, 1, 128, 192), dtype=torch.float32, device=DEV)
+    vring = torch.zeros((1, 1, 128, 128), dtype=torch.float32, device=DEV)
+    out = torch.empty((T, 4, 128), dtype=torch.float32, device=DEV)
+    hsw.hsw_swa_prefill(shape, 1, T, dev(d["cu_seqlens"]), dev(d["start_pos"]), q_rot, kst, vst,
+                        kring, vring, dev(d["sinks"]), out)
+    torch.cuda.synchronize()
+    P = d["pos"].numpy()
+    qr = oracle.rope(f64(d["q"]), P, shape.rope_theta)
+    kr = oracle.rope(f64(d["k"]), P, shape.rope_theta)
+    ref = oracle.attn_linear(qr, P, kr, f64(d["v"]), 0, window=128, sinks=f64(d["sinks"]), **shape_kw(shape))
+    ma, mr = assert_close(f64(out), ref, mean_rel=1e-5, what="fp32 chain")
+    print(f"fp32 logit-shift chain: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_decode_matches_prefill_row():
+    """Decode at position P equals prefill row P (colibri 'Correctness':
+    prefill in blocks and one token at a time agree)."""
+    note("decode vs prefill row")
+    batch = wl.swa_prefill_batch(seed=51, n_seqs=1, seqlens=(300,), start_pos=(0,))
+    shape = batch["shape"]
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    # ring now holds positions 172..299; decode position 299 with its q_rot row
+    o = torch.empty((1, 64, 128), dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_swa_decode(shape, 1, torch.tensor([299], device=DEV), q_rot[299:300].contiguous(), kring,
+                       vring, dev(batch["sinks"]), o)
+    torch.cuda.synchronize()
+    assert_close(f64(o)[0], f64(out)[299], what="decode vs prefill row")
+
+
+# ------------------------------------------------------- full decode
+def run_full_decode(batch, chunk=2048, sinks=None):
+    shape = batch["shape"]
+    S = batch["ctx_len"].shape[0]
+    kpool, vpool = dev(batch["kpool"]), dev(batch["vpool"])
+    q_rot = torch.empty_like(dev(batch["q"]))
+    rows = kpool.shape[0]
+    hsw.hsw_rope_partial_kv_write(shape, S, dev(batch["q"]), dev(batch["k"]), dev(batch["v"]),
+                                  dev(batch["pos"]), dev(batch["seq"]), POOL, kpool, vpool, rows,
+                                  dev(batch["seq_base"]), q_rot)
+    max_ctx = int(batch["ctx_len"].max())
+    wsb = hsw.hsw_full_decode_workspace_bytes(shape, S, max_ctx, chunk)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=DEV)
+    out = torch.empty((S, shape.n_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_full_decode_splitk(shape, S, max_ctx, dev(batch["ctx_len"]), dev(batch["seq_base"]), q_rot,
+                               kpool, vpool, rows, dev(sinks), chunk, ws, wsb, out)
+    torch.cuda.synchronize()
+    return q_rot, kpool, vpool, out
+
+
+def oracle_full_decode(batch, q_rot, kpool, vpool, seqs, sinks=None):
+    shape = batch["shape"]
+    L = batch["ctx_len"].tolist()
+    base = batch["seq_base"].tolist()
+    qr = f64(q_rot)
+    res = []
+    for s in seqs:
+        k = f64(kpool[base[s]:base[s] + L[s]])
+        v = f64(vpool[base[s]:base[s] + L[s]])
+        res.append(oracle.attn_linear(qr[s:s + 1], [L[s] - 1], k, v, 0, window=0,
+                                      sinks=None if sinks is None else f64(sinks), **shape_kw(shape))[0])
+    return np.stack(res)
+
+
+@pytest.mark.parametrize("chunk,with_sink", [(2048, False), (1024, False), (2048, True), (128, True)])
+def test_full_decode_small(chunk, with_sink):
+    note(f"full_decode small chunk={chunk} sink={with_sink}")
+    lengths = [1, 2, 127, 2047, 2048, 2049, 9000, 4097]
+    batch = wl.full_decode_batch(seed=61, n_seqs=len(lengths), lengths=lengths, with_sinks=with_sink)
+    q_rot, kpool, vpool, out = run_full_decode(batch, chunk, batch["sinks"])
+    ref = oracle_full_decode(batch, q_rot, kpool, vpool, range(len(lengths)), batch["sinks"])
+    ma, mr = assert_close(f64(out), ref, what="full_decode small")
+    print(f"full_decode chunk={chunk} sink={with_sink}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_full_decode_full_size_sampled():
+    """64 sequences with contexts U{32768..131072}: the shortest, the longest
+    and two random sequences checked against the oracle, all heads."""
+    note("full_decode 64 seqs sampled")
+    batch = wl.full_decode_batch(seed=4, device=DEV)
+    q_rot, kpool, vpool, out = run_full_decode(batch)
+    L = batch["ctx_len"].numpy()
+    seqs = sorted({int(L.argmin()), int(L.argmax()), 17, 42})
+    ref = oracle_full_decode(batch, q_rot, kpool, vpool, seqs)
+    ma, mr = assert_close(f64(out[seqs]), ref, what="full_decode 64 seqs")
+    print(f"full_decode 64 seqs (sampled {seqs}): max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+# ------------------------------------------------------ full prefill
+def run_full_prefill(batch):
+    shape = batch["shape"]
+    T = batch["q"].shape[0]
+    S = batch["start_pos"].shape[0]
+    kpool, vpool = dev(batch["kpool"]), dev(batch["vpool"])
+    rows = kpool.shape[0]
+    q_rot = torch.empty_like(dev(batch["q"]))
+    hsw.hsw_rope_partial_kv_write(shape, T, dev(batch["q"]), dev(batch["k"]), dev(batch["v"]),
+                                  dev(batch["pos"]), dev(batch["seq"]), POOL, kpool, vpool, rows,
+                                  dev(batch["seq_base"]), q_rot)
+    lens = batch["cu_seqlens"][1:] - batch["cu_seqlens"][:-1]
+    out = torch.empty((T, shape.n_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_full_prefill_chunk(shape, S, int(lens.max()), dev(batch["cu_seqlens"]), dev(batch["start_pos"]),
+                               dev(batch["seq_base"]), q_rot, kpool, vpool, rows, None, out)
+    torch.cuda.synchronize()
+    return q_rot, kpool, vpool, out
+
+
+def oracle_full_prefill(batch, q_rot, kpool, vpool, rows_per_seq):
+    shape = batch["shape"]
+    cu = batch["cu_seqlens"].tolist()
+    st = batch["start_pos"].tolist()
+    base = batch["seq_base"].tolist()
+    qr = f64(q_rot)
+    got_idx, refs = [], []
+    for s, sel in enumerate(rows_per_seq):
+        sel = np.asarray(sel)
+        n = st[s] + cu[s + 1] - cu[s]
+        k = f64(kpool[base[s]:base[s] + n])
+        v = f64(vpool[base[s]:base[s] + n])
+        refs.append(oracle.attn_linear(qr[sel], st[s] + sel - cu[s], k, v, 0, window=0, **shape_kw(shape)))
+        got_idx.append(sel)
+    return np.concatenate(got_idx), np.concatenate(refs)
+
+
+def test_full_prefill_ragged():
+    note("full_prefill ragged")
+    batch = wl.full_prefill_batch(seed=71, n_seqs=3, seqlens=(300, 77, 129), start_pos=(3000, 100, 0))
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    cu = batch["cu_seqlens"].tolist()
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(3)])
+    ma, mr = assert_close(f64(out)[idx], ref, what="full_prefill ragged")
+    print(f"full_prefill ragged: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_full_prefill_chunk_8192_after_131072_sampled():
+    note("full_prefill 8192 @ 131072 sampled")
+    batch = wl.full_prefill_batch(seed=5, device=DEV)
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    rows = [np.array([0, 1, 2, 1000, 4095, 6000, 8190, 8191])]
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, rows)
+    ma, mr = assert_close(f64(out[torch.from_numpy(idx)]), ref, what="full_prefill 8192")
+    print(f"full_prefill 8192@131072 sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
