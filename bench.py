@@ -1,0 +1,280 @@
+"""Benchmark of the attention core on one MI355X (synthetic, seeded inputs).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+
+Prints ONE JSON line.  The headline `value` is the windowed (SWA) prefill
+throughput in algorithmic TFLOP/s on the 4 x 8192-token workload (64 q / 8 KV
+heads, window 128, per-head sinks): in-window (q, k) pairs x 2 x (192 + 128)
+flop, divided by the mean duration of one hsw_swa_prefill call (band kernel +
+ring commit) measured with HIP events on the stream the kernels run on.
+The same line carries the windowed-decode HBM GB/s on 256 sequences (the
+second half of the metric), the other calls of the path, a roofline object
+for the dominant kernel and the fp64 CPU oracle timed on a bounded sample.
+
+Inputs are resident in HBM before each timed region.  Timed regions cycle
+over enough replicas of the inputs that every launch reads HBM rather than
+the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SWA decode HBM GB/s (% peak) + SWA prefill TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+DEV = "cuda:0"
+
+
+def ev_time(fn, n, stream):
+    """Mean ms per call of fn() over n back-to-back calls, HIP events on `stream`."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def swa_prefill_pairs(lens, starts, window=128):
+    """In-window (query, key) pairs per head: sum over rows of min(p + 1, W)."""
+    tot = 0
+    for n, s in zip(lens, starts):
+        p = np.arange(s, s + n, dtype=np.int64)
+        tot += int(np.minimum(p + 1, window).sum())
+    return tot
+
+
+def bench_swa_prefill(hsw, wl, steps, warmup, stream):
+    """Windowed prefill, 4 x 8192 tokens from position 0; also times the RoPE +
+    staging write that feeds it."""
+    S, T1 = 4, 8192
+    b = wl.swa_prefill_batch(seed=2, device=DEV)
+    sh = b["shape"]
+    T = S * T1
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
+    q_rot = torch.empty_like(d["q"])
+    kst = torch.empty_like(d["k"])
+    vst = torch.empty_like(d["v"])
+
+    def rope(i):
+        hsw.hsw_rope_partial_kv_write(sh, T, d["q"], d["k"], d["v"], d["pos"], None, hsw.HSW_DST_STAGING,
+                                      kst, vst, T, None, q_rot, None, stream)
+    rope(0)
+    out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=DEV)
+
+    def call(i):
+        hsw.hsw_swa_prefill(sh, S, T1, d["cu_seqlens"], d["start_pos"], q_rot, kst, vst, d["kring"],
+                            d["vring"], d["sinks"], out, stream)
+    for i in range(warmup):
+        call(i)
+        rope(i)
+    torch.cuda.synchronize()
+    t_call = ev_time(call, steps, stream)
+    t_rope = ev_time(rope, max(steps, 20), stream)
+    pairs = swa_prefill_pairs([T1] * S, [0] * S)
+    flops = pairs * 64 * 2 * (192 + 128)
+    # algorithmic bytes: q_rot, staged K/V read once, out written once, the
+    # ring commit (last 128 rows of K and V per sequence) written once
+    bytes_ = T * 64 * 192 * 2 + T * 8 * (192 + 128) * 2 + T * 64 * 128 * 2 + S * 8 * 128 * (192 + 128) * 2
+    rope_bytes = T * 2 * (64 * 192 + 8 * 192 + 8 * 128) * 2
+    return dict(
+        ms=t_call, flops=flops, bytes=bytes_, tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
+        rope=dict(ms=t_rope, bytes=rope_bytes, gbs=rope_bytes / t_rope / 1e6,
+                  frac_hbm_peak=rope_bytes / t_rope / 1e6 / HBM_PEAK_GBS,
+                  workload="RoPE + staging write of 32768 tokens (64 q / 8 KV heads)"))
+
+
+def bench_swa_decode(hsw, wl, steps, stream, replicas=8):
+    """Windowed decode, 256 sequences at positions U{128..524288}; 8 replicas
+    of (q, rings, out) so each launch reads HBM (working set 178 MB < MALL)."""
+    S = 256
+    reps = []
+    for r in range(replicas):
+        b = wl.swa_decode_batch(seed=3 if r == 0 else 300 + r, device=DEV)
+        d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
+        q_rot = torch.empty_like(d["q"])
+        hsw.hsw_rope_partial_kv_write(b["shape"], S, d["q"], d["k"], d["v"], d["pos"], d["seq"],
+                                      hsw.HSW_DST_RING, d["kring"], d["vring"], S, None, q_rot, None, stream)
+        d["q_rot"] = q_rot
+        d["out"] = torch.empty((S, 64, 128), dtype=torch.bfloat16, device=DEV)
+        reps.append(d)
+    sh = b["shape"]
+
+    def call(i):
+        d = reps[i % replicas]
+        hsw.hsw_swa_decode(sh, S, d["pos"], d["q_rot"], d["kring"], d["vring"], d["sinks"], d["out"], stream)
+    for i in range(2 * replicas):
+        call(i)
+    torch.cuda.synchronize()
+    n = max(steps, 25) * replicas
+    t = ev_time(call, n, stream)
+    bytes_ = S * (8 * 128 * (192 + 128) * 2 + 64 * 192 * 2 + 64 * 128 * 2)
+    flops = S * 64 * 128 * 2 * (192 + 128)
+    return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
+                flops=flops, launches=n, replicas=replicas,
+                workload="windowed decode, 256 sequences at positions U{128..524288}, 64 q / 8 KV heads, 128-slot ring")
+
+
+def bench_full_decode(hsw, wl, steps, stream):
+    """Full-attention decode, 64 sequences, contexts U{32768..131072}, split-K 2048."""
+    b = wl.full_decode_batch(seed=4, device=DEV)
+    sh = b["shape"]
+    S = 64
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
+    rows = d["kpool"].shape[0]
+    q_rot = torch.empty_like(d["q"])
+    hsw.hsw_rope_partial_kv_write(sh, S, d["q"], d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
+                                  d["kpool"], d["vpool"], rows, d["seq_base"], q_rot, None, stream)
+    max_ctx = int(b["ctx_len"].max())
+    wsb = hsw.hsw_full_decode_workspace_bytes(sh, S, max_ctx, 2048)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=DEV)
+    out = torch.empty((S, 64, 128), dtype=torch.bfloat16, device=DEV)
+
+    def call(i):
+        hsw.hsw_full_decode_splitk(sh, S, max_ctx, d["ctx_len"], d["seq_base"], q_rot, d["kpool"], d["vpool"],
+                                   rows, None, 2048, ws, wsb, out, stream)
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    t = ev_time(call, max(steps // 2, 10), stream)
+    L = int(b["ctx_len"].sum())
+    bytes_ = L * 4 * (192 + 128) * 2 + S * 64 * (192 + 128) * 2
+    flops = L * 64 * 2 * (192 + 128)
+    del d, ws
+    return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
+                tflops=flops / t / 1e9,
+                workload="full-attention decode, 64 sequences, contexts U{32768..131072}, 64 q / 4 KV heads, split-K 2048")
+
+
+def bench_full_prefill(hsw, wl, steps, stream):
+    """Full-attention chunked prefill: 8192 tokens after 131072 prior rows."""
+    b = wl.full_prefill_batch(seed=5, device=DEV)
+    sh = b["shape"]
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
+    T = 8192
+    rows = d["kpool"].shape[0]
+    q_rot = torch.empty_like(d["q"])
+    hsw.hsw_rope_partial_kv_write(sh, T, d["q"], d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
+                                  d["kpool"], d["vpool"], rows, d["seq_base"], q_rot, None, stream)
+    out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=DEV)
+
+    def call(i):
+        hsw.hsw_full_prefill_chunk(sh, 1, T, d["cu_seqlens"], d["start_pos"], d["seq_base"], q_rot, d["kpool"],
+                                   d["vpool"], rows, None, out, stream)
+    call(0)
+    torch.cuda.synchronize()
+    t = ev_time(call, max(2, steps // 10), stream)
+    pairs = T * 131072 + T * (T + 1) // 2
+    flops = pairs * 64 * 2 * (192 + 128)
+    return dict(ms=t, flops=flops, tflops=flops / t / 1e9, frac_mfma_peak=flops / t / 1e9 / BF16_PEAK_TFLOPS,
+                workload="full-attention prefill, 8192 tokens after 131072 prior rows, 64 q / 4 KV heads")
+
+
+def cpu_baseline(target_s=15.0, max_seqs=4):
+    """The fp64 oracle on a bounded sample of the windowed-prefill workload:
+    one whole 8192-token sequence (all 64 heads, window 128, sinks), run
+    repeatedly until about target_s seconds of oracle time (at most max_seqs
+    runs), scaled to algorithmic TFLOP/s (the headline unit).  Input
+    generation is untimed."""
+    import oracle
+    from hybrid_sliding_window_amd import workloads as wl
+    kw = dict(window=128, tau=1 / math.sqrt(192), lam=0.707)
+    pos = np.arange(8192)
+    pairs_per_seq = int(np.minimum(pos + 1, 128).sum())
+    b = wl.swa_prefill_batch(seed=2, n_seqs=1, seqlens=(8192,))
+    q, k, v = (b[x].double().numpy() for x in "qkv")
+    spent, n = 0.0, 0
+    while n < max_seqs and spent < target_s:
+        t0 = time.perf_counter()
+        oracle.attn_linear(q, pos, k, v, 0, sinks=b["sinks"].double().numpy(), **kw)
+        spent += time.perf_counter() - t0
+        n += 1
+    flops = n * pairs_per_seq * 64 * 2 * (192 + 128)
+    return dict(value=flops / spent / 1e12, unit="TFLOP/s", cores=oracle.num_threads(), kind="oracle",
+                seconds=round(spent, 2),
+                sample=f"{n} run(s) of one windowed-prefill sequence of 8192 tokens (all 64 heads, window 128, "
+                       f"sinks) through the fp64 oracle; algorithmic in-window flops per second")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--quick", action="store_true", help="only the two metric calls")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence / KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    from hybrid_sliding_window_amd import hsw
+    from hybrid_sliding_window_amd import workloads as wl
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
+    print(f"[bench] swa_prefill {pre['ms']:.3f} ms {pre['tflops']:.1f} TFLOP/s {pre['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    dec = bench_swa_decode(hsw, wl, args.steps, stream)
+    print(f"[bench] swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    calls = {"rope_partial_kv_write": pre.pop("rope"), "swa_decode": dec}
+    if not args.quick:
+        fd = bench_full_decode(hsw, wl, args.steps, stream)
+        print(f"[bench] full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        fp = bench_full_prefill(hsw, wl, args.steps, stream)
+        print(f"[bench] full_prefill {fp['ms']:.2f} ms {fp['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        calls["full_decode_splitk"] = fd
+        calls["full_prefill_chunk"] = fp
+    calls["swa_prefill"] = dict(ms=pre["ms"], tflops=pre["tflops"], gbs=pre["gbs"],
+                                frac_mfma_peak=pre["tflops"] / BF16_PEAK_TFLOPS,
+                                frac_hbm_peak=pre["gbs"] / HBM_PEAK_GBS, flops=pre["flops"], bytes=pre["bytes"])
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "windowed (SWA) prefill bf16: 4 sequences x 8192 tokens from position 0, "
+                               "64 q / 8 KV heads, q/k 192, v 128, window 128, per-head sinks, value scale 0.707",
+                   "global_batch": 4, "seq_len": 8192, "parallelism": "single GPU"},
+        "swa_decode": {"value": round(dec["gbs"], 1), "unit": "GB/s",
+                       "frac_hbm_peak": round(dec["frac_hbm_peak"], 4), "us_per_call": round(dec["ms"] * 1e3, 2),
+                       "workload": dec["workload"]},
+        "swa_prefill_frac_mfma_peak": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "swa_prefill (band kernel + ring commit), 1.513 GB algorithmic per call"},
+        "calls": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                  for k, v in calls.items()},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
