@@ -23,6 +23,7 @@ namespace hsw {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
@@ -51,6 +52,10 @@ __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_16x16x16_bf16(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(u16x4, a),
                                                      __builtin_bit_cast(u16x4, b), c, 0, 0, 0);
@@ -58,6 +63,19 @@ __device__ __forceinline__ f32x4 mfma_16x16x16_bf16(u32x2 a, u32x2 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_16x16x16_f16(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed fp16, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+}
+
+// Two bf16 (packed in one word) -> two fp16 (packed), round to nearest even:
+// exact for |v| in the fp16 normal range; |v| >= 65536 becomes infinity.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 // Split four fp32 values into bf16 hi = bf16(p) and lo = bf16(p - hi) so that
