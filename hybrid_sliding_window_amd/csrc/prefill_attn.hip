@@ -287,12 +287,6 @@ bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
            (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
-bool full_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
-    int G = a.hq / a.hkv;
-    return dtype == 0 && out_dtype == 0 && a.dqk == DQK && a.dv == DV && a.window == 0 &&
-           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
-}
-
 template <bool FULL>
 static hipError_t launch_prefill(const AttnArgs &a, hipStream_t s) {
     int G = a.hq / a.hkv;
@@ -310,6 +304,5 @@ static hipError_t launch_prefill(const AttnArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s) { return launch_prefill<false>(a, s); }
-hipError_t launch_full_prefill(const AttnArgs &a, hipStream_t s) { return launch_prefill<true>(a, s); }
 
 }  // namespace hsw

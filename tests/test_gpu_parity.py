@@ -454,3 +454,19 @@ def test_full_prefill_chunk_8192_after_131072_sampled():
     idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, rows)
     ma, mr = assert_close(f64(out[torch.from_numpy(idx)]), ref, what="full_prefill 8192")
     print(f"full_prefill 8192@131072 sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_full_prefill_values_beyond_fp16_range():
+    """V rows with |v| ~ 1e5 (outside fp16 range) take the exact bf16 path and
+    still match the oracle."""
+    note("full_prefill large V")
+    batch = wl.full_prefill_batch(seed=72, n_seqs=2, seqlens=(200, 64), start_pos=(300, 37))
+    rows = batch["vpool"].shape[0]
+    big = torch.arange(0, rows, 37)
+    batch["vpool"][big] = (batch["vpool"][big].float() * 2.0e5).to(torch.bfloat16)
+    batch["v"][5] = (batch["v"][5].float() * 3.0e5).to(torch.bfloat16)
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    cu = batch["cu_seqlens"].tolist()
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(2)])
+    ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * float(np.abs(ref).max()), what="full_prefill large V")
+    print(f"full_prefill large V: max_abs={ma:.2e} mean_rel={mr:.2e}")
