@@ -1,0 +1,351 @@
+// swa_prefill.hip -- banded sliding-window prefill with a per-head sink
+// (bf16 storage, MFMA).  The ring commit that follows it is ring_commit_kernel
+// (generic_attn.hip), launched after it on the same stream.
+//
+// gaudi-cookbook "MiMo-V2.6-Flash on Gaudi 2", "What was built": windowed
+// prefill as banded tiles with an fp32 softmax that includes the sink;
+// "Tiled global-attention prefill": softmax is per query row, so query tiles
+// need no merge.  colibri "MiMo-V2.6 (Xiaomi)", "What the engine implements":
+// each query sees the last 128 positions (itself included), the sink logit
+// joins the denominator only, values carry the value scale (applied to the
+// fp32 output); "System One mode and prompt reuse": keys before the chunk
+// start come from ring slot p mod 128.
+//
+// One workgroup (4 waves) per query block: 128 rows = 128/G positions x the G
+// query heads of one KV head (the heads are the 16-wide MFMA columns), two
+// column tiles per wave.  The block's band (positions max(0, p0-127) .. its
+// last position, <= 143 keys for G = 8) streams through LDS in 32-key chunks
+// with a three-stage pipeline: chunk c+2 is fetched by direct global->LDS
+// 16-byte loads (no VGPR staging) while chunk c is computed, one barrier per
+// chunk; each wave skips chunks outside its rows' windows.  Per chunk:
+//   S^T = K Q^T      v_mfma_f32_16x16x32_bf16 (K rows from LDS, q in VGPRs)
+//   softmax          online in log2 units over logits only (the sink joins the
+//                    denominator at the end); the reference max is raised only
+//                    when a chunk's max exceeds it by more than 2^8 (P <= 256)
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P split into bf16 hi + lo
+//                    (about 16 significant bits, V exact in bf16); the V^T
+//                    operand is read from row-major V by ds_read_b64_tr_b16.
+// LDS rows are XOR-swizzled (the load side places each 16-byte piece where
+// the swizzle wants it), so both the K row reads and the transposing V reads
+// are free of bank conflicts.  Block ids are remapped so consecutive query
+// blocks of one (sequence, KV head) run on one XCD and re-read their
+// overlapping bands from its L2.
+#include "hsw_device.h"
+#include "hsw_launch.h"
+
+namespace hsw {
+namespace {
+
+constexpr int DQK = 192, DV = 128, W = 128;
+constexpr int STEPS = DQK / 32;
+constexpr int DT = DV / 16;
+constexpr int KC = 32;                      // keys per chunk
+constexpr int K_PIECES = KC * DQK / 8;      // 16-byte pieces per K stage (768)
+constexpr int V_PIECES = KC * DV / 8;       // per V stage (512)
+constexpr int kThreads = 256;
+constexpr int K_LOADS = K_PIECES / kThreads;  // 3 per thread
+constexpr int V_LOADS = V_PIECES / kThreads;  // 2 per thread
+constexpr int LOADS = K_LOADS + V_LOADS;      // vector-memory ops per chunk per thread
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most N vector-memory
+// ops of this wave are outstanding; expcnt and lgkmcnt left unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0).  Issued
+// as inline asm so that the compiler does not track it: it would otherwise
+// make every transposing LDS read (an intrinsic without alias information)
+// wait for all such loads in flight, the next chunks' included.  Completion
+// is awaited explicitly (s_waitcnt vmcnt) before the barrier that publishes a
+// stage; m0 is used by nothing else in these kernels.
+__device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave_base) {
+    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(const void *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int full = (total / 8) * 8;
+    if (bid >= full) return bid;
+    return (bid % 8) * (total / 8) + bid / 8;
+}
+
+// LDS placement, in 16-byte pieces.
+// K: key row r(key) = key ^ ((key >> 3) & 1), piece lp ^ (key & 7) of 24.  A
+//    quad's 16 lanes read keys 16h .. 16h+15 at one logical piece: the xor
+//    spreads 8 consecutive keys over 8 different 16-byte bank groups and the
+//    row swap puts keys k and k+8 on opposite halves of a 256-byte bank line.
+// V: row key, piece lp ^ 2 (key & 7) of 16.  A transposing read takes rows
+//    4q .. 4q+3 (16 lanes) / 8 rows (32 lanes) at two logical pieces; the xor
+//    gives each row its own pair of pieces.
+
+template <int G>
+__global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, int nqb) {
+    constexpr int BQ = 128 / G;
+    // Three stages, each its own LDS object so the compiler can tell that a
+    // read of one stage does not depend on the loads in flight to another.
+    __shared__ __attribute__((aligned(1024))) uint16_t ks0[KC * DQK], ks1[KC * DQK], ks2[KC * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs0[KC * DV], vs1[KC * DV], vs2[KC * DV];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
+    const int quad = lane >> 4, col = lane & 15;
+    const int total = a.n_seqs * a.hkv * nqb;
+    const int bid = xcd_remap(blockIdx.x, total);
+    const int qb = bid % nqb;
+    const int g = (bid / nqb) % a.hkv;
+    const int s = bid / (nqb * a.hkv);
+
+    const int64_t tok0 = a.cu_seqlens[s];
+    const int len = (int)(a.cu_seqlens[s + 1] - tok0);
+    if (qb * BQ >= len) return;
+    const int start = (int)a.start_pos[s];
+    const int p0 = start + qb * BQ;                 // first query position
+    const int plast = start + min(len, qb * BQ + BQ) - 1;
+    const int kstart = max(0, p0 - (W - 1));        // band: kstart .. plast
+    const int nch = (plast - kstart + KC) / KC;
+
+    // q of this wave's rows (row r = 32w + 16n + col -> position r / G, head
+    // r % G), from a clamped row so the load is unconditional; rows past the
+    // chunk only affect their own column and are never stored.
+    u32x4 qv[2][STEPS];
+    int qpos[2];
+    const uint16_t *qg = (const uint16_t *)a.q;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        int r = 32 * w + 16 * n + col;
+        int local = min(qb * BQ + r / G, len - 1);
+        qpos[n] = p0 + r / G;
+        const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+    }
+
+    // Sources: this sequence's staging rows and ring for KV head g.
+    const char *kst = (const char *)a.k_main + (tok0 * a.hkv + g) * (int64_t)(DQK * 2);
+    const char *vst = (const char *)a.v_main + (tok0 * a.hkv + g) * (int64_t)(DV * 2);
+    const char *kring = (const char *)a.k_ring + ((int64_t)(s * a.hkv + g) * W) * (DQK * 2);
+    const char *vring = (const char *)a.v_ring + ((int64_t)(s * a.hkv + g) * W) * (DV * 2);
+    const int64_t krow = (int64_t)a.hkv * DQK * 2, vrow = (int64_t)a.hkv * DV * 2;
+
+    // Load side: piece slot S = (i * 4 + w) * 64 + lane of a stage is written
+    // by this lane's i-th load; invert the placement to find what it holds.
+    int kkey[K_LOADS], kbyte[K_LOADS], vkey[V_LOADS], vbyte[V_LOADS];
+#pragma unroll
+    for (int i = 0; i < K_LOADS; ++i) {
+        int S = (i * 4 + w) * 64 + lane;
+        int r = S / (DQK / 8), pp = S % (DQK / 8);
+        kkey[i] = r ^ ((r >> 3) & 1);
+        kbyte[i] = 16 * (pp ^ (kkey[i] & 7));
+    }
+#pragma unroll
+    for (int i = 0; i < V_LOADS; ++i) {
+        int S = (i * 4 + w) * 64 + lane;
+        vkey[i] = S / (DV / 8);
+        vbyte[i] = 16 * ((S % (DV / 8)) ^ (2 * (vkey[i] & 7)));
+    }
+    // Key at band position kp: ring slot (kp mod W) before the chunk start,
+    // staging row (kp - start) from it; positions past plast are clamped to
+    // plast (finite data, masked).
+    auto key_src = [&](int kp, const char *st_base, const char *ring_base, int64_t row_bytes,
+                       int ring_row_bytes) -> const char * {
+        return kp >= start ? st_base + (int64_t)(kp - start) * row_bytes
+                           : ring_base + (int64_t)(kp % W) * ring_row_bytes;
+    };
+    auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd) {
+        const int k0 = kstart + c * KC;
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) {
+            int kp = min(k0 + kkey[i], plast);
+            const char *src = key_src(kp, kst, kring, krow, DQK * 2) + kbyte[i];
+            load_lds16(src, (const char *)ksd + (i * 4 + w) * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) {
+            int kp = min(k0 + vkey[i], plast);
+            const char *src = key_src(kp, vst, vring, vrow, DV * 2) + vbyte[i];
+            load_lds16(src, (const char *)vsd + (i * 4 + w) * 1024);
+        }
+    };
+
+    // Read side.  K: row base of key col (+16 rows for the second half) and
+    // piece (4 st + quad) ^ (col & 7) = 4 (st ^ s2) + q2 -> two bases, for
+    // even and odd st, each advancing 64 bytes per st.
+    const int krow_l = (col ^ ((col >> 3) & 1)) * DQK;
+    const int s2 = (col >> 2) & 1, q2 = quad ^ (col & 3);
+    const int k_even = krow_l + 8 * (4 * s2 + q2), k_odd = krow_l + 8 * (q2 - 4 * s2);
+    // V: lane 4k + mm of a quad supplies row 4 quad + k, logical dims
+    // 16 dt + 4 mm .. +3 = byte 32 dt + 8 mm, placed at 32 (dt ^ (row & 7)) + 8 mm.
+    const int tr_row = 4 * quad + (col >> 2);
+    const int v_base = tr_row * DV + 4 * (col & 3), v_x = 16 * (tr_row & 7);
+
+    const float scale2 = a.scale * kLog2e;
+    f32x4 oacc[2][DT];
+    float m[2], l[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        m[n] = -INFINITY;
+        l[n] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
+    }
+    const int wpos_lo = p0 + (32 * w) / G, wpos_hi = p0 + (32 * w + 31) / G;
+
+    auto step = [&](int c, const uint16_t *ksc, const uint16_t *vsc, uint16_t *ksn, uint16_t *vsn) {
+        // Own loads of chunk c done (chunk c+1's may still fly), then make
+        // every wave's visible.  The stage chunk c+2 goes to was last read in
+        // step c-1, which every wave has finished once past this barrier.
+        __asm__ volatile("" ::: "memory");
+        if (c + 1 < nch)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (c + 2 < nch) issue(c + 2, ksn, vsn);
+
+        const int k0 = kstart + c * KC;
+        // skip a chunk no row of this wave can see (wave-uniform)
+        if (!(k0 <= wpos_hi && k0 + KC - 1 > wpos_lo - W)) return;
+        // every key of the chunk inside every row's window: no mask
+        const bool interior = k0 + KC - 1 <= wpos_lo && k0 > wpos_hi - W && k0 + KC - 1 <= plast;
+        float sv[2][2][4];  // [16-key half][n][j]
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4 ak[STEPS];
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+                ak[st] = *reinterpret_cast<const u32x4 *>(ksc + (st & 1 ? k_odd : k_even) + 16 * DQK * h + 32 * st);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st) acc = mfma_16x16x32_bf16(ak[st], qv[n][st], acc);
+                if (interior) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][n][j] = acc[j];
+                } else {
+                    // key j of this lane is visible iff 0 <= qpos - kp < W (kp <= plast follows)
+                    const int d = qpos[n] - (k0 + 16 * h + 4 * quad);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][n][j] = (unsigned)(d - j) < (unsigned)W ? acc[j] : -INFINITY;
+                }
+            }
+        }
+        u32x4 bhi[2], blo[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float cm = fmaxf(fmaxf(fmaxf(sv[0][n][0], sv[0][n][1]), fmaxf(sv[0][n][2], sv[0][n][3])),
+                             fmaxf(fmaxf(sv[1][n][0], sv[1][n][1]), fmaxf(sv[1][n][2], sv[1][n][3])));
+            cm = quad_max(cm) * scale2;
+            const bool raise = cm > m[n] + kRescale;
+            if (__any(raise)) {
+                const float mn = raise ? cm : m[n];
+                const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
+                l[n] *= f;
+                m[n] = mn;
+            }
+            const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
+            float pv[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pv[4 * h + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][n][j], scale2, mu));
+                    l[n] += pv[4 * h + j];
+                }
+            u32x2 h0, l0, h1, l1;
+            split_hi_lo(pv, h0, l0);
+            split_hi_lo(pv + 4, h1, l1);
+            bhi[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+            blo[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+        }
+        // O^T += V^T P^T: slots 0-3 of a quad are keys 4quad.. of the first
+        // 16-key half, slots 4-7 the same keys of the second half, on both
+        // operands.
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int off = v_base + ((16 * dt) ^ v_x);
+            u32x2 a0 = ds_read_tr16(vsc + off);
+            u32x2 a1 = ds_read_tr16(vsc + off + 16 * DV);
+            u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                oacc[n][dt] = mfma_16x16x32_bf16(av, bhi[n], oacc[n][dt]);
+                oacc[n][dt] = mfma_16x16x32_bf16(av, blo[n], oacc[n][dt]);
+            }
+        }
+    };
+
+    issue(0, ks0, vs0);
+    if (nch > 1) issue(1, ks1, vs1);
+    for (int c = 0; c < nch; c += 3) {
+        step(c, ks0, vs0, ks2, vs2);
+        if (c + 1 < nch) step(c + 1, ks1, vs1, ks0, vs0);
+        if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1);
+    }
+
+    // Epilogue: the sink joins the denominator once; scale; store bf16.
+    uint16_t *outg = (uint16_t *)a.out;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        int r = 32 * w + 16 * n + col;
+        int local = qb * BQ + r / G;
+        float ll = quad_sum(l[n]);
+        if (local >= len) continue;
+        int head = r % G;
+        float mm = m[n], fac = 1.0f;
+        if (a.sinks) {
+            float sk = a.sinks[g * G + head] * kLog2e;
+            float mf = fmaxf(mm, sk);
+            fac = exp2f(mm - mf);
+            ll = ll * fac + exp2f(sk - mf);
+        }
+        float rs = a.value_scale * fac / ll;
+        uint16_t *orow = outg + ((tok0 + local) * a.hq + g * G + head) * (int64_t)DV;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            f32x4 o = oacc[n][dt];
+            u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * rs) | ((uint32_t)f2bf(o[1] * rs) << 16),
+                             (uint32_t)f2bf(o[2] * rs) | ((uint32_t)f2bf(o[3] * rs) << 16)};
+            *reinterpret_cast<u32x2 *>(orow + 16 * dt + 4 * quad) = pk;
+        }
+    }
+}
+
+}  // namespace
+
+bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
+    int G = a.hq / a.hkv;
+    return dtype == 0 && out_dtype == 0 && a.dqk == DQK && a.dv == DV && a.window == W &&
+           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s) {
+    const int G = a.hq / a.hkv;
+    const int BQ = 128 / G;
+    const int64_t nqb = (a.max_seqlen + BQ - 1) / BQ;
+    dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(kThreads);
+    const int nq = (int)nqb;
+    switch (G) {
+        case 1: hipLaunchKernelGGL(swa_prefill_kernel<1>, grid, block, 0, s, a, nq); break;
+        case 2: hipLaunchKernelGGL(swa_prefill_kernel<2>, grid, block, 0, s, a, nq); break;
+        case 4: hipLaunchKernelGGL(swa_prefill_kernel<4>, grid, block, 0, s, a, nq); break;
+        case 8: hipLaunchKernelGGL(swa_prefill_kernel<8>, grid, block, 0, s, a, nq); break;
+        default: hipLaunchKernelGGL(swa_prefill_kernel<16>, grid, block, 0, s, a, nq); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hsw
