@@ -37,6 +37,19 @@ BF16_PEAK_TFLOPS = 2500.0
 DEV = "cuda:0"
 
 
+def warm(fn, stream, seconds=0.3):
+    """Call fn until `seconds` of wall time have passed, so the GPU clocks have
+    ramped before anything is timed."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            stream.synchronize()
+    stream.synchronize()
+
+
 def ev_time(fn, n, stream):
     """Mean ms per call of fn() over n back-to-back calls, HIP events on `stream`."""
     start = torch.cuda.Event(enable_timing=True)
@@ -82,7 +95,7 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream):
     for i in range(warmup):
         call(i)
         rope(i)
-    torch.cuda.synchronize()
+    warm(call, stream)
     t_call = ev_time(call, steps, stream)
     t_rope = ev_time(rope, max(steps, 20), stream)
     pairs = swa_prefill_pairs([T1] * S, [0] * S)
@@ -119,7 +132,7 @@ def bench_swa_decode(hsw, wl, steps, stream, replicas=8):
         hsw.hsw_swa_decode(sh, S, d["pos"], d["q_rot"], d["kring"], d["vring"], d["sinks"], d["out"], stream)
     for i in range(2 * replicas):
         call(i)
-    torch.cuda.synchronize()
+    warm(call, stream)
     n = max(steps, 25) * replicas
     t = ev_time(call, n, stream)
     bytes_ = S * (8 * 128 * (192 + 128) * 2 + 64 * 192 * 2 + 64 * 128 * 2)

@@ -25,9 +25,9 @@
 //   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P split into bf16 hi + lo
 //                    (about 16 significant bits, V exact in bf16); the V^T
 //                    operand is read from row-major V by ds_read_b64_tr_b16.
-// LDS rows are XOR-swizzled (the load side places each 16-byte piece where
-// the swizzle wants it), so both the K row reads and the transposing V reads
-// are free of bank conflicts.  Block ids are remapped so consecutive query
+// LDS holds K and V in MFMA fragment order (the load side places each
+// 16-byte piece where a lane will read it), so every LDS read is a contiguous
+// run in lane order, free of bank conflicts.  Block ids are remapped so consecutive query
 // blocks of one (sequence, KV head) run on one XCD and re-read their
 // overlapping bands from its L2.
 #include "hsw_device.h"
@@ -56,20 +56,33 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0).  Issued
-// as inline asm so that the compiler does not track it: it would otherwise
-// make every transposing LDS read (an intrinsic without alias information)
-// wait for all such loads in flight, the next chunks' included.  Completion
-// is awaited explicitly (s_waitcnt vmcnt) before the barrier that publishes a
-// stage; m0 is used by nothing else in these kernels.
+// lds_wave_base + 16 i (lds_wave_base is wave-uniform).
+typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave_base) {
-    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
 }
 
+// Max / sum over the four quads (lanes c, c+16, c+32, c+48) with the gfx950
+// half-wave and row swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float quad_max_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float quad_sum_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
+// Transposing LDS read.  The pointer is cast straight to the LDS address
+// space (not through an integer) so the read keeps the alias scope of its LDS
+// array: the compiler then makes it wait only for loads into that array, not
+// for the loads in flight to the other stages.
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(const void *)p);
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     return __builtin_bit_cast(u32x2, v);
 }
 
@@ -127,7 +140,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         qpos[n] = p0 + r / G;
         const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+        for (int st = 0; st < STEPS; ++st) {
+            qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+        }
     }
 
     // Sources: this sequence's staging rows and ring for KV head g.
@@ -137,22 +152,28 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     const char *vring = (const char *)a.v_ring + ((int64_t)(s * a.hkv + g) * W) * (DV * 2);
     const int64_t krow = (int64_t)a.hkv * DQK * 2, vrow = (int64_t)a.hkv * DV * 2;
 
-    // Load side: piece slot S = (i * 4 + w) * 64 + lane of a stage is written
-    // by this lane's i-th load; invert the placement to find what it holds.
-    int kkey[K_LOADS], kbyte[K_LOADS], vkey[V_LOADS], vbyte[V_LOADS];
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-        int S = (i * 4 + w) * 64 + lane;
-        int r = S / (DQK / 8), pp = S % (DQK / 8);
-        kkey[i] = r ^ ((r >> 3) & 1);
-        kbyte[i] = 16 * (pp ^ (kkey[i] & 7));
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-        int S = (i * 4 + w) * 64 + lane;
-        vkey[i] = S / (DV / 8);
-        vbyte[i] = 16 * ((S % (DV / 8)) ^ (2 * (vkey[i] & 7)));
-    }
+    // LDS layout: fragment order.  K: 16-byte unit (h * 6 + st) * 64 + lane
+    // holds what lane (quad, col) feeds the S^T MFMA of key half h, step st:
+    // K[16h + col][pieces 4st + quad].  V: 8-byte unit (hh * 8 + dt) * 64 +
+    // lane holds what lane (quad, 4k + mm) supplies to the transposing read of
+    // key half hh, output tile dt: V[16hh + 4quad + k][16dt + 4mm .. +3].  So
+    // every LDS read is one contiguous 1 KB (K) or 512 B (V) run in lane
+    // order: no bank conflicts, and the address is the lane offset plus an
+    // immediate.  The load side picks each lane's global source to match: the
+    // i-th 16-byte load of wave w fills units (4i + w) * 64 + lane.
+    //   K load i: j = 4i + w, h = j / 6, st = j % 6: key 16h + col, bytes
+    //             64 st + 16 quad.
+    //   V load i: j = 4i + w, hh = j / 4, tiles 2 (j % 4) + (lane >> 5); with
+    //             u = lane & 31: row 16hh + 4 (u >> 3) + ((u >> 1) & 3), bytes
+    //             64 (j % 4) + 32 (lane >> 5) + 16 (u & 1).
+    const int u = lane & 31;
+    const int vrow_l = 4 * (u >> 3) + ((u >> 1) & 3);
+    const int vbyte_l = 32 * (lane >> 5) + 16 * (u & 1);
+    // Interior chunks (all keys from staging, none past plast): source =
+    // scalar base + this lane's constant offset.
+    const uint32_t koff_l = (uint32_t)(col * krow + 16 * quad);
+    const uint32_t voff_l = (uint32_t)(vrow_l * vrow + vbyte_l);
+
     // Key at band position kp: ring slot (kp mod W) before the chunk start,
     // staging row (kp - start) from it; positions past plast are clamped to
     // plast (finite data, masked).
@@ -163,30 +184,36 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     };
     auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd) {
         const int k0 = kstart + c * KC;
+        if (k0 >= start && k0 + KC - 1 <= plast) {
 #pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            int kp = min(k0 + kkey[i], plast);
-            const char *src = key_src(kp, kst, kring, krow, DQK * 2) + kbyte[i];
-            load_lds16(src, (const char *)ksd + (i * 4 + w) * 1024);
-        }
+            for (int i = 0; i < K_LOADS; ++i) {
+                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
+                load_lds16(kst + (int64_t)(k0 + 16 * h - start) * krow + 64 * st + koff_l,
+                           (const char *)ksd + j * 1024);
+            }
 #pragma unroll
-        for (int i = 0; i < V_LOADS; ++i) {
-            int kp = min(k0 + vkey[i], plast);
-            const char *src = key_src(kp, vst, vring, vrow, DV * 2) + vbyte[i];
-            load_lds16(src, (const char *)vsd + (i * 4 + w) * 1024);
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int j = 4 * i + w, hh = j / 4;
+                load_lds16(vst + (int64_t)(k0 + 16 * hh - start) * vrow + 64 * (j % 4) + voff_l,
+                           (const char *)vsd + j * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < K_LOADS; ++i) {
+                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
+                const int kp = min(k0 + 16 * h + col, plast);
+                load_lds16(key_src(kp, kst, kring, krow, DQK * 2) + 64 * st + 16 * quad,
+                           (const char *)ksd + j * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int j = 4 * i + w, hh = j / 4;
+                const int kp = min(k0 + 16 * hh + vrow_l, plast);
+                load_lds16(key_src(kp, vst, vring, vrow, DV * 2) + 64 * (j % 4) + vbyte_l,
+                           (const char *)vsd + j * 1024);
+            }
         }
     };
-
-    // Read side.  K: row base of key col (+16 rows for the second half) and
-    // piece (4 st + quad) ^ (col & 7) = 4 (st ^ s2) + q2 -> two bases, for
-    // even and odd st, each advancing 64 bytes per st.
-    const int krow_l = (col ^ ((col >> 3) & 1)) * DQK;
-    const int s2 = (col >> 2) & 1, q2 = quad ^ (col & 3);
-    const int k_even = krow_l + 8 * (4 * s2 + q2), k_odd = krow_l + 8 * (q2 - 4 * s2);
-    // V: lane 4k + mm of a quad supplies row 4 quad + k, logical dims
-    // 16 dt + 4 mm .. +3 = byte 32 dt + 8 mm, placed at 32 (dt ^ (row & 7)) + 8 mm.
-    const int tr_row = 4 * quad + (col >> 2);
-    const int v_base = tr_row * DV + 4 * (col & 3), v_x = 16 * (tr_row & 7);
 
     const float scale2 = a.scale * kLog2e;
     f32x4 oacc[2][DT];
@@ -224,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
             u32x4 ak[STEPS];
 #pragma unroll
             for (int st = 0; st < STEPS; ++st)
-                ak[st] = *reinterpret_cast<const u32x4 *>(ksc + (st & 1 ? k_odd : k_even) + 16 * DQK * h + 32 * st);
+                ak[st] = *reinterpret_cast<const u32x4 *>(ksc + ((h * STEPS + st) * 64 + lane) * 8);
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 f32x4 acc = f32x4{0, 0, 0, 0};
@@ -246,14 +273,17 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         for (int n = 0; n < 2; ++n) {
             float cm = fmaxf(fmaxf(fmaxf(sv[0][n][0], sv[0][n][1]), fmaxf(sv[0][n][2], sv[0][n][3])),
                              fmaxf(fmaxf(sv[1][n][0], sv[1][n][1]), fmaxf(sv[1][n][2], sv[1][n][3])));
-            cm = quad_max(cm) * scale2;
+            cm = quad_max_swap(cm) * scale2;
             const bool raise = cm > m[n] + kRescale;
             if (__any(raise)) {
                 const float mn = raise ? cm : m[n];
-                const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
+                // rows that have seen no key yet hold zeros: nothing to rescale
+                if (__any(raise && m[n] != -INFINITY)) {
+                    const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
-                l[n] *= f;
+                    for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
+                    l[n] *= f;
+                }
                 m[n] = mn;
             }
             const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
@@ -276,9 +306,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         // operands.
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const int off = v_base + ((16 * dt) ^ v_x);
-            u32x2 a0 = ds_read_tr16(vsc + off);
-            u32x2 a1 = ds_read_tr16(vsc + off + 16 * DV);
+            u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+            u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
             u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
@@ -302,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     for (int n = 0; n < 2; ++n) {
         int r = 32 * w + 16 * n + col;
         int local = qb * BQ + r / G;
-        float ll = quad_sum(l[n]);
+        float ll = quad_sum_swap(l[n]);
         if (local >= len) continue;
         int head = r % G;
         float mm = m[n], fac = 1.0f;
