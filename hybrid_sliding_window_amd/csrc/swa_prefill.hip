@@ -325,15 +325,19 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1);
     }
 
-    // Epilogue: the sink joins the denominator once; scale; store bf16.
-    uint16_t *outg = (uint16_t *)a.out;
+    // Epilogue: the sink joins the denominator once; scale; bf16.  Each wave
+    // turns its 32 x 128 output tile around in LDS (a stage no wave reads any
+    // more: only the last chunk's stage is still in use) so that the stores
+    // cover whole 256-byte rows, four per instruction.  Tile row stride 256 B,
+    // 16-byte units xor-swizzled by (row & 15): conflict-free both ways.
+    const int sl = (nch - 1) % 3;
+    const int fs = (w & 1) ? (sl + 2) % 3 : (sl + 1) % 3;
+    uint16_t *ep = (w < 2) ? (fs == 0 ? ks0 : fs == 1 ? ks1 : ks2) : (fs == 0 ? vs0 : fs == 1 ? vs1 : vs2);
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        int r = 32 * w + 16 * n + col;
-        int local = qb * BQ + r / G;
+        const int r = 32 * w + 16 * n + col;
         float ll = quad_sum_swap(l[n]);
-        if (local >= len) continue;
-        int head = r % G;
+        const int head = r % G;
         float mm = m[n], fac = 1.0f;
         if (a.sinks) {
             float sk = a.sinks[g * G + head] * kLog2e;
@@ -341,15 +345,26 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
             fac = exp2f(mm - mf);
             ll = ll * fac + exp2f(sk - mf);
         }
-        float rs = a.value_scale * fac / ll;
-        uint16_t *orow = outg + ((tok0 + local) * a.hq + g * G + head) * (int64_t)DV;
+        const float rs = a.value_scale * fac / ll;
+        const int row = 16 * n + col;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            f32x4 o = oacc[n][dt];
-            u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * rs) | ((uint32_t)f2bf(o[1] * rs) << 16),
-                             (uint32_t)f2bf(o[2] * rs) | ((uint32_t)f2bf(o[3] * rs) << 16)};
-            *reinterpret_cast<u32x2 *>(orow + 16 * dt + 4 * quad) = pk;
+            const f32x4 o = oacc[n][dt];
+            const u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * rs) | ((uint32_t)f2bf(o[1] * rs) << 16),
+                                   (uint32_t)f2bf(o[2] * rs) | ((uint32_t)f2bf(o[3] * rs) << 16)};
+            const int unit = (2 * dt + (quad >> 1)) ^ (row & 15);
+            *reinterpret_cast<u32x2 *>(ep + row * DV + unit * 8 + 4 * (quad & 1)) = pk;
         }
+    }
+    uint16_t *outg = (uint16_t *)a.out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + (lane >> 4), c = lane & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * DV + ((c ^ (row & 15)) * 8));
+        const int r = 32 * w + row;
+        const int local = qb * BQ + r / G;
+        if (local < len)
+            st16(outg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DV + 8 * c, v);
     }
 }
 
