@@ -35,6 +35,29 @@ METRIC = "SWA decode HBM GB/s (% peak) + SWA prefill TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 DEV = "cuda:0"
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_window_amd", "csrc")
+
+# HBM bytes per call read by the TCC counters (FETCH_SIZE / WRITE_SIZE, scaled
+# by a plain copy of known size) for the kernel sources whose digest is given;
+# profiles/swa_prefill_4x8192_hbm_traffic.md and
+# profiles/swa_decode_256seq_hbm_traffic.md hold the runs.  Reported as null
+# once those sources differ from the ones measured.
+MEASURED_TRAFFIC = {
+    # band kernel 1510.2 MB + ring commit 2.7 MB read / 2.6 MB written
+    "swa_prefill": (1515.5e6, ("swa_prefill.hip", "generic_attn.hip"), "8b53b54d869ea5bc"),
+    "swa_decode": (178.36e6, ("swa_decode.hip",), "a29143a54058a654"),
+}
+
+
+def measured_traffic(call):
+    """Counter-measured HBM bytes per call, or None if the kernel changed."""
+    import hashlib
+    nbytes, files, digest = MEASURED_TRAFFIC[call]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return nbytes if h.hexdigest()[:16] == digest else None
 
 
 def warm(fn, stream, seconds=0.3):
@@ -109,6 +132,20 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream):
         rope=dict(ms=t_rope, bytes=rope_bytes, gbs=rope_bytes / t_rope / 1e6,
                   frac_hbm_peak=rope_bytes / t_rope / 1e6 / HBM_PEAK_GBS,
                   workload="RoPE + staging write of 32768 tokens (64 q / 8 KV heads)"))
+
+
+def bench_copy(steps, stream, nbytes=1 << 30):
+    """Plain device-to-device copy of `nbytes` (torch's copy kernel): the
+    reference for scaling the HBM byte counters of a profiled run (it reads
+    and writes exactly nbytes per launch)."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=DEV).normal_()
+    dst = torch.empty_like(src)
+
+    def call(i):
+        dst.copy_(src)
+    warm(call, stream)
+    t = ev_time(call, max(steps, 10), stream)
+    return dict(ms=t, bytes=2 * nbytes, gbs=2 * nbytes / t / 1e6, read_bytes=nbytes, write_bytes=nbytes)
 
 
 def bench_swa_decode(hsw, wl, steps, stream, replicas=8):
@@ -331,7 +368,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="only the two metric calls")
-    ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid"],
+    ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid", "copy"],
                     help="run one call's timing only (for profiling) and print its numbers")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -348,7 +385,8 @@ def main():
               "swa_decode": lambda: bench_swa_decode(hsw, wl, args.steps, stream),
               "full_decode": lambda: bench_full_decode(hsw, wl, args.steps, stream),
               "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream),
-              "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream)}[args.only]
+              "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream),
+              "copy": lambda: bench_copy(args.steps, stream)}[args.only]
         r = fn()
         print(json.dumps({"only": args.only, **{k: v for k, v in r.items() if not isinstance(v, dict)}}))
         return
@@ -395,11 +433,12 @@ def main():
                    "global_batch": 4, "seq_len": 8192, "parallelism": "single GPU"},
         "swa_decode": {"value": round(dec["gbs"], 1), "unit": "GB/s",
                        "frac_hbm_peak": round(dec["frac_hbm_peak"], 4), "us_per_call": round(dec["ms"] * 1e3, 2),
+                       "traffic": measured_traffic("swa_decode"),
                        "workload": dec["workload"]},
         "swa_prefill_frac_mfma_peak": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "swa_prefill (band kernel + ring commit), 1.513 GB algorithmic per call"},
+                     "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic("swa_prefill"),
+                     "kernel": "hsw_swa_prefill call (band kernel + ring commit), 1.513 GB algorithmic per call"},
         "calls": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in calls.items()},
     }
