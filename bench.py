@@ -235,104 +235,28 @@ def bench_full_prefill(hsw, wl, steps, stream):
 
 
 def bench_hybrid(hsw, wl, steps, stream):
-    """One hybrid step: 48 attention-only layers (39 windowed, 9 full at
-    seeded indices), each running RoPE + prefill for an 8192-token chunk at
-    positions 131072..139263 and RoPE + decode for 128 sequences with contexts
-    U{4096..262144}.  Per-layer q/k/v are generated before timing; the 9 full
-    layers share one pool (their bytes read per layer are the same)."""
-    T, S = 8192, 128
-    P0 = 131072
-    pattern = wl.hybrid_pattern(seed=5)
-    g = wl.gen(5)
-    L = torch.randint(4096, 262144 + 1, (S,), generator=g, dtype=torch.int64)
-    swa, full = wl.swa_shape(), wl.full_shape()
-    gd = wl.gen(5000, DEV)
-    layers = []
-    for li, kind in enumerate(pattern):
-        hkv = 8 if kind == 1 else 4
-        layers.append(dict(
-            qc=wl.randn((T, 64, 192), gd, device=DEV), kc=wl.randn((T, hkv, 192), gd, device=DEV),
-            vc=wl.randn((T, hkv, 128), gd, device=DEV), qd=wl.randn((S, 64, 192), gd, device=DEV),
-            kd=wl.randn((S, hkv, 192), gd, device=DEV), vd=wl.randn((S, hkv, 128), gd, device=DEV)))
-        if kind == 1:
-            # rings: decode sequences 0..S-1, the chunk's sequence at index S
-            layers[-1]["kring"] = wl.randn((S + 1, 8, 128, 192), gd, device=DEV)
-            layers[-1]["vring"] = wl.randn((S + 1, 8, 128, 128), gd, device=DEV)
-    sinks = wl.sinks(64, g).to(DEV)
-    # shared full-attention pool: chunk sequence rows [0, P0 + T), then decode sequences
-    base_dec = torch.zeros(S, dtype=torch.int64)
-    base_dec[0] = P0 + T
-    base_dec[1:] = P0 + T + torch.cumsum(L, 0)[:-1]
-    rows = int(P0 + T + L.sum())
-    kpool = wl.randn((rows, 4, 192), gd, device=DEV)
-    vpool = wl.randn((rows, 4, 128), gd, device=DEV)
-    d_L, d_base_dec = L.to(DEV), base_dec.to(DEV)
-    d_pos_dec = (L - 1).to(DEV)
-    d_seq_dec = torch.arange(S, dtype=torch.int32, device=DEV)
-    d_pos_c = torch.arange(P0, P0 + T, dtype=torch.int64, device=DEV)
-    d_seq_c0 = torch.zeros(T, dtype=torch.int32, device=DEV)
-    d_seq_cS = torch.full((T,), S, dtype=torch.int32, device=DEV)
-    d_cu = torch.tensor([0, T], dtype=torch.int64, device=DEV)
-    d_start = torch.tensor([P0], dtype=torch.int64, device=DEV)
-    d_base_c = torch.zeros(1, dtype=torch.int64, device=DEV)
-    q_rot = torch.empty((T, 64, 192), dtype=torch.bfloat16, device=DEV)
-    q_rot_d = torch.empty((S, 64, 192), dtype=torch.bfloat16, device=DEV)
-    kst = torch.empty((T, 8, 192), dtype=torch.bfloat16, device=DEV)
-    vst = torch.empty((T, 8, 128), dtype=torch.bfloat16, device=DEV)
-    out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=DEV)
-    out_d = torch.empty((S, 64, 128), dtype=torch.bfloat16, device=DEV)
-    max_ctx = int(L.max())
-    wsb = hsw.hsw_full_decode_workspace_bytes(full, S, max_ctx, 2048)
-    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=DEV)
-    kinds = {"rope": 0.0, "swa_prefill": 0.0, "swa_decode": 0.0, "full_prefill": 0.0, "full_decode": 0.0}
-
-    def step(timer=None):
-        def run(kind, fn):
-            if timer is None:
-                fn()
-            else:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                timer.append((kind, e0, e1))
-        for li, kind in enumerate(pattern):
-            d = layers[li]
-            if kind == 1:
-                run("rope", lambda: hsw.hsw_rope_partial_kv_write(swa, T, d["qc"], d["kc"], d["vc"], d_pos_c, None,
-                                                                  hsw.HSW_DST_STAGING, kst, vst, T, None, q_rot, None, stream))
-                run("swa_prefill", lambda: hsw.hsw_swa_prefill(
-                    swa, 1, T, d_cu, d_start, q_rot, kst, vst, d["kring"][S:], d["vring"][S:], sinks, out, stream))
-                run("rope", lambda: hsw.hsw_rope_partial_kv_write(swa, S, d["qd"], d["kd"], d["vd"], d_pos_dec, d_seq_dec,
-                                                                  hsw.HSW_DST_RING, d["kring"], d["vring"], S + 1, None,
-                                                                  q_rot_d, None, stream))
-                run("swa_decode", lambda: hsw.hsw_swa_decode(swa, S, d_pos_dec, q_rot_d, d["kring"], d["vring"], sinks,
-                                                             out_d, stream))
-            else:
-                run("rope", lambda: hsw.hsw_rope_partial_kv_write(full, T, d["qc"], d["kc"], d["vc"], d_pos_c, d_seq_c0,
-                                                                  hsw.HSW_DST_POOL, kpool, vpool, rows, d_base_c, q_rot,
-                                                                  None, stream))
-                run("full_prefill", lambda: hsw.hsw_full_prefill_chunk(full, 1, T, d_cu, d_start, d_base_c, q_rot, kpool,
-                                                                       vpool, rows, None, out, stream))
-                run("rope", lambda: hsw.hsw_rope_partial_kv_write(full, S, d["qd"], d["kd"], d["vd"], d_pos_dec, d_seq_dec,
-                                                                  hsw.HSW_DST_POOL, kpool, vpool, rows, d_base_dec, q_rot_d,
-                                                                  None, stream))
-                run("full_decode", lambda: hsw.hsw_full_decode_splitk(full, S, max_ctx, d_L, d_base_dec, q_rot_d, kpool,
-                                                                      vpool, rows, None, 2048, ws, wsb, out_d, stream))
-    step()
+    """One hybrid step (hybrid_sliding_window_amd.hybrid.HybridStep): 48
+    attention-only layers (39 windowed, 9 full at seeded indices), each running
+    RoPE + prefill for an 8192-token chunk at positions 131072..139263 and RoPE
+    + decode for 128 sequences with contexts U{4096..262144}."""
+    from hybrid_sliding_window_amd.hybrid import HybridStep
+    hs = HybridStep(hsw, device=DEV)
+    hs.step(stream)
     torch.cuda.synchronize()
     n = max(1, steps)
-    t = ev_time(lambda i: step(), n, stream)
+    t = ev_time(lambda i: hs.step(stream), n, stream)
     timer = []
-    step(timer)
+    hs.step(stream, timer)
     torch.cuda.synchronize()
+    kinds = {"rope": 0.0, "swa_prefill": 0.0, "swa_decode": 0.0, "full_prefill": 0.0, "full_decode": 0.0}
     for kind, e0, e1 in timer:
         kinds[kind] += e0.elapsed_time(e1)
-    pool_gb = rows * 4 * 320 * 2 / 1e9
-    return dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps=n, per_call_ms={k: round(v, 3) for k, v in kinds.items()},
-                layers="39 windowed + 9 full (seeded pattern)", pool_gb=round(pool_gb, 1),
-                workload="hybrid step: 48 layers, 8192-token chunk at 131072 + 128 decode sequences U{4096..262144}")
+    T, S = hs.T, hs.S
+    res = dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps=n, per_call_ms={k: round(v, 3) for k, v in kinds.items()},
+               layers="39 windowed + 9 full (seeded pattern)", pool_gb=round(hs.pool_gb, 1),
+               workload="hybrid step: 48 layers, 8192-token chunk at 131072 + 128 decode sequences U{4096..262144}")
+    del hs
+    return res
 
 
 def cpu_baseline(target_s=15.0, max_seqs=64):

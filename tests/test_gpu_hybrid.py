@@ -1,0 +1,136 @@
+"""GPU parity of the hybrid step at its full size (sampled).
+
+One windowed and one full layer of the hybrid step (8192-token chunk at
+positions 131072..139263, 128 decode sequences with contexts
+U{4096..262144}, 64 q heads; 8 / 4 KV heads) run through the same driver the
+bench times (hybrid_sliding_window_amd.hybrid.HybridStep).  After each call
+its sampled outputs are checked against the fp64 oracle fed the exact tensors
+the call consumed: RoPE rows within one bf16 ulp, written cache rows exact,
+attention rows to max_abs 2e-2 / mean_rel 2e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import bf16_ulp, f64, linear_kv_from_ring, note, shape_kw
+from parity import assert_close
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+hsw = pytest.importorskip("hybrid_sliding_window_amd.hsw")
+from hybrid_sliding_window_amd.hybrid import HybridStep  # noqa: E402
+
+
+def check_rope(x_in, y, pos, theta, what):
+    ref = oracle.rope(f64(x_in), pos, theta)
+    err = np.abs(f64(y) - ref)
+    tol = bf16_ulp(ref) + 1e-6
+    assert np.all(err <= tol), f"{what}: rope off by up to {float((err - tol).max()):.3e} beyond one bf16 ulp"
+
+
+@pytest.fixture(scope="module")
+def hs():
+    note("hybrid step: building one windowed + one full layer at full size")
+    h = HybridStep(hsw, pattern=[1, 0])
+    yield h
+    del h
+    torch.cuda.empty_cache()
+
+
+def test_hybrid_windowed_layer_sampled(hs):
+    T, S, P0 = hs.T, hs.S, hs.P0
+    d = hs.layers[0]
+    swa = hs.swa
+    calls = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(0)))
+    g = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(0, 130), [T - 2, T - 1], g.choice(np.arange(130, T - 2), 30)]))
+
+    note("hybrid windowed: rope (chunk -> staging)")
+    calls["rope0"]()
+    torch.cuda.synchronize()
+    pos_c = np.arange(P0, P0 + T)
+    check_rope(d["qc"][rows], hs.q_rot[rows], pos_c[rows], swa.rope_theta, "chunk q")
+    check_rope(d["kc"][rows], hs.kst[rows], pos_c[rows], swa.rope_theta, "chunk k")
+    assert torch.equal(hs.vst.cpu(), d["vc"].cpu())
+
+    note("hybrid windowed: swa prefill (ring keys before the chunk)")
+    kring_s, vring_s = f64(d["kring"][S]), f64(d["vring"][S])   # before the commit
+    calls["swa_prefill1"]()
+    torch.cuda.synchronize()
+    k, v, kpos0 = linear_kv_from_ring(kring_s, vring_s, P0, f64(hs.kst), f64(hs.vst))
+    ref = oracle.attn_linear(f64(hs.q_rot[rows]), pos_c[rows], k, v, kpos0, window=128,
+                             sinks=f64(hs.sinks), **shape_kw(swa))
+    ma, mr = assert_close(f64(hs.out[rows]), ref, what="hybrid swa_prefill")
+    print(f"hybrid swa_prefill sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    # the commit left the chunk's last 128 rows in slots p mod 128
+    last = np.arange(T - 128, T)
+    slots = (P0 + last) % 128
+    assert torch.equal(d["kring"][S][:, slots].cpu(), hs.kst[last].permute(1, 0, 2).cpu())
+    assert torch.equal(d["vring"][S][:, slots].cpu(), hs.vst[last].permute(1, 0, 2).cpu())
+
+    note("hybrid windowed: rope (decode tokens -> ring)")
+    calls["rope2"]()
+    torch.cuda.synchronize()
+    P = hs.L.numpy() - 1
+    check_rope(d["qd"], hs.q_rot_d, P, swa.rope_theta, "decode q")
+    kn = oracle.rope(f64(d["kd"]), P, swa.rope_theta)
+    written = f64(d["kring"][torch.arange(S), :, torch.from_numpy(P % 128)])
+    assert np.all(np.abs(written - kn) <= bf16_ulp(kn) + 1e-6)
+
+    note("hybrid windowed: swa decode")
+    calls["swa_decode3"]()
+    torch.cuda.synchronize()
+    seqs = sorted({int(P.argmin()), int(P.argmax()), 5, 77})
+    ref = oracle.ring_decode(f64(hs.q_rot_d[seqs]), P[seqs], f64(d["kring"][seqs]), f64(d["vring"][seqs]),
+                             sinks=f64(hs.sinks), **shape_kw(swa))
+    ma, mr = assert_close(f64(hs.out_d[seqs]), ref, what="hybrid swa_decode")
+    print(f"hybrid swa_decode sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_hybrid_full_layer_sampled(hs):
+    T, S, P0 = hs.T, hs.S, hs.P0
+    d = hs.layers[1]
+    full = hs.full
+    calls = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(1)))
+    rows = np.array([0, 1, 2, 1000, 4095, 6000, 8190, 8191])
+
+    note("hybrid full: rope (chunk -> pool)")
+    calls["rope0"]()
+    torch.cuda.synchronize()
+    pos_c = np.arange(P0, P0 + T)
+    check_rope(d["qc"][rows], hs.q_rot[rows], pos_c[rows], full.rope_theta, "chunk q (full)")
+    check_rope(d["kc"][rows], hs.kpool[P0 + rows], pos_c[rows], full.rope_theta, "chunk k -> pool")
+    assert torch.equal(hs.vpool[P0:P0 + T].cpu(), d["vc"].cpu())
+
+    note("hybrid full: full prefill over 139264 pool rows")
+    calls["full_prefill1"]()
+    torch.cuda.synchronize()
+    k, v = f64(hs.kpool[:P0 + T]), f64(hs.vpool[:P0 + T])
+    ref = oracle.attn_linear(f64(hs.q_rot[rows]), pos_c[rows], k, v, 0, window=0, **shape_kw(full))
+    del k, v
+    ma, mr = assert_close(f64(hs.out[rows]), ref, what="hybrid full_prefill")
+    print(f"hybrid full_prefill sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+    note("hybrid full: rope (decode tokens -> pool)")
+    calls["rope2"]()
+    torch.cuda.synchronize()
+    L, base = hs.L.numpy(), hs.base_dec.numpy()
+    check_rope(d["qd"], hs.q_rot_d, L - 1, full.rope_theta, "decode q (full)")
+    check_rope(d["kd"], hs.kpool[torch.from_numpy(base + L - 1)], L - 1, full.rope_theta, "decode k -> pool")
+
+    note("hybrid full: split-K full decode")
+    calls["full_decode3"]()
+    torch.cuda.synchronize()
+    seqs = sorted({int(L.argmin()), int(L.argmax()), 9})
+    got, refs = [], []
+    qd = f64(hs.q_rot_d)
+    for s in seqs:
+        k = f64(hs.kpool[base[s]:base[s] + L[s]])
+        v = f64(hs.vpool[base[s]:base[s] + L[s]])
+        refs.append(oracle.attn_linear(qd[s:s + 1], [L[s] - 1], k, v, 0, window=0, **shape_kw(full))[0])
+        got.append(f64(hs.out_d[s]))
+    ma, mr = assert_close(np.stack(got), np.stack(refs), what="hybrid full_decode")
+    print(f"hybrid full_decode sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
