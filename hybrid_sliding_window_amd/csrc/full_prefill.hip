@@ -11,22 +11,25 @@
 // values carry the value scale (applied to the fp32 output).
 //
 // MFMA-bound (~6.6e4 flop/B for an 8192-token chunk after 131072 rows).
-// One workgroup (4 waves) per (sequence, KV head, 128/G query positions):
-// 128 query rows = the G heads of each position as 16-wide MFMA columns, two
-// column tiles per wave.  Keys stream through LDS in 32-row chunks, double
-// buffered (the next chunk's global loads are in flight while the current one
-// computes; one barrier per chunk):
+// One workgroup (4 waves) per query block: 128 rows = 128/G positions x the G
+// query heads of one KV head (the heads are the 16-wide MFMA columns), two
+// column tiles per wave.  The block's keys (pool rows base + 0 .. base +
+// its last position) stream through LDS in 32-key chunks with a three-stage
+// pipeline: chunk c+2 is fetched by direct global->LDS 16-byte loads (no VGPR
+// staging) while chunk c is computed, one barrier per chunk; each wave skips
+// chunks past its rows' positions.  Per chunk:
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16 (K rows from LDS, q in VGPRs)
-//   softmax          online, log2 units; the reference max is raised only when
-//                    a chunk's max exceeds it by more than 2^8 (P <= 256), so
-//                    the O rescale is rare
-//   O^T += V^T P^T   v_mfma_f32_16x16x32_f16 on fp16 P and fp16 V; the V^T
-//                    operand comes straight from row-major V in LDS through the
-//                    gfx950 transposing read (ds_read_b64_tr_b16).
-// V is converted bf16 -> fp16 once per chunk when it enters LDS (exact for
-// |v| < 65520).  A bf16 copy is kept beside it: a chunk holding a value
-// outside fp16 range is computed exactly instead, with bf16 V^T and P split
-// into bf16 hi + lo (two MFMAs).
+//   softmax          online in log2 units; the reference max is raised only
+//                    when a chunk's max exceeds it by more than 2^8 (P <= 256),
+//                    so the O rescale is rare
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P split into bf16 hi + lo
+//                    (about 16 significant bits, V exact in bf16); the V^T
+//                    operand is read from row-major V by ds_read_b64_tr_b16.
+// LDS holds K and V in MFMA fragment order (the load side places each
+// 16-byte piece where a lane will read it), so every LDS read is a contiguous
+// run in lane order, free of bank conflicts.  Block ids are remapped so
+// consecutive query blocks of one (sequence, KV head) run on one XCD and
+// stream the same keys through its L2.
 #include "hsw_device.h"
 #include "hsw_launch.h"
 
@@ -36,20 +39,60 @@ namespace {
 constexpr int DQK = 192, DV = 128;
 constexpr int STEPS = DQK / 32;
 constexpr int DT = DV / 16;
-constexpr int KC = 32;                     // keys per chunk
-constexpr int KS_STRIDE = DQK + 8;         // bf16 per K row in LDS
-constexpr int VS_STRIDE = DV + 16;         // 16-bit elements per V row in LDS
-constexpr int K_STAGE = KC * KS_STRIDE;
-constexpr int V_STAGE = KC * VS_STRIDE;
+constexpr int KC = 32;                      // keys per chunk
+constexpr int K_PIECES = KC * DQK / 8;      // 16-byte pieces per K stage (768)
+constexpr int V_PIECES = KC * DV / 8;       // per V stage (512)
 constexpr int kThreads = 256;
+constexpr int K_LOADS = K_PIECES / kThreads;  // 3 per thread
+constexpr int V_LOADS = V_PIECES / kThreads;  // 2 per thread
+constexpr int LOADS = K_LOADS + V_LOADS;      // vector-memory ops per chunk per thread
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;
 
+// s_waitcnt immediates (gfx9 encoding): wait until at most N vector-memory
+// ops of this wave are outstanding; expcnt and lgkmcnt left unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0).  Issued
+// as inline asm so the compiler does not track it: it would otherwise add
+// waits of its own before some LDS reads, for more of these loads than the
+// read needs.  Completion is awaited explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes a stage; m0 is used by nothing else in this kernel.
+__device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave_base) {
+    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
+}
+
+// 16-byte global load into v, untracked like the loads above (v keeps its
+// register; the first wait of the pipeline covers it, as it was issued first).
+__device__ __forceinline__ void load_q16(u32x4 &v, const void *src) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(v) : "v"(src) : "memory");
+}
+
+// Max / sum over the four quads (lanes c, c+16, c+32, c+48) with the gfx950
+// half-wave and row swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float quad_max_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float quad_sum_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
+// Transposing LDS read.  The pointer is cast straight to the LDS address
+// space (not through an integer) so the read keeps the alias scope of its LDS
+// array: the compiler then makes it wait only for loads into that array, not
+// for the loads in flight to the other stages.
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(const void *)p);
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     return __builtin_bit_cast(u32x2, v);
 }
 
@@ -59,104 +102,120 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return (bid % 8) * (total / 8) + bid / 8;
 }
 
-struct ChunkRegs {
-    u32x4 k[3];  // 768 K chunks (32 keys x 24) over 256 threads
-    u32x4 v[2];  // 512 V chunks (32 keys x 16)
-};
-
 template <int G>
-__global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, int nqb) {
     constexpr int BQ = 128 / G;
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][K_STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t vs16[2][V_STAGE];  // fp16
-    __shared__ __attribute__((aligned(16))) uint16_t vsbf[2][V_STAGE];  // bf16
+    // Three stages, each its own LDS object so the compiler can tell that a
+    // read of one stage does not depend on the loads in flight to another.
+    __shared__ __attribute__((aligned(1024))) uint16_t ks0[KC * DQK], ks1[KC * DQK], ks2[KC * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs0[KC * DV], vs1[KC * DV], vs2[KC * DV];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
     const int quad = lane >> 4, col = lane & 15;
-    const int nqb = (int)((a.max_seqlen + BQ - 1) / BQ);
     const int total = a.n_seqs * a.hkv * nqb;
     const int bid = xcd_remap(blockIdx.x, total);
-    const int qblk = bid % nqb;
+    const int qb = bid % nqb;
     const int g = (bid / nqb) % a.hkv;
     const int s = bid / (nqb * a.hkv);
 
     const int64_t tok0 = a.cu_seqlens[s];
     const int len = (int)(a.cu_seqlens[s + 1] - tok0);
-    const int local0 = qblk * BQ;
-    if (local0 >= len) return;
+    if (qb * BQ >= len) return;
     const int start = (int)a.start_pos[s];
-    const int p0 = start + local0;
-    const int plast = start + min(len, local0 + BQ) - 1;  // last query position of the block
+    const int p0 = start + qb * BQ;                         // first query position
+    const int plast = start + min(len, qb * BQ + BQ) - 1;   // last query position
     const int64_t base = a.seq_base[s];
-    // Keys are rows base + 0 .. base + plast, clamped to the pool.
+    // Keys are pool rows base + 0 .. base + plast, clamped to the pool.
     int nkeys = plast + 1;
     if (base + nkeys > a.pool_rows) nkeys = (int)(a.pool_rows - base);
-    if (base < 0) nkeys = 0;
+    if (base < 0 || nkeys < 0) nkeys = 0;
+    const int klast = max(nkeys - 1, 0);
+    const int nch = max((nkeys + KC - 1) / KC, 1);
 
+    // q of this wave's rows (row r = 32w + 16n + col -> position r / G, head
+    // r % G), from a clamped row so the load is unconditional; rows past the
+    // block only affect their own column and are never stored.
+    u32x4 qv[2][STEPS];
     const uint16_t *qg = (const uint16_t *)a.q;
-    // Uniform per-workgroup bases of this sequence's K/V rows for KV head g;
-    // per-thread 32-bit byte offsets from them (row stride hkv * 384 / 256 B;
-    // the host bounds contexts so the offsets fit).
-    const char *kseq = (const char *)a.k_main + ((base < 0 ? 0 : base) * a.hkv + g) * (int64_t)(DQK * 2);
-    const char *vseq = (const char *)a.v_main + ((base < 0 ? 0 : base) * a.hkv + g) * (int64_t)(DV * 2);
-    const uint32_t krow = (uint32_t)a.hkv * DQK * 2, vrow = (uint32_t)a.hkv * DV * 2;
-
-    // q of this wave's rows (row r = 32w + 16n + col -> position r / G, head r % G),
-    // from a clamped row so the load is unconditional.
-    u32x4 qb[2][STEPS];
-    int qpos[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         int r = 32 * w + 16 * n + col;
-        int local = min(local0 + r / G, len - 1);
-        qpos[n] = p0 + r / G;
+        int local = min(qb * BQ + r / G, len - 1);
         const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) qb[n][st] = ld16(qrow + 32 * st + 8 * quad);
+        for (int st = 0; st < STEPS; ++st) {
+            qv[n][st] = u32x4{0, 0, 0, 0};
+            load_q16(qv[n][st], qrow + 32 * st + 8 * quad);
+        }
     }
-    const int wpos_lo = p0 + (32 * w) / G, wpos_hi = p0 + (32 * w + 31) / G;
-    const int nchunks = (nkeys + KC - 1) / KC;
 
-    auto load_chunk = [&](int c, ChunkRegs &r) {
+    // This sequence's K/V rows for KV head g.
+    const int64_t b0 = base < 0 ? 0 : base;
+    const char *kseq = (const char *)a.k_main + (b0 * a.hkv + g) * (int64_t)(DQK * 2);
+    const char *vseq = (const char *)a.v_main + (b0 * a.hkv + g) * (int64_t)(DV * 2);
+    const int64_t krow = (int64_t)a.hkv * DQK * 2, vrow = (int64_t)a.hkv * DV * 2;
+
+    // LDS layout: fragment order.  K: 16-byte unit (h * 6 + st) * 64 + lane
+    // holds what lane (quad, col) feeds the S^T MFMA of key half h, step st:
+    // K[16h + col][pieces 4st + quad].  V: 8-byte unit (hh * 8 + dt) * 64 +
+    // lane holds what lane (quad, 4k + mm) supplies to the transposing read of
+    // key half hh, output tile dt: V[16hh + 4quad + k][16dt + 4mm .. +3].  The
+    // i-th 16-byte load of wave w fills units (4i + w) * 64 + lane:
+    //   K load i: j = 4i + w, h = j / 6, st = j % 6: key 16h + col, bytes
+    //             64 st + 16 quad.
+    //   V load i: j = 4i + w, hh = j / 4, tiles 2 (j % 4) + (lane >> 5); with
+    //             u = lane & 31: row 16hh + 4 (u >> 3) + ((u >> 1) & 3), bytes
+    //             64 (j % 4) + 32 (lane >> 5) + 16 (u & 1).
+    const int u = lane & 31;
+    const int vrow_l = 4 * (u >> 3) + ((u >> 1) & 3);
+    const int vbyte_l = 32 * (lane >> 5) + 16 * (u & 1);
+    const int64_t koff_l = col * krow + 16 * quad;
+    const int64_t voff_l = vrow_l * vrow + vbyte_l;
+
+    // Chunk c's loads.  Keys past the last one are clamped to it (finite
+    // data, masked); past the band a dummy set (the first row, again) keeps
+    // the number of loads per step constant.
+    auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd) {
         const int k0 = c * KC;
+        const char *ksrc[K_LOADS], *vsrc[V_LOADS];
+        if (c >= nch) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            int cc = threadIdx.x + kThreads * i;
-            uint32_t key = (uint32_t)min(k0 + cc / (DQK / 8), nkeys - 1);
-            r.k[i] = ld16(kseq + (key * krow + 16u * (uint32_t)(cc % (DQK / 8))));
-        }
+            for (int i = 0; i < K_LOADS; ++i) ksrc[i] = kseq;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int cc = threadIdx.x + kThreads * i;
-            uint32_t key = (uint32_t)min(k0 + cc / (DV / 8), nkeys - 1);
-            r.v[i] = ld16(vseq + (key * vrow + 16u * (uint32_t)(cc % (DV / 8))));
-        }
-    };
-    // Returns true if this thread's V values include one outside fp16 range.
-    auto store_chunk = [&](int buf, const ChunkRegs &r) -> bool {
+            for (int i = 0; i < V_LOADS; ++i) vsrc[i] = vseq;
+        } else if (k0 + KC - 1 <= klast) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            int cc = threadIdx.x + kThreads * i;
-            *reinterpret_cast<u32x4 *>(&ks[buf][(cc / (DQK / 8)) * KS_STRIDE + 8 * (cc % (DQK / 8))]) = r.k[i];
-        }
-        bool bad = false;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int cc = threadIdx.x + kThreads * i;
-            int off = (cc / (DV / 8)) * VS_STRIDE + 8 * (cc % (DV / 8));
-            *reinterpret_cast<u32x4 *>(&vsbf[buf][off]) = r.v[i];
-            u32x4 h;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                h[j] = bf16x2_to_f16x2(r.v[i][j]);
-                bad |= ((h[j] & 0x7c00u) == 0x7c00u) | ((h[j] & 0x7c000000u) == 0x7c000000u);
+            for (int i = 0; i < K_LOADS; ++i) {
+                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
+                ksrc[i] = kseq + (int64_t)(k0 + 16 * h) * krow + 64 * st + koff_l;
             }
-            *reinterpret_cast<u32x4 *>(&vs16[buf][off]) = h;
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int j = 4 * i + w, hh = j / 4;
+                vsrc[i] = vseq + (int64_t)(k0 + 16 * hh) * vrow + 64 * (j % 4) + voff_l;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < K_LOADS; ++i) {
+                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
+                const int kp = min(k0 + 16 * h + col, klast);
+                ksrc[i] = kseq + (int64_t)kp * krow + 64 * st + 16 * quad;
+            }
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int j = 4 * i + w, hh = j / 4;
+                const int kp = min(k0 + 16 * hh + vrow_l, klast);
+                vsrc[i] = vseq + (int64_t)kp * vrow + 64 * (j % 4) + vbyte_l;
+            }
         }
-        return bad;
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) load_lds16(ksrc[i], (const char *)ksd + (4 * i + w) * 1024);
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) load_lds16(vsrc[i], (const char *)vsd + (4 * i + w) * 1024);
     };
 
+    const float scale2 = a.scale * kLog2e;
     f32x4 oacc[2][DT];
     float m[2], l[2];
 #pragma unroll
@@ -166,126 +225,130 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
     }
-    const float scale2 = a.scale * kLog2e;
-    // transposing-read lane roles: within a quad's 16 lanes, lane 4k + mm
-    // supplies row (4 quad + k) of a 16-key half, dims (16 dt + 4 mm) .. + 3
-    const int tr_row = 4 * quad + (col >> 2), tr_col = 4 * (col & 3);
+    const int wpos_lo = p0 + (32 * w) / G, wpos_hi = p0 + (32 * w + 31) / G;
+    // last key visible to the wave's rows / to its first row
+    const int vis_hi = min(wpos_hi, nkeys - 1), vis_lo = min(wpos_lo, nkeys - 1);
 
-    ChunkRegs regs;
-    bool bad = false;
-    if (nchunks > 0) {
-        load_chunk(0, regs);
-        bad = store_chunk(0, regs);
-    }
-    bool chunk_bad = __syncthreads_or(bad);
-    int buf = 0;
-    for (int c = 0; c < nchunks; ++c) {
-        const bool more = c + 1 < nchunks;
-        if (more) load_chunk(c + 1, regs);
+    auto step = [&](int c, const uint16_t *ksc, const uint16_t *vsc, uint16_t *ksn, uint16_t *vsn) {
+        // Own loads of chunk c done (chunk c+1's, the last LOADS issued, may
+        // still fly), then make every wave's visible.  The stage chunk c+2
+        // goes to was last read in step c-1, which every wave has finished
+        // once past this barrier.
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        issue(c + 2, ksn, vsn);
+
         const int k0 = c * KC;
-        // chunk wholly above every row of this wave: nothing to do (wave-uniform)
-        if (k0 <= wpos_hi) {
-            const bool interior = k0 + KC - 1 <= wpos_lo && k0 + KC <= nkeys;
-            float sv[2][2][4];  // [16-key half][n][j]
+        // skip a chunk no row of this wave can see (wave-uniform)
+        if (k0 > vis_hi) return;
+        // every key of the chunk visible to every row: no mask
+        const bool interior = k0 + KC - 1 <= vis_lo;
+        float sv[2][2][4];  // [16-key half][n][j]
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                u32x4 ak[STEPS];
+        for (int h = 0; h < 2; ++h) {
+            u32x4 ak[STEPS];
 #pragma unroll
-                for (int st = 0; st < STEPS; ++st)
-                    ak[st] = *reinterpret_cast<const u32x4 *>(&ks[buf][(16 * h + col) * KS_STRIDE + 32 * st + 8 * quad]);
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    f32x4 acc = f32x4{0, 0, 0, 0};
-#pragma unroll
-                    for (int st = 0; st < STEPS; ++st) acc = mfma_16x16x32_bf16(ak[st], qb[n][st], acc);
-                    if (interior) {  // wave-uniform: no per-element mask
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) sv[h][n][j] = acc[j];
-                    } else {
-                        const int d = min(qpos[n], nkeys - 1) - (k0 + 16 * h + 4 * quad);  // key j visible iff j <= d
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) sv[h][n][j] = j <= d ? acc[j] : -INFINITY;
-                    }
-                }
-            }
-            u32x4 bhi[2], blo[2];
+            for (int st = 0; st < STEPS; ++st)
+                ak[st] = *reinterpret_cast<const u32x4 *>(ksc + ((h * STEPS + st) * 64 + lane) * 8);
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                float cm = fmaxf(fmaxf(fmaxf(sv[0][n][0], sv[0][n][1]), fmaxf(sv[0][n][2], sv[0][n][3])),
-                                 fmaxf(fmaxf(sv[1][n][0], sv[1][n][1]), fmaxf(sv[1][n][2], sv[1][n][3])));
-                cm = quad_max(cm) * scale2;
-                const bool raise = cm > m[n] + kRescale;
-                if (__any(raise)) {
-                    const float mn = raise ? cm : m[n];
+                f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st) acc = mfma_16x16x32_bf16(ak[st], qv[n][st], acc);
+                if (interior) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][n][j] = acc[j];
+                } else {
+                    // key j of this lane is visible iff key <= min(qpos, nkeys - 1)
+                    const int d = min(p0 + (32 * w + 16 * n + col) / G, nkeys - 1) - (k0 + 16 * h + 4 * quad);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][n][j] = j <= d ? acc[j] : -INFINITY;
+                }
+            }
+        }
+        u32x4 bhi[2], blo[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float cm = fmaxf(fmaxf(fmaxf(sv[0][n][0], sv[0][n][1]), fmaxf(sv[0][n][2], sv[0][n][3])),
+                             fmaxf(fmaxf(sv[1][n][0], sv[1][n][1]), fmaxf(sv[1][n][2], sv[1][n][3])));
+            cm = quad_max_swap(cm) * scale2;
+            const bool raise = cm > m[n] + kRescale;
+            if (__any(raise)) {
+                const float mn = raise ? cm : m[n];
+                // rows that have seen no key yet hold zeros: nothing to rescale
+                if (__any(raise && m[n] != -INFINITY)) {
                     const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
                     l[n] *= f;
-                    m[n] = mn;
                 }
-                const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
-                float pv[8];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pv[4 * h + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][n][j], scale2, mu));
-                        l[n] += pv[4 * h + j];
-                    }
-                if (!chunk_bad) {
-                    bhi[n] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
-                                   pack_f16x2(pv[6], pv[7])};
-                } else {
-                    u32x2 h0, l0, h1, l1;
-                    split_hi_lo(pv, h0, l0);
-                    split_hi_lo(pv + 4, h1, l1);
-                    bhi[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
-                    blo[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
-                }
+                m[n] = mn;
             }
-            // O^T += V^T P^T: slots 0-3 of a quad are keys 4quad.. of the first
-            // 16-key half, slots 4-7 the same keys of the second half, on both
-            // operands.
-            if (!chunk_bad) {
+            const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
+            float pv[8];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    u32x2 a0 = ds_read_tr16(&vs16[buf][tr_row * VS_STRIDE + 16 * dt + tr_col]);
-                    u32x2 a1 = ds_read_tr16(&vs16[buf][(16 + tr_row) * VS_STRIDE + 16 * dt + tr_col]);
-                    u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, bhi[n], oacc[n][dt]);
+                for (int j = 0; j < 4; ++j) {
+                    pv[4 * h + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][n][j], scale2, mu));
+                    l[n] += pv[4 * h + j];
                 }
-            } else {
+            u32x2 h0, l0, h1, l1;
+            split_hi_lo(pv, h0, l0);
+            split_hi_lo(pv + 4, h1, l1);
+            bhi[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+            blo[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+        }
+        // O^T += V^T P^T: slots 0-3 of a quad are keys 4quad.. of the first
+        // 16-key half, slots 4-7 the same keys of the second half, on both
+        // operands.
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    u32x2 a0 = ds_read_tr16(&vsbf[buf][tr_row * VS_STRIDE + 16 * dt + tr_col]);
-                    u32x2 a1 = ds_read_tr16(&vsbf[buf][(16 + tr_row) * VS_STRIDE + 16 * dt + tr_col]);
-                    u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        for (int dt = 0; dt < DT; ++dt) {
+            u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+            u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
+            u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        oacc[n][dt] = mfma_16x16x32_bf16(av, bhi[n], oacc[n][dt]);
-                        oacc[n][dt] = mfma_16x16x32_bf16(av, blo[n], oacc[n][dt]);
-                    }
-                }
+            for (int n = 0; n < 2; ++n) {
+                oacc[n][dt] = mfma_16x16x32_bf16(av, bhi[n], oacc[n][dt]);
+                oacc[n][dt] = mfma_16x16x32_bf16(av, blo[n], oacc[n][dt]);
             }
         }
-        if (more) {
-            // buf ^ 1 was last read in iteration c - 1, before the barrier that ended it
-            bad = store_chunk(buf ^ 1, regs);
-            chunk_bad = __syncthreads_or(bad);
-            buf ^= 1;
+    };
+
+    // No key row in the pool (base outside it): no load at all.
+    if (nkeys > 0) {
+        issue(0, ks0, vs0);
+        issue(1, ks1, vs1);
+        // Unrolled by the three stages; nested so that each step is reached
+        // only through the one before it (the compiler then knows which loads
+        // into a stage have landed).
+        for (int c = 0; c < nch; c += 3) {
+            step(c, ks0, vs0, ks2, vs2);
+            if (c + 1 < nch) {
+                step(c + 1, ks1, vs1, ks0, vs0);
+                if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1);
+            }
         }
+        // The dummy loads past the band must land before a stage is reused
+        // below (and before the workgroup's LDS is released).
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the q loads
     }
 
-    // Epilogue: an optional sink joins the denominator once; scale; store bf16.
-    uint16_t *outg = (uint16_t *)a.out;
+    // Epilogue: an optional sink joins the denominator once; scale; bf16.
+    // Each wave turns its 32 x 128 output tile around in LDS so that the
+    // stores cover whole 256-byte rows, four per instruction.  Tile row
+    // stride 256 B, 16-byte units xor-swizzled by (row & 15).
+    uint16_t *ep = (w == 0) ? ks0 : (w == 1) ? ks1 : (w == 2) ? ks2 : vs0;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-        int r = 32 * w + 16 * n + col;
-        int local = local0 + r / G;
-        float ll = quad_sum(l[n]);
-        if (local >= len) continue;
-        int head = r % G;
+        const int r = 32 * w + 16 * n + col;
+        float ll = quad_sum_swap(l[n]);
+        const int head = r % G;
         float mm = m[n], fac = 1.0f;
         if (a.sinks) {
             float sk = a.sinks[g * G + head] * kLog2e;
@@ -293,15 +356,26 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a) {
             fac = exp2f(mm - mf);
             ll = ll * fac + exp2f(sk - mf);
         }
-        float rs = ll > 0.0f ? a.value_scale * fac / ll : 0.0f;
-        uint16_t *orow = outg + ((tok0 + local) * a.hq + g * G + head) * (int64_t)DV;
+        const float rs = a.value_scale * fac / ll;
+        const int row = 16 * n + col;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            f32x4 o = oacc[n][dt];
-            u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * rs) | ((uint32_t)f2bf(o[1] * rs) << 16),
-                             (uint32_t)f2bf(o[2] * rs) | ((uint32_t)f2bf(o[3] * rs) << 16)};
-            *reinterpret_cast<u32x2 *>(orow + 16 * dt + 4 * quad) = pk;
+            const f32x4 o = oacc[n][dt];
+            const u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * rs) | ((uint32_t)f2bf(o[1] * rs) << 16),
+                                   (uint32_t)f2bf(o[2] * rs) | ((uint32_t)f2bf(o[3] * rs) << 16)};
+            const int unit = (2 * dt + (quad >> 1)) ^ (row & 15);
+            *reinterpret_cast<u32x2 *>(ep + row * DV + unit * 8 + 4 * (quad & 1)) = pk;
         }
+    }
+    uint16_t *outg = (uint16_t *)a.out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + (lane >> 4), c = lane & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * DV + ((c ^ (row & 15)) * 8));
+        const int r = 32 * w + row;
+        const int local = qb * BQ + r / G;
+        if (local < len)
+            st16(outg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DV + 8 * c, v);
     }
 }
 
@@ -317,13 +391,14 @@ hipError_t launch_full_prefill(const AttnArgs &a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int BQ = 128 / G;
     const int64_t nqb = (a.max_seqlen + BQ - 1) / BQ;
-    dim3 grid((unsigned)(a.n_seqs * a.hkv * nqb)), block(kThreads);
+    dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(kThreads);
+    const int nq = (int)nqb;
     switch (G) {
-        case 1: hipLaunchKernelGGL(full_prefill_kernel<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(full_prefill_kernel<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(full_prefill_kernel<4>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(full_prefill_kernel<8>, grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(full_prefill_kernel<16>, grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL(full_prefill_kernel<1>, grid, block, 0, s, a, nq); break;
+        case 2: hipLaunchKernelGGL(full_prefill_kernel<2>, grid, block, 0, s, a, nq); break;
+        case 4: hipLaunchKernelGGL(full_prefill_kernel<4>, grid, block, 0, s, a, nq); break;
+        case 8: hipLaunchKernelGGL(full_prefill_kernel<8>, grid, block, 0, s, a, nq); break;
+        default: hipLaunchKernelGGL(full_prefill_kernel<16>, grid, block, 0, s, a, nq); break;
     }
     return hipGetLastError();
 }
