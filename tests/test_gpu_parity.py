@@ -258,6 +258,8 @@ def oracle_swa_prefill_rows(batch, q_rot, kst, vst, kring_before, vring_before, 
     outs = []
     for s in range(len(st)):
         sel = np.arange(cu[s], cu[s + 1]) if rows is None else np.asarray(rows[s])
+        if sel.size == 0:
+            continue
         ks, vs = f64(kst[cu[s]:cu[s + 1]]), f64(vst[cu[s]:cu[s + 1]])
         k, v, kpos0 = linear_kv_from_ring(kr0[s], vr0[s], st[s], ks, vs)
         qpos = st[s] + (sel - cu[s])
@@ -428,6 +430,8 @@ def oracle_full_prefill(batch, q_rot, kpool, vpool, rows_per_seq):
     got_idx, refs = [], []
     for s, sel in enumerate(rows_per_seq):
         sel = np.asarray(sel)
+        if sel.size == 0:
+            continue
         n = st[s] + cu[s + 1] - cu[s]
         k = f64(kpool[base[s]:base[s] + n])
         v = f64(vpool[base[s]:base[s] + n])
@@ -470,3 +474,99 @@ def test_full_prefill_values_beyond_fp16_range():
     idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(2)])
     ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * float(np.abs(ref).max()), what="full_prefill large V")
     print(f"full_prefill large V: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+# ------------------------------------------------------- degenerate cases
+def test_swa_prefill_empty_and_single_token_sequences():
+    """Zero-length sequences inside a batch (no rows, ring untouched),
+    single-token chunks at position 0 and deep in a sequence, and a chunk
+    that starts at the last ring slot and wraps it."""
+    note("swa_prefill empty / single-token sequences")
+    batch = wl.swa_prefill_batch(seed=43, n_seqs=6, seqlens=(0, 1, 200, 0, 129, 1),
+                                 start_pos=(0, 7, 250, 40, 127, 0))
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb)])
+    ma, mr = assert_close(f64(out), ref, what="swa_prefill degenerate")
+    print(f"swa_prefill empty/single: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_full_prefill_empty_and_single_token_sequences():
+    """Zero-length chunks (one of them with no pool rows at all) and
+    single-token chunks, at position 0 and after prior rows."""
+    note("full_prefill empty / single-token sequences")
+    batch = wl.full_prefill_batch(seed=73, n_seqs=5, seqlens=(1, 0, 65, 1, 0), start_pos=(0, 500, 31, 4000, 0))
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    cu = batch["cu_seqlens"].tolist()
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(5)])
+    ma, mr = assert_close(f64(out)[idx], ref, what="full_prefill degenerate")
+    print(f"full_prefill empty/single: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_general_group_size_bf16():
+    """A q/KV head group of 3 (24 q heads over 8 KV heads, 12 over 4), which
+    the MFMA kernels do not take: every call goes through the wave-per-row
+    kernel in bf16 and must meet the same bars."""
+    note("general group size: swa_prefill hq=24 hkv=8")
+    b = wl.swa_prefill_batch(seed=44, n_seqs=2, seqlens=(150, 40), start_pos=(300, 0), hq=24, hkv=8)
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(b)
+    check_ring_commit(b, kst, vst, kb, vb, kring, vring)
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(b, q_rot, kst, vst, kb, vb)])
+    assert_close(f64(out), ref, what="swa_prefill G=3")
+
+    note("general group size: swa_decode hq=24 hkv=8")
+    b = wl.swa_decode_batch(seed=45, n_seqs=5, positions=[0, 3, 127, 128, 99999], hq=24, hkv=8)
+    q_rot, kring, vring, out, _ = run_swa_decode(b)
+    ref = oracle.ring_decode(f64(q_rot), b["pos"].numpy(), f64(kring), f64(vring), sinks=f64(b["sinks"]),
+                             **shape_kw(b["shape"]))
+    assert_close(f64(out), ref, what="swa_decode G=3")
+
+    note("general group size: full_decode hq=12 hkv=4")
+    b = wl.full_decode_batch(seed=46, n_seqs=3, lengths=[1, 300, 2500], hq=12, hkv=4, with_sinks=True)
+    q_rot, kpool, vpool, out = run_full_decode(b, 1024, b["sinks"])
+    ref = oracle_full_decode(b, q_rot, kpool, vpool, range(3), b["sinks"])
+    assert_close(f64(out), ref, what="full_decode G=3")
+
+    note("general group size: full_prefill hq=12 hkv=4")
+    b = wl.full_prefill_batch(seed=47, n_seqs=2, seqlens=(70, 33), start_pos=(200, 0), hq=12, hkv=4)
+    q_rot, kpool, vpool, out = run_full_prefill(b)
+    cu = b["cu_seqlens"].tolist()
+    idx, ref = oracle_full_prefill(b, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(2)])
+    assert_close(f64(out)[idx], ref, what="full_prefill G=3")
+
+
+def test_zero_sizes_launch_nothing():
+    """Calls with zero tokens, sequences or keys return without writing: on
+    real device buffers every output keeps its sentinel."""
+    note("zero-size calls")
+    swa, full = wl.swa_shape(), wl.full_shape()
+    bf = torch.bfloat16
+    q = torch.zeros((4, 64, 192), dtype=bf, device=DEV)
+    k8 = torch.zeros((4, 8, 192), dtype=bf, device=DEV)
+    v8 = torch.zeros((4, 8, 128), dtype=bf, device=DEV)
+    k4, v4 = k8[:, :4].contiguous(), v8[:, :4].contiguous()
+    ring_k = torch.full((2, 8, 128, 192), SENTINEL, dtype=bf, device=DEV)
+    ring_v = torch.full((2, 8, 128, 128), SENTINEL, dtype=bf, device=DEV)
+    pool_k = torch.full((8, 4, 192), SENTINEL, dtype=bf, device=DEV)
+    pool_v = torch.full((8, 4, 128), SENTINEL, dtype=bf, device=DEV)
+    q_rot = torch.full_like(q, SENTINEL)
+    out = torch.full((4, 64, 128), SENTINEL, dtype=bf, device=DEV)
+    pos = torch.zeros(4, dtype=torch.int64, device=DEV)
+    seq = torch.zeros(4, dtype=torch.int32, device=DEV)
+    base = torch.zeros(4, dtype=torch.int64, device=DEV)
+    cu = torch.zeros(5, dtype=torch.int64, device=DEV)
+    lens = torch.ones(4, dtype=torch.int64, device=DEV)
+    ws = torch.full((1024,), SENTINEL, dtype=torch.float32, device=DEV)
+    hsw.hsw_rope_partial_kv_write(swa, 0, q, k8, v8, pos, seq, RING, ring_k, ring_v, 2, None, q_rot)
+    hsw.hsw_rope_partial_kv_write(full, 0, q, k4, v4, pos, seq, POOL, pool_k, pool_v, 8, base, q_rot)
+    hsw.hsw_swa_prefill(swa, 0, 16, cu, pos, q, k8, v8, ring_k, ring_v, None, out)
+    hsw.hsw_swa_prefill(swa, 4, 0, cu, pos, q, k8, v8, ring_k, ring_v, None, out)
+    hsw.hsw_swa_decode(swa, 0, pos, q, ring_k, ring_v, None, out)
+    hsw.hsw_full_decode_splitk(full, 0, 16, lens, base, q, pool_k, pool_v, 8, None, 2048, ws, 4096, out)
+    hsw.hsw_full_decode_splitk(full, 4, 0, lens, base, q, pool_k, pool_v, 8, None, 2048, ws, 4096, out)
+    hsw.hsw_full_prefill_chunk(full, 0, 16, cu, pos, base, q, pool_k, pool_v, 8, None, out)
+    hsw.hsw_full_prefill_chunk(full, 4, 0, cu, pos, base, q, pool_k, pool_v, 8, None, out)
+    torch.cuda.synchronize()
+    for name, t in [("q_rot", q_rot), ("out", out), ("ring_k", ring_k), ("ring_v", ring_v),
+                    ("pool_k", pool_k), ("pool_v", pool_v), ("ws", ws)]:
+        assert bool((t == SENTINEL).all()), f"{name} was written by a zero-size call"
