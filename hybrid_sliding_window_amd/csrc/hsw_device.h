@@ -48,6 +48,19 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) {
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// Streaming (non-temporal) forms, for bytes a kernel reads or writes exactly
+// once: the access is marked so it does not displace reused lines in L2 and
+// the Infinity Cache.
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void st16_nt(void *p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void st8_nt(void *p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

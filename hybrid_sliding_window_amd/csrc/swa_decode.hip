@@ -9,14 +9,22 @@
 // the engine implements": the sink logit joins the denominator only, values
 // are scaled by the value scale (applied here to the fp32 output).
 //
-// HBM-bound: each (sequence, KV head) reads its 48 KiB K ring and 32 KiB V
-// ring exactly once.  One workgroup (4 waves) per (sequence, KV head); wave w
-// owns ring slots [32w, 32w+32).  The G query heads of the group share every
-// K/V load: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows straight from
-// HBM into the A operand, the G heads as the 16 B columns, zero-padded), an
-// fp32 softmax reduced across quads and waves, then O^T = V^T P^T with
-// v_mfma_f32_16x16x16_bf16 on P split into bf16 hi + lo (so P keeps ~16 bits;
-// a single bf16 P costs too much accuracy), V transposed through LDS.
+// HBM-bound: each (sequence, KV head) -- an "item" -- reads its 48 KiB K ring
+// and 32 KiB V ring exactly once.  Persistent workgroups (two per CU, 4 waves)
+// walk the items with the next item's bytes always in flight: at the top of
+// item i the workgroup issues every load of item i + grid (K and q into a
+// second register set, V by direct global->LDS loads into a second LDS
+// buffer), then waits only for item i's.  Wave w owns ring slots
+// [32w, 32w+32) of an item:
+//   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, K rows straight from HBM as the
+//                    A operand, the G query heads as the 16 B columns (heads
+//                    past G repeat real ones and are never stored);
+//   softmax          per wave over its 32 slots, in log2 units;
+//   O^T = V^T P^T    v_mfma_f32_16x16x32_bf16 on P split into bf16 hi + lo (P
+//                    keeps ~16 bits), V^T read from LDS by ds_read_b64_tr_b16
+//                    (V is placed in MFMA fragment order by the loads);
+// then the four waves' (max, sum, O) partials meet in LDS (in the V buffer the
+// wave has finished with) and are combined with the sink, scaled and stored.
 #include "hsw_device.h"
 #include "hsw_launch.h"
 
@@ -26,140 +34,267 @@ namespace {
 constexpr int DQK = 192, DV = 128, W = 128;
 constexpr int STEPS = DQK / 32;       // 16x16x32 MFMA steps over q/k dims
 constexpr int DT = DV / 16;           // 16-wide value tiles
-constexpr int VT_STRIDE = 36;         // bf16 per transposed V row (32 keys + pad)
 constexpr int kThreads = 256;
+constexpr int KEYS = W / 4;           // ring slots per wave
+constexpr int K_LOADS = 2 * STEPS;    // per wave per item: K, 16 bytes a lane
+constexpr int Q_LOADS = STEPS;        // q
+constexpr int V_LOADS = KEYS * DV * 2 / (64 * 16);  // V, direct to LDS (8)
+constexpr int LOADS = K_LOADS + Q_LOADS + V_LOADS + 1;  // 27 (+ the position)
+constexpr int VBUF = 4 * KEYS * DV;   // bf16 per V buffer (32 KiB)
+constexpr int MAX_HQ = 256;           // sinks staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) alone, and lgkmcnt(0) alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The item loads are inline asm so the compiler does not track them (it would
+// otherwise wait for all of them, the next item's included, before the first
+// use of any); their completion is awaited explicitly with s_waitcnt vmcnt.
+// Vector-memory loads complete in issue order, so "at most LOADS outstanding"
+// right after the next item's LOADS were issued means this item's have landed.
+__device__ __forceinline__ void load16(u32x4 &v, const void *src) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(v) : "v"(src) : "memory");
+}
+__device__ __forceinline__ void load8(u32x2 &v, const void *src) {
+    asm volatile("global_load_dwordx2 %0, %1, off" : "+v"(v) : "v"(src) : "memory");
+}
+// Direct global -> LDS load: lane i's 16 bytes land at lds_wave_base + 16 i.
+__device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave_base) {
+    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float quad_max_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float quad_sum_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 template <int G>
-__global__ __launch_bounds__(kThreads) void swa_decode_kernel(AttnArgs a) {
-    // LDS: per-wave transposed V tile [DV][32 keys], later reused for the
-    // per-wave output partials [16 heads][DV] fp32.
-    __shared__ __attribute__((aligned(16))) uint16_t vt[4 * DV * VT_STRIDE];
-    __shared__ float red_m[4][16], red_l[4][16], m_fin[16];
+__global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
+    // V of the current and the next item, each wave's 32 slots in its own
+    // 8 KiB; after a wave's PV it holds that wave's O partial [G][PS] fp32.
+    __shared__ __attribute__((aligned(1024))) uint16_t vb0[VBUF], vb1[VBUF];
+    __shared__ float ml[2][4][16][2];  // (max, sum) per buffer, wave, head
+    __shared__ float sk[MAX_HQ];       // sinks in log2 units
+    constexpr int PS = G * (DV + 4) * 4 <= KEYS * DV * 2 ? DV + 4 : DV;  // partial row stride (floats)
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int quad = lane >> 4, col = lane & 15;
-    const int s = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
-    const int64_t P = a.pos[s];
+    const int n_items = a.n_seqs * a.hkv;
 
-    const uint16_t *K = (const uint16_t *)a.k_main + ((int64_t)(s * a.hkv + g) * W) * DQK;
-    const uint16_t *V = (const uint16_t *)a.v_main + ((int64_t)(s * a.hkv + g) * W) * DV;
-    const uint16_t *Q = (const uint16_t *)a.q + ((int64_t)s * a.hq + g * G) * DQK;
+    for (int i = threadIdx.x; i < a.hq; i += kThreads) sk[i] = a.sinks ? a.sinks[i] * kLog2e : -INFINITY;
 
-    // Issue every global load of this wave up front.
-    u32x4 qb[STEPS], ka[2][STEPS], vr[8];
+    // Per-lane constant parts of the load addresses.  K: A operand of the
+    // S^T MFMA, lane (quad, col) takes slot 32w + 16h + col, dims 32st + 8quad.
+    // V: load i fills 8-byte units (2i + (lane >> 5)) * 64 + (2u, 2u + 1),
+    // u = lane & 31, i.e. what lane (quad', 4k + mm) supplies to the
+    // transposing read of key half hh = i / 4, tile dt = 2 (i % 4) + (lane >> 5):
+    // slot 32w + 16hh + 4 (u >> 3) + ((u >> 1) & 3), bytes 64 (i % 4) +
+    // 32 (lane >> 5) + 16 (u & 1).
+    const int u = lane & 31;
+    const uint32_t koff = (uint32_t)((32 * w + col) * DQK * 2 + 16 * quad);
+    const uint32_t voff = (uint32_t)((32 * w + 4 * (u >> 3) + ((u >> 1) & 3)) * DV * 2 + 32 * (lane >> 5) + 16 * (u & 1));
+    const uint32_t qoff = (uint32_t)((col % G) * DQK * 2 + 16 * quad);
+
+    auto issue = [&](int item, u32x4 (&ka)[2][STEPS], u32x4 (&qb)[STEPS], uint16_t *vb, u32x2 &pos) {
+        const int s = item / a.hkv, g = item % a.hkv;
+        load8(pos, a.pos + s);
+        const char *K = (const char *)a.k_main + (int64_t)item * W * DQK * 2;
+        const char *V = (const char *)a.v_main + (int64_t)item * W * DV * 2;
+        const char *Q = (const char *)a.q + ((int64_t)s * a.hq + g * G) * DQK * 2;
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st)
-        qb[st] = col < G ? ld16(Q + col * DQK + 32 * st + 8 * quad) : u32x4{0, 0, 0, 0};
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+            for (int st = 0; st < STEPS; ++st) load16(ka[h][st], K + koff + 16 * h * DQK * 2 + 64 * st);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) load16(qb[st], Q + qoff + 64 * st);
+        const char *vw = (const char *)vb + w * KEYS * DV * 2;
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i)
+            load_lds16(V + voff + 16 * (i / 4) * DV * 2 + 64 * (i % 4), vw + i * 1024);
+    };
+
+    const float scale2 = a.scale * kLog2e;
+    auto compute = [&](int item, const u32x4 (&ka)[2][STEPS], const u32x4 (&qb)[STEPS], uint16_t *vb,
+                       float (&mlb)[4][16][2], u32x2 pos) {
+        const int s = item / a.hkv, g = item % a.hkv;
+        const int64_t P = (int64_t)(((uint64_t)pos[1] << 32) | pos[0]);
+        const int pc = P < W - 1 ? (int)P : W - 1;  // slot positions >= 0 iff (P - slot) mod W <= pc
+
+        f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
-            ka[kt][st] = ld16(K + (32 * w + 16 * kt + col) * DQK + 32 * st + 8 * quad);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        int c = it * 64 + lane;  // 16-byte chunk of this wave's 32 x DV tile
-        vr[it] = ld16(V + (32 * w + (c >> 4)) * DV + 8 * (c & 15));
-    }
+            for (int h = 0; h < 2; ++h) sacc[h] = mfma_16x16x32_bf16(ka[h][st], qb[st], sacc[h]);
 
-    // S^T[key][head] for the wave's two 16-key tiles.
-    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        float sv[8], mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sacc[kt] = mfma_16x16x32_bf16(ka[kt][st], qb[st], sacc[kt]);
-
-    // V transposed into LDS: vt[w][dv][key].
-    uint16_t *vtw = vt + w * DV * VT_STRIDE;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        int c = it * 64 + lane, key = c >> 4, dv0 = 8 * (c & 15);
+            for (int j = 0; j < 4; ++j) {
+                const int slot = 32 * w + 16 * h + 4 * quad + j;
+                const int back = ((int)P - slot) & (W - 1);
+                const float v = back <= pc ? sacc[h][j] * scale2 : -INFINITY;
+                sv[4 * h + j] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = quad_max_swap(mx);
+        const float mu = mx == -INFINITY ? 0.0f : mx;
+        float pv[8], lsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            uint32_t word = vr[it][e >> 1];
-            vtw[(dv0 + e) * VT_STRIDE + key] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+            pv[e] = __builtin_amdgcn_exp2f(sv[e] - mu);
+            lsum += pv[e];
         }
-    }
+        lsum = quad_sum_swap(lsum);
+        u32x2 h0, l0, h1, l1;
+        split_hi_lo(pv, h0, l0);
+        split_hi_lo(pv + 4, h1, l1);
+        const u32x4 bhi = u32x4{h0[0], h0[1], h1[0], h1[1]};
+        const u32x4 blo = u32x4{l0[0], l0[1], l1[0], l1[1]};
 
-    // Scaled logits in log2 units, masked where the slot holds a position < 0.
-    const float scale2 = a.scale * kLog2e;
-    float sv[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int slot = 32 * w + 16 * kt + 4 * quad + i;
-            int64_t back = (P - slot) & (W - 1);
-            float v = back <= P ? sacc[kt][i] * scale2 : -INFINITY;
-            sv[4 * kt + i] = v;
-            mx = fmaxf(mx, v);
-        }
-    mx = quad_max(mx);
-    if (quad == 0) red_m[w][col] = mx;
-    __syncthreads();
-    float m = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
-    const bool has_sink = a.sinks != nullptr && col < G;
-    const float sink2 = has_sink ? a.sinks[g * G + col] * kLog2e : -INFINITY;
-    m = fmaxf(m, sink2);  // finite: the current position is always in the ring
-    float pv[8], lsum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        pv[e] = exp2f(sv[e] - m);
-        lsum += pv[e];
-    }
-    lsum = quad_sum(lsum);
-    if (quad == 0) red_l[w][col] = lsum;
-    if (w == 0 && quad == 0) m_fin[col] = m;
-
-    // O^T[dv][head] = V^T P^T over this wave's 32 keys.
-    f32x4 oacc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        u32x2 hi, lo;
-        split_hi_lo(pv + 4 * kt, hi, lo);
+        // O^T = V^T P^T over the wave's 32 slots: operand slots 0-3 of a quad
+        // are keys 4quad.. of the first 16-key half, slots 4-7 of the second.
+        uint16_t *vw = vb + w * KEYS * DV;
+        f32x4 oacc[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            u32x2 av = *reinterpret_cast<const u32x2 *>(vtw + (16 * dt + col) * VT_STRIDE + 16 * kt + 4 * quad);
-            oacc[dt] = mfma_16x16x16_bf16(av, hi, oacc[dt]);
-            oacc[dt] = mfma_16x16x16_bf16(av, lo, oacc[dt]);
+            const u32x2 a0 = ds_read_tr16(vw + (dt * 64 + lane) * 4);
+            const u32x2 a1 = ds_read_tr16(vw + ((DT + dt) * 64 + lane) * 4);
+            const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            oacc[dt] = mfma_16x16x32_bf16(av, bhi, f32x4{0, 0, 0, 0});
+            oacc[dt] = mfma_16x16x32_bf16(av, blo, oacc[dt]);
         }
-    }
-    __syncthreads();  // every wave is done with vt: reuse it for the partials
-    float *opart = reinterpret_cast<float *>(vt);  // [4][16][DV]
+        // The wave's partial over its own V slots (its reads of them are done:
+        // LDS accesses of one wave are performed in order).
+        float *part = reinterpret_cast<float *>(vw);
+        if (col < G) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4 *>(opart + (w * 16 + col) * DV + 16 * dt + 4 * quad) = oacc[dt];
-    __syncthreads();
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4 *>(part + col * PS + 16 * dt + 4 * quad) = oacc[dt];
+            if (quad == 0) {
+                mlb[w][col][0] = mx;
+                mlb[w][col][1] = lsum;
+            }
+        }
+        lds_barrier();
 
-    // Combine the four waves, add the sink to the denominator, scale, store.
-    uint16_t *out = (uint16_t *)a.out + ((int64_t)s * a.hq + g * G) * DV;
-    for (int idx = threadIdx.x; idx < G * DV / 4; idx += kThreads) {
-        int h = idx / (DV / 4), d4 = 4 * (idx % (DV / 4));
-        f32x4 o = *reinterpret_cast<const f32x4 *>(opart + h * DV + d4);
+        // Combine the four waves; the sink joins the denominator once.
+        uint16_t *out = (uint16_t *)a.out + ((int64_t)s * a.hq + g * G) * DV;
+        const float *pbase = reinterpret_cast<const float *>(vb);
+        for (int idx = threadIdx.x; idx < G * (DV / 4); idx += kThreads) {
+            const int hd = idx / (DV / 4), d4 = 4 * (idx % (DV / 4));
+            const float sink2 = sk[g * G + hd];
+            float mw[4], M = sink2;
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) o += *reinterpret_cast<const f32x4 *>(opart + (ww * 16 + h) * DV + d4);
-        float l = red_l[0][h] + red_l[1][h] + red_l[2][h] + red_l[3][h];
-        if (a.sinks) l += exp2f(a.sinks[g * G + h] * kLog2e - m_fin[h]);
-        float r = a.value_scale / l;
-        u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * r) | ((uint32_t)f2bf(o[1] * r) << 16),
-                         (uint32_t)f2bf(o[2] * r) | ((uint32_t)f2bf(o[3] * r) << 16)};
-        *reinterpret_cast<u32x2 *>(out + h * DV + d4) = pk;
+            for (int ww = 0; ww < 4; ++ww) {
+                mw[ww] = mlb[ww][hd][0];
+                M = fmaxf(M, mw[ww]);
+            }
+            float L = __builtin_amdgcn_exp2f(sink2 - M);  // 0 without a sink
+            f32x4 o = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                const float f = __builtin_amdgcn_exp2f(mw[ww] - M);
+                L += f * mlb[ww][hd][1];
+                o += f * *reinterpret_cast<const f32x4 *>(pbase + ww * (KEYS * DV / 2) + hd * PS + d4);
+            }
+            const float r = a.value_scale / L;
+            const u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * r) | ((uint32_t)f2bf(o[1] * r) << 16),
+                                   (uint32_t)f2bf(o[2] * r) | ((uint32_t)f2bf(o[3] * r) << 16)};
+            *reinterpret_cast<u32x2 *>(out + hd * DV + d4) = pk;
+        }
+        // Every wave is done with this buffer before the loads of the item
+        // after next are issued into it.
+        lds_barrier();
+    };
+
+    u32x4 kaA[2][STEPS], kaB[2][STEPS], qbA[STEPS], qbB[STEPS];
+    u32x2 pA = u32x2{0, 0}, pB = u32x2{0, 0};
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        qbA[st] = qbB[st] = u32x4{0, 0, 0, 0};
+        kaA[0][st] = kaA[1][st] = kaB[0][st] = kaB[1][st] = u32x4{0, 0, 0, 0};
     }
+    lds_barrier();  // sinks staged (their global loads were awaited by the compiler)
+
+    int item = blockIdx.x;
+    const int grid = gridDim.x;
+    issue(item, kaA, qbA, vb0, pA);
+    while (true) {
+        bool more = item + grid < n_items;
+        if (more) {
+            issue(item + grid, kaB, qbB, vb1, pB);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __asm__ volatile("" ::: "memory");
+        compute(item, kaA, qbA, vb0, ml[0], pA);
+        item += grid;
+        if (!more) break;
+        more = item + grid < n_items;
+        if (more) {
+            issue(item + grid, kaA, qbA, vb0, pA);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __asm__ volatile("" ::: "memory");
+        compute(item, kaB, qbB, vb1, ml[1], pB);
+        item += grid;
+        if (!more) break;
+    }
+}
+
+int cu_count() {
+    static int n[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (n[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        n[dev] = c;
+    }
+    return n[dev];
 }
 
 }  // namespace
 
 bool swa_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
     int G = a.hq / a.hkv;
-    return dtype == 0 && out_dtype == 0 && a.dqk == DQK && a.dv == DV && a.window == W &&
+    return dtype == 0 && out_dtype == 0 && a.dqk == DQK && a.dv == DV && a.window == W && a.hq <= MAX_HQ &&
            (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
 hipError_t launch_swa_decode(const AttnArgs &a, hipStream_t s) {
-    dim3 grid((unsigned)(a.n_seqs * a.hkv)), block(kThreads);
+    const int64_t items = (int64_t)a.n_seqs * a.hkv;
+    const int64_t nb = items < 2 * cu_count() ? items : 2 * cu_count();
+    dim3 grid((unsigned)nb), block(kThreads);
     switch (a.hq / a.hkv) {
         case 1: hipLaunchKernelGGL(swa_decode_kernel<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(swa_decode_kernel<2>, grid, block, 0, s, a); break;
