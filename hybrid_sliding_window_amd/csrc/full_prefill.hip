@@ -66,6 +66,13 @@ __device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane
+// offset: no per-lane address arithmetic.
+__device__ __forceinline__ void load_lds16_s(const void *sbase, uint32_t voff, const void *lds_wave_base) {
+    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
 // 16-byte global load into v, untracked like the loads above (v keeps its
 // register; the first wait of the pipeline covers it, as it was issued first).
 __device__ __forceinline__ void load_q16(u32x4 &v, const void *src) {
@@ -110,11 +117,12 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[KC * DQK], ks1[KC * DQK], ks2[KC * DQK];
     __shared__ __attribute__((aligned(1024))) uint16_t vs0[KC * DV], vs1[KC * DV], vs2[KC * DV];
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();  // the intrinsics, so no library call is needed
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int quad = lane >> 4, col = lane & 15;
     const int total = a.n_seqs * a.hkv * nqb;
-    const int bid = xcd_remap(blockIdx.x, total);
+    const int bid = xcd_remap((int)__builtin_amdgcn_workgroup_id_x(), total);
     const int qb = bid % nqb;
     const int g = (bid / nqb) % a.hkv;
     const int s = bid / (nqb * a.hkv);
@@ -170,8 +178,9 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     const int u = lane & 31;
     const int vrow_l = 4 * (u >> 3) + ((u >> 1) & 3);
     const int vbyte_l = 32 * (lane >> 5) + 16 * (u & 1);
-    const int64_t koff_l = col * krow + 16 * quad;
-    const int64_t voff_l = vrow_l * vrow + vbyte_l;
+    // per-lane byte offsets of the unclamped loads (within 16 pool rows)
+    const uint32_t koff_l = (uint32_t)(col * krow + 16 * quad);
+    const uint32_t voff_l = (uint32_t)(vrow_l * vrow + vbyte_l);
 
     // Chunk c's loads.  Keys past the last one are clamped to it (finite
     // data, masked); past the band a dummy set (the first row, again) keeps
@@ -179,22 +188,27 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd) {
         const int k0 = c * KC;
         const char *ksrc[K_LOADS], *vsrc[V_LOADS];
+        if (c < nch && k0 + KC - 1 <= klast) {
+            // whole chunk inside the band: uniform base + per-lane offset
+#pragma unroll
+            for (int i = 0; i < K_LOADS; ++i) {
+                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
+                load_lds16_s(kseq + (int64_t)(k0 + 16 * h) * krow + 64 * st, koff_l,
+                             (const char *)ksd + (4 * i + w) * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int j = 4 * i + w, hh = j / 4;
+                load_lds16_s(vseq + (int64_t)(k0 + 16 * hh) * vrow + 64 * (j % 4), voff_l,
+                             (const char *)vsd + (4 * i + w) * 1024);
+            }
+            return;
+        }
         if (c >= nch) {
 #pragma unroll
             for (int i = 0; i < K_LOADS; ++i) ksrc[i] = kseq;
 #pragma unroll
             for (int i = 0; i < V_LOADS; ++i) vsrc[i] = vseq;
-        } else if (k0 + KC - 1 <= klast) {
-#pragma unroll
-            for (int i = 0; i < K_LOADS; ++i) {
-                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
-                ksrc[i] = kseq + (int64_t)(k0 + 16 * h) * krow + 64 * st + koff_l;
-            }
-#pragma unroll
-            for (int i = 0; i < V_LOADS; ++i) {
-                const int j = 4 * i + w, hh = j / 4;
-                vsrc[i] = vseq + (int64_t)(k0 + 16 * hh) * vrow + 64 * (j % 4) + voff_l;
-            }
         } else {
 #pragma unroll
             for (int i = 0; i < K_LOADS; ++i) {

@@ -56,10 +56,20 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_wave_base + 16 i (lds_wave_base is wave-uniform).
-typedef __attribute__((address_space(3))) void lds_void;
+// lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0).  Issued
+// as inline asm so the compiler does not track it (it would otherwise add
+// waits of its own before LDS reads, for more of these loads than a read
+// needs); completion is awaited explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes a stage.  m0 is used by nothing else here.
 __device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
+    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane
+// offset: no per-lane address arithmetic.
+__device__ __forceinline__ void load_lds16_s(const void *sbase, uint32_t voff, const void *lds_wave_base) {
+    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
 // Max / sum over the four quads (lanes c, c+16, c+32, c+48) with the gfx950
@@ -109,11 +119,12 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[KC * DQK], ks1[KC * DQK], ks2[KC * DQK];
     __shared__ __attribute__((aligned(1024))) uint16_t vs0[KC * DV], vs1[KC * DV], vs2[KC * DV];
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();  // the intrinsics, so no library call is needed
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int quad = lane >> 4, col = lane & 15;
     const int total = a.n_seqs * a.hkv * nqb;
-    const int bid = xcd_remap(blockIdx.x, total);
+    const int bid = xcd_remap((int)__builtin_amdgcn_workgroup_id_x(), total);
     const int qb = bid % nqb;
     const int g = (bid / nqb) % a.hkv;
     const int s = bid / (nqb * a.hkv);
@@ -188,14 +199,14 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
 #pragma unroll
             for (int i = 0; i < K_LOADS; ++i) {
                 const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
-                load_lds16(kst + (int64_t)(k0 + 16 * h - start) * krow + 64 * st + koff_l,
-                           (const char *)ksd + j * 1024);
+                load_lds16_s(kst + (int64_t)(k0 + 16 * h - start) * krow + 64 * st, koff_l,
+                             (const char *)ksd + j * 1024);
             }
 #pragma unroll
             for (int i = 0; i < V_LOADS; ++i) {
                 const int j = 4 * i + w, hh = j / 4;
-                load_lds16(vst + (int64_t)(k0 + 16 * hh - start) * vrow + 64 * (j % 4) + voff_l,
-                           (const char *)vsd + j * 1024);
+                load_lds16_s(vst + (int64_t)(k0 + 16 * hh - start) * vrow + 64 * (j % 4), voff_l,
+                             (const char *)vsd + j * 1024);
             }
         } else {
 #pragma unroll
