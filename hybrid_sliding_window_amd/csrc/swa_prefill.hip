@@ -256,28 +256,42 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         if (!(k0 <= wpos_hi && k0 + KC - 1 > wpos_lo - W)) return;
         // every key of the chunk inside every row's window: no mask
         const bool interior = k0 + KC - 1 <= wpos_lo && k0 > wpos_hi - W && k0 + KC - 1 <= plast;
+        // S^T for both 16-key halves and both row tiles: four independent
+        // accumulation chains, so consecutive MFMAs never wait on each other.
         float sv[2][2][4];  // [16-key half][n][j]
+        {
+            u32x4 ak[2][STEPS];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            u32x4 ak[STEPS];
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+                    ak[h][st] = *reinterpret_cast<const u32x4 *>(ksc + ((h * STEPS + st) * 64 + lane) * 8);
+            f32x4 acc[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) acc[h][n] = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int st = 0; st < STEPS; ++st)
-                ak[st] = *reinterpret_cast<const u32x4 *>(ksc + ((h * STEPS + st) * 64 + lane) * 8);
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                f32x4 acc = f32x4{0, 0, 0, 0};
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int st = 0; st < STEPS; ++st) acc = mfma_16x16x32_bf16(ak[st], qv[n][st], acc);
-                if (interior) {
+                    for (int n = 0; n < 2; ++n) acc[h][n] = mfma_16x16x32_bf16(ak[h][st], qv[n][st], acc[h][n]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sv[h][n][j] = acc[j];
-                } else {
-                    // key j of this lane is visible iff 0 <= qpos - kp < W (kp <= plast follows)
-                    const int d = qpos[n] - (k0 + 16 * h + 4 * quad);
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sv[h][n][j] = (unsigned)(d - j) < (unsigned)W ? acc[j] : -INFINITY;
+                for (int n = 0; n < 2; ++n) {
+                    if (interior) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sv[h][n][j] = acc[h][n][j];
+                    } else {
+                        // key j of this lane is visible iff 0 <= qpos - kp < W (kp <= plast follows)
+                        const int d = qpos[n] - (k0 + 16 * h + 4 * quad);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            sv[h][n][j] = (unsigned)(d - j) < (unsigned)W ? acc[h][n][j] : -INFINITY;
+                    }
                 }
-            }
         }
         u32x4 bhi[2], blo[2];
 #pragma unroll
