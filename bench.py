@@ -44,8 +44,8 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_
 # once those sources differ from the ones measured.
 MEASURED_TRAFFIC = {
     # band kernel 1510.2 MB + ring commit 2.7 MB read / 2.6 MB written
-    "swa_prefill": (1515.5e6, ("swa_prefill.hip", "generic_attn.hip"), "8b53b54d869ea5bc"),
-    "swa_decode": (178.36e6, ("swa_decode.hip",), "a29143a54058a654"),
+    "swa_prefill": (1515.5e6, ("swa_prefill.hip", "generic_attn.hip"), "0d5a6933c06a5bb7"),
+    "swa_decode": (178.47e6, ("swa_decode.hip",), "f65d449858588a56"),
 }
 
 
