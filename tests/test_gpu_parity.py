@@ -476,6 +476,26 @@ def test_full_prefill_values_beyond_fp16_range():
     print(f"full_prefill large V: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
+def test_full_prefill_values_beyond_fp16_range_in_some_columns():
+    """Out-of-fp16-range V confined to a few columns (inside one or two of
+    the four 32-column blocks of a 32-key chunk): those blocks keep bf16 while
+    the rest of the chunk goes through fp16, and the result still matches."""
+    note("full_prefill large V in some columns")
+    batch = wl.full_prefill_batch(seed=74, n_seqs=2, seqlens=(150, 90), start_pos=(250, 60))
+    rows = batch["vpool"].shape[0]
+    big = torch.arange(3, rows, 29)
+    vp = batch["vpool"].float()
+    vp[big, :, 40] *= 1.5e5          # column block 1 only
+    vp[big[::2], :, 100:103] *= -3.0e5  # and block 3 in every other such row
+    batch["vpool"] = vp.to(torch.bfloat16)
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    cu = batch["cu_seqlens"].tolist()
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(2)])
+    ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * float(np.abs(ref).max()),
+                          what="full_prefill large V in some columns")
+    print(f"full_prefill large V in some columns: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
 # ------------------------------------------------------- degenerate cases
 def test_swa_prefill_empty_and_single_token_sequences():
     """Zero-length sequences inside a batch (no rows, ring untouched),
