@@ -52,6 +52,7 @@ constexpr float kRescale = 8.0f;
 // s_waitcnt immediates (gfx9 encoding): wait until at most N vector-memory
 // ops of this wave are outstanding; expcnt and lgkmcnt left unconstrained.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) alone
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -118,6 +119,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     // read of one stage does not depend on the loads in flight to another.
     __shared__ __attribute__((aligned(1024))) uint16_t ks0[KC * DQK], ks1[KC * DQK], ks2[KC * DQK];
     __shared__ __attribute__((aligned(1024))) uint16_t vs0[KC * DV], vs1[KC * DV], vs2[KC * DV];
+    // per stage and wave: 1 if the wave's block of V columns stayed bf16
+    // (a value beyond the fp16 range), 0 if it was converted to fp16
+    __shared__ int vflag[3][4];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();  // the intrinsics, so no library call is needed
     const int lane = tid & 63;
@@ -238,15 +242,49 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     }
     const int wpos_lo = p0 + (32 * w) / G, wpos_hi = p0 + (32 * w + 31) / G;
 
-    auto step = [&](int c, const uint16_t *ksc, const uint16_t *vsc, uint16_t *ksn, uint16_t *vsn) {
-        // Own loads of chunk c done (chunk c+1's may still fly), then make
-        // every wave's visible.  The stage chunk c+2 goes to was last read in
+    // Each wave converts the V pieces it loaded for a chunk (columns 32w ..
+    // 32w+31 of the chunk's 32 keys) from bf16 to fp16 in place, unless one
+    // of them is beyond the fp16 range (|v| >= 65536, the first bf16 value
+    // fp16 cannot hold): then they stay bf16 and the wave's flag says so.
+    // The wave's own loads of those pieces must have landed; the barrier
+    // after it publishes the result (the flags are read after it too).
+    auto convert_v = [&](uint16_t *vst, int (&vf)[4]) {
+        u32x4 raw[V_LOADS];
+        float big = 0.0f;
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) {
+            raw[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(vst) + (4 * i + w) * 1024 + lane * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                big = fmaxf(big, fmaxf(fabsf(__uint_as_float(raw[i][e] << 16)),
+                                       fabsf(__uint_as_float(raw[i][e] & 0xffff0000u))));
+        }
+        const bool keep = __any(big >= 65536.0f);
+        if (!keep) {
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                u32x4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(raw[i][e]);
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(vst) + (4 * i + w) * 1024 + lane * 16) = h;
+            }
+        }
+        if (lane == 0) vf[w] = keep ? 1 : 0;
+    };
+
+    auto step = [&](int c, const uint16_t *ksc, uint16_t *vsc, uint16_t *ksn, uint16_t *vsn, int (&vf)[4]) {
+        // Own loads of chunk c done (chunk c+1's may still fly); the wave
+        // converts its V pieces of chunk c; the barrier makes every wave's K,
+        // V and flags visible.  The stage chunk c+2 goes to was last read in
         // step c-1, which every wave has finished once past this barrier.
         __asm__ volatile("" ::: "memory");
         if (c + 1 < nch)
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __asm__ volatile("" ::: "memory");
+        convert_v(vsc, vf);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
         if (c + 2 < nch) issue(c + 2, ksn, vsn);
@@ -293,7 +331,10 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
                     }
                 }
         }
-        u32x4 bhi[2], blo[2];
+        // V column blocks kept in bf16 (rare): their tiles take P as bf16
+        // hi + lo; the others fp16 P x fp16 V.
+        const int kept = vf[0] | (vf[1] << 1) | (vf[2] << 2) | (vf[3] << 3);
+        u32x4 pf16[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             float cm = fmaxf(fmaxf(fmaxf(sv[0][n][0], sv[0][n][1]), fmaxf(sv[0][n][2], sv[0][n][3])),
@@ -320,24 +361,54 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
                     pv[4 * h + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][n][j], scale2, mu));
                     l[n] += pv[4 * h + j];
                 }
-            u32x2 h0, l0, h1, l1;
-            split_hi_lo(pv, h0, l0);
-            split_hi_lo(pv + 4, h1, l1);
-            bhi[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
-            blo[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+            // P <= 2^8, so fp16 holds it with 11 significant bits
+            pf16[n] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
+                            pack_f16x2(pv[6], pv[7])};
         }
         // O^T += V^T P^T: slots 0-3 of a quad are keys 4quad.. of the first
         // 16-key half, slots 4-7 the same keys of the second half, on both
         // operands.
+        if (!kept) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
-            u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
-            u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            for (int dt = 0; dt < DT; ++dt) {
+                u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+                u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
+                u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                oacc[n][dt] = mfma_16x16x32_bf16(av, bhi[n], oacc[n][dt]);
-                oacc[n][dt] = mfma_16x16x32_bf16(av, blo[n], oacc[n][dt]);
+                for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf16[n], oacc[n][dt]);
+            }
+        } else {
+            // A kept block's tiles multiply the same fp16-rounded P, split
+            // exactly into bf16 hi + lo (11 significant bits fit in two
+            // bf16), by the bf16 V.
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+                u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
+                u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                if ((kept >> (dt / 2)) & 1) {
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        float pf[8];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            // (copied out first: a bit cast of a vector element in place
+                            // reads element 0 with this compiler)
+                            const uint32_t word = pf16[n][e];
+                            const f16x2 hp = __builtin_bit_cast(f16x2, word);
+                            pf[2 * e] = (float)hp[0];
+                            pf[2 * e + 1] = (float)hp[1];
+                        }
+                        u32x2 h0, l0, h1, l1;
+                        split_hi_lo(pf, h0, l0);
+                        split_hi_lo(pf + 4, h1, l1);
+                        oacc[n][dt] = mfma_16x16x32_bf16(av, u32x4{h0[0], h0[1], h1[0], h1[1]}, oacc[n][dt]);
+                        oacc[n][dt] = mfma_16x16x32_bf16(av, u32x4{l0[0], l0[1], l1[0], l1[1]}, oacc[n][dt]);
+                    }
+                } else {
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf16[n], oacc[n][dt]);
+                }
             }
         }
     };
@@ -345,9 +416,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     issue(0, ks0, vs0);
     if (nch > 1) issue(1, ks1, vs1);
     for (int c = 0; c < nch; c += 3) {
-        step(c, ks0, vs0, ks2, vs2);
-        if (c + 1 < nch) step(c + 1, ks1, vs1, ks0, vs0);
-        if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1);
+        step(c, ks0, vs0, ks2, vs2, vflag[0]);
+        if (c + 1 < nch) step(c + 1, ks1, vs1, ks0, vs0, vflag[1]);
+        if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1, vflag[2]);
     }
 
     // Epilogue: the sink joins the denominator once; scale; bf16.  Each wave

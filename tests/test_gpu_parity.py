@@ -269,6 +269,26 @@ def oracle_swa_prefill_rows(batch, q_rot, kst, vst, kring_before, vring_before, 
     return outs
 
 
+def test_swa_prefill_values_beyond_fp16_range():
+    """V beyond the fp16 range in whole rows (chunk rows and ring rows) and
+    in single columns: the column blocks holding them keep bf16, the rest of
+    each 32-key chunk goes through fp16, and the result matches."""
+    note("swa_prefill large V")
+    batch = wl.swa_prefill_batch(seed=45, n_seqs=2, seqlens=(400, 150), start_pos=(300, 0))
+    v = batch["v"].float()
+    v[7::41] *= 2.0e5                      # whole rows of the chunk
+    v[20::23, :, 70] *= -1.5e5             # one column: column block 2 only
+    batch["v"] = v.to(torch.bfloat16)
+    vr = batch["vring"].float()
+    vr[0, :, 5::37] *= 3.0e5               # ring rows read by the first sequence's early rows
+    batch["vring"] = vr.to(torch.bfloat16)
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb)])
+    ma, mr = assert_close(f64(out), ref, max_abs=2e-2 * float(np.abs(ref).max()), what="swa_prefill large V")
+    print(f"swa_prefill large V: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (128, 8), (32, 8)])
 def test_swa_prefill_ragged(hq, hkv):
     note(f"swa_prefill ragged hq={hq} hkv={hkv}")
