@@ -1,6 +1,7 @@
 """Benchmark of the attention core on one MI355X (synthetic, seeded inputs).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+                    [--only CALL [--model flash|pro]]
 
 Prints ONE JSON line.  The headline `value` is the windowed (SWA) prefill
 throughput in algorithmic TFLOP/s on the 4 x 8192-token workload (64 q / 8 KV
@@ -10,6 +11,9 @@ ring commit) measured with HIP events on the stream the kernels run on.
 The same line carries the windowed-decode HBM GB/s on 256 sequences (the
 second half of the metric), the other calls of the path, a roofline object
 for the dominant kernel and the fp64 CPU oracle timed on a bounded sample.
+Unless --quick, a `pro` object repeats every call and the hybrid step at
+MiMo-V2.6-Pro shapes (128 q heads, 8 KV heads on both layer kinds, value
+scale 0.612, 70 layers of which 10 full).
 
 Inputs are resident in HBM before each timed region.  Timed regions cycle
 over enough replicas of the inputs that every launch reads HBM rather than
@@ -94,11 +98,17 @@ def swa_prefill_pairs(lens, starts, window=128):
     return tot
 
 
-def bench_swa_prefill(hsw, wl, steps, warmup, stream):
+def heads(model):
+    return f"{model.n_q_heads} q / {model.swa_kv_heads} KV heads"
+
+
+def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
     """Windowed prefill, 4 x 8192 tokens from position 0; also times the RoPE +
     staging write that feeds it."""
+    model = model or wl.FLASH
+    hq, hkv = model.n_q_heads, model.swa_kv_heads
     S, T1 = 4, 8192
-    b = wl.swa_prefill_batch(seed=2, device=DEV)
+    b = wl.swa_prefill_batch(seed=2, device=DEV, **wl.model_kw(model, "swa"))
     sh = b["shape"]
     T = S * T1
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
@@ -110,7 +120,7 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream):
         hsw.hsw_rope_partial_kv_write(sh, T, d["q"], d["k"], d["v"], d["pos"], None, hsw.HSW_DST_STAGING,
                                       kst, vst, T, None, q_rot, None, stream)
     rope(0)
-    out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((T, hq, 128), dtype=torch.bfloat16, device=DEV)
 
     def call(i):
         hsw.hsw_swa_prefill(sh, S, T1, d["cu_seqlens"], d["start_pos"], q_rot, kst, vst, d["kring"],
@@ -122,16 +132,18 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream):
     t_call = ev_time(call, steps, stream)
     t_rope = ev_time(rope, max(steps, 20), stream)
     pairs = swa_prefill_pairs([T1] * S, [0] * S)
-    flops = pairs * 64 * 2 * (192 + 128)
+    flops = pairs * hq * 2 * (192 + 128)
     # algorithmic bytes: q_rot, staged K/V read once, out written once, the
     # ring commit (last 128 rows of K and V per sequence) written once
-    bytes_ = T * 64 * 192 * 2 + T * 8 * (192 + 128) * 2 + T * 64 * 128 * 2 + S * 8 * 128 * (192 + 128) * 2
-    rope_bytes = T * 2 * (64 * 192 + 8 * 192 + 8 * 128) * 2
+    bytes_ = T * hq * 192 * 2 + T * hkv * (192 + 128) * 2 + T * hq * 128 * 2 + S * hkv * 128 * (192 + 128) * 2
+    rope_bytes = T * 2 * (hq * 192 + hkv * 192 + hkv * 128) * 2
     return dict(
         ms=t_call, flops=flops, bytes=bytes_, tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
+        frac_mfma_peak=flops / t_call / 1e9 / BF16_PEAK_TFLOPS, frac_hbm_peak=bytes_ / t_call / 1e6 / HBM_PEAK_GBS,
+        workload=f"windowed prefill, 4 x 8192 tokens from position 0, {heads(model)}, window 128",
         rope=dict(ms=t_rope, bytes=rope_bytes, gbs=rope_bytes / t_rope / 1e6,
                   frac_hbm_peak=rope_bytes / t_rope / 1e6 / HBM_PEAK_GBS,
-                  workload="RoPE + staging write of 32768 tokens (64 q / 8 KV heads)"))
+                  workload=f"RoPE + staging write of 32768 tokens ({heads(model)})"))
 
 
 def bench_copy(steps, stream, nbytes=1 << 30):
@@ -148,19 +160,21 @@ def bench_copy(steps, stream, nbytes=1 << 30):
     return dict(ms=t, bytes=2 * nbytes, gbs=2 * nbytes / t / 1e6, read_bytes=nbytes, write_bytes=nbytes)
 
 
-def bench_swa_decode(hsw, wl, steps, stream, replicas=8):
+def bench_swa_decode(hsw, wl, steps, stream, replicas=8, model=None):
     """Windowed decode, 256 sequences at positions U{128..524288}; 8 replicas
     of (q, rings, out) so each launch reads HBM (working set 178 MB < MALL)."""
+    model = model or wl.FLASH
+    hq, hkv = model.n_q_heads, model.swa_kv_heads
     S = 256
     reps = []
     for r in range(replicas):
-        b = wl.swa_decode_batch(seed=3 if r == 0 else 300 + r, device=DEV)
+        b = wl.swa_decode_batch(seed=3 if r == 0 else 300 + r, device=DEV, **wl.model_kw(model, "swa"))
         d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
         q_rot = torch.empty_like(d["q"])
         hsw.hsw_rope_partial_kv_write(b["shape"], S, d["q"], d["k"], d["v"], d["pos"], d["seq"],
                                       hsw.HSW_DST_RING, d["kring"], d["vring"], S, None, q_rot, None, stream)
         d["q_rot"] = q_rot
-        d["out"] = torch.empty((S, 64, 128), dtype=torch.bfloat16, device=DEV)
+        d["out"] = torch.empty((S, hq, 128), dtype=torch.bfloat16, device=DEV)
         reps.append(d)
     sh = b["shape"]
 
@@ -172,16 +186,19 @@ def bench_swa_decode(hsw, wl, steps, stream, replicas=8):
     warm(call, stream)
     n = max(steps, 25) * replicas
     t = ev_time(call, n, stream)
-    bytes_ = S * (8 * 128 * (192 + 128) * 2 + 64 * 192 * 2 + 64 * 128 * 2)
-    flops = S * 64 * 128 * 2 * (192 + 128)
+    bytes_ = S * (hkv * 128 * (192 + 128) * 2 + hq * 192 * 2 + hq * 128 * 2)
+    flops = S * hq * 128 * 2 * (192 + 128)
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
                 flops=flops, launches=n, replicas=replicas,
-                workload="windowed decode, 256 sequences at positions U{128..524288}, 64 q / 8 KV heads, 128-slot ring")
+                workload=f"windowed decode, 256 sequences at positions U{{128..524288}}, {heads(model)}, "
+                         "128-slot ring")
 
 
-def bench_full_decode(hsw, wl, steps, stream):
+def bench_full_decode(hsw, wl, steps, stream, model=None):
     """Full-attention decode, 64 sequences, contexts U{32768..131072}, split-K 2048."""
-    b = wl.full_decode_batch(seed=4, device=DEV)
+    model = model or wl.FLASH
+    hq, hkv = model.n_q_heads, model.full_kv_heads
+    b = wl.full_decode_batch(seed=4, device=DEV, **wl.model_kw(model, "full"))
     sh = b["shape"]
     S = 64
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
@@ -192,7 +209,7 @@ def bench_full_decode(hsw, wl, steps, stream):
     max_ctx = int(b["ctx_len"].max())
     wsb = hsw.hsw_full_decode_workspace_bytes(sh, S, max_ctx, 2048)
     ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=DEV)
-    out = torch.empty((S, 64, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((S, hq, 128), dtype=torch.bfloat16, device=DEV)
 
     def call(i):
         hsw.hsw_full_decode_splitk(sh, S, max_ctx, d["ctx_len"], d["seq_base"], q_rot, d["kpool"], d["vpool"],
@@ -202,17 +219,20 @@ def bench_full_decode(hsw, wl, steps, stream):
     torch.cuda.synchronize()
     t = ev_time(call, max(steps // 2, 10), stream)
     L = int(b["ctx_len"].sum())
-    bytes_ = L * 4 * (192 + 128) * 2 + S * 64 * (192 + 128) * 2
-    flops = L * 64 * 2 * (192 + 128)
+    bytes_ = L * hkv * (192 + 128) * 2 + S * hq * (192 + 128) * 2
+    flops = L * hq * 2 * (192 + 128)
     del d, ws
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
                 tflops=flops / t / 1e9,
-                workload="full-attention decode, 64 sequences, contexts U{32768..131072}, 64 q / 4 KV heads, split-K 2048")
+                workload=f"full-attention decode, 64 sequences, contexts U{{32768..131072}}, {hq} q / {hkv} KV "
+                         "heads, split-K 2048")
 
 
-def bench_full_prefill(hsw, wl, steps, stream):
+def bench_full_prefill(hsw, wl, steps, stream, model=None):
     """Full-attention chunked prefill: 8192 tokens after 131072 prior rows."""
-    b = wl.full_prefill_batch(seed=5, device=DEV)
+    model = model or wl.FLASH
+    hq, hkv = model.n_q_heads, model.full_kv_heads
+    b = wl.full_prefill_batch(seed=5, device=DEV, **wl.model_kw(model, "full"))
     sh = b["shape"]
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
     T = 8192
@@ -220,7 +240,7 @@ def bench_full_prefill(hsw, wl, steps, stream):
     q_rot = torch.empty_like(d["q"])
     hsw.hsw_rope_partial_kv_write(sh, T, d["q"], d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
                                   d["kpool"], d["vpool"], rows, d["seq_base"], q_rot, None, stream)
-    out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((T, hq, 128), dtype=torch.bfloat16, device=DEV)
 
     def call(i):
         hsw.hsw_full_prefill_chunk(sh, 1, T, d["cu_seqlens"], d["start_pos"], d["seq_base"], q_rot, d["kpool"],
@@ -229,18 +249,20 @@ def bench_full_prefill(hsw, wl, steps, stream):
     torch.cuda.synchronize()
     t = ev_time(call, max(2, steps // 10), stream)
     pairs = T * 131072 + T * (T + 1) // 2
-    flops = pairs * 64 * 2 * (192 + 128)
+    flops = pairs * hq * 2 * (192 + 128)
     return dict(ms=t, flops=flops, tflops=flops / t / 1e9, frac_mfma_peak=flops / t / 1e9 / BF16_PEAK_TFLOPS,
-                workload="full-attention prefill, 8192 tokens after 131072 prior rows, 64 q / 4 KV heads")
+                workload=f"full-attention prefill, 8192 tokens after 131072 prior rows, {hq} q / {hkv} KV heads")
 
 
-def bench_hybrid(hsw, wl, steps, stream):
-    """One hybrid step (hybrid_sliding_window_amd.hybrid.HybridStep): 48
-    attention-only layers (39 windowed, 9 full at seeded indices), each running
-    RoPE + prefill for an 8192-token chunk at positions 131072..139263 and RoPE
-    + decode for 128 sequences with contexts U{4096..262144}."""
+def bench_hybrid(hsw, wl, steps, stream, model=None):
+    """One hybrid step (hybrid_sliding_window_amd.hybrid.HybridStep) over the
+    model's attention-only layers (Flash: 39 windowed + 9 full, Pro: 60 + 10,
+    full layers at seeded indices), each running RoPE + prefill for an
+    8192-token chunk at positions 131072..139263 and RoPE + decode for 128
+    sequences with contexts U{4096..262144}."""
     from hybrid_sliding_window_amd.hybrid import HybridStep
-    hs = HybridStep(hsw, device=DEV)
+    model = model or wl.FLASH
+    hs = HybridStep(hsw, device=DEV, model=model)
     hs.step(stream)
     torch.cuda.synchronize()
     n = max(1, steps)
@@ -252,11 +274,47 @@ def bench_hybrid(hsw, wl, steps, stream):
     for kind, e0, e1 in timer:
         kinds[kind] += e0.elapsed_time(e1)
     T, S = hs.T, hs.S
+    nl, nf = len(hs.pattern), len(hs.pattern) - sum(hs.pattern)
     res = dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps=n, per_call_ms={k: round(v, 3) for k, v in kinds.items()},
-               layers="39 windowed + 9 full (seeded pattern)", pool_gb=round(hs.pool_gb, 1),
-               workload="hybrid step: 48 layers, 8192-token chunk at 131072 + 128 decode sequences U{4096..262144}")
+               layers=f"{nl - nf} windowed + {nf} full (seeded pattern)", pool_gb=round(hs.pool_gb, 1),
+               workload=f"hybrid step {model.name}: {nl} layers, 8192-token chunk at 131072 + 128 decode "
+                        "sequences U{4096..262144}")
     del hs
     return res
+
+
+def rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def bench_pro(hsw, wl, args, stream):
+    """Every call of the path and the 70-layer hybrid step at MiMo-V2.6-Pro
+    shapes (128 q heads, 8 KV heads on both layer kinds, value scale 0.612)."""
+    m = wl.PRO
+    out = {"model": m.name, "heads": "128 q / 8 KV heads on both layer kinds", "value_scale": m.value_scale}
+    pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream, m)
+    print(f"[bench] pro swa_prefill {pre['ms']:.3f} ms {pre['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    out["rope_partial_kv_write"] = rounded(pre.pop("rope"))
+    out["swa_prefill"] = rounded(pre)
+    torch.cuda.empty_cache()
+    dec = bench_swa_decode(hsw, wl, args.steps, stream, model=m)
+    print(f"[bench] pro swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    out["swa_decode"] = rounded(dec)
+    torch.cuda.empty_cache()
+    fd = bench_full_decode(hsw, wl, args.steps, stream, m)
+    print(f"[bench] pro full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    out["full_decode_splitk"] = rounded(fd)
+    torch.cuda.empty_cache()
+    fp = bench_full_prefill(hsw, wl, args.steps, stream, m)
+    print(f"[bench] pro full_prefill {fp['ms']:.2f} ms {fp['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    out["full_prefill_chunk"] = rounded(fp)
+    torch.cuda.empty_cache()
+    hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m)
+    print(f"[bench] pro hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}",
+          file=sys.stderr, flush=True)
+    out["hybrid_step"] = rounded(hy)
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(target_s=15.0, max_seqs=64):
@@ -294,6 +352,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="only the two metric calls")
     ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid", "copy"],
                     help="run one call's timing only (for profiling) and print its numbers")
+    ap.add_argument("--model", choices=["flash", "pro"], default="flash", help="shapes for --only")
+    ap.add_argument("--no-pro", action="store_true", help="skip the MiMo-V2.6-Pro section")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -305,14 +365,16 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     if args.only:
-        fn = {"swa_prefill": lambda: bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream),
-              "swa_decode": lambda: bench_swa_decode(hsw, wl, args.steps, stream),
-              "full_decode": lambda: bench_full_decode(hsw, wl, args.steps, stream),
-              "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream),
-              "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream),
+        m = wl.MODELS[args.model]
+        fn = {"swa_prefill": lambda: bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream, m),
+              "swa_decode": lambda: bench_swa_decode(hsw, wl, args.steps, stream, model=m),
+              "full_decode": lambda: bench_full_decode(hsw, wl, args.steps, stream, m),
+              "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream, m),
+              "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m),
               "copy": lambda: bench_copy(args.steps, stream)}[args.only]
         r = fn()
-        print(json.dumps({"only": args.only, **{k: v for k, v in r.items() if not isinstance(v, dict)}}))
+        print(json.dumps({"only": args.only, "model": m.name,
+                          **{k: v for k, v in r.items() if not isinstance(v, dict)}}))
         return
 
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
@@ -366,6 +428,8 @@ def main():
         "calls": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in calls.items()},
     }
+    if not args.quick and not args.no_pro:
+        line["pro"] = bench_pro(hsw, wl, args, stream)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line))

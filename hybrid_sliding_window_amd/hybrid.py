@@ -16,11 +16,12 @@ batch of decode sequences on every layer:
                   the pool, RoPE + pool write of the decode tokens, split-K
                   full decode.
 
-Sizes default to the bench workload: 48 layers (39 windowed, 9 full at seeded
+Sizes default to the bench workload: the model's layers (MiMo-V2.6-Flash: 48,
+39 windowed + 9 full; MiMo-V2.6-Pro: 70, 60 + 10; the full layers at seeded
 indices), an 8192-token chunk at positions 131072..139263 and 128 decode
 sequences with contexts U{4096..262144}.  Per-layer q/k/v are generated up
 front; the full layers share one pool (each full layer reads the same number
-of bytes, and nine separate pools would exceed one GPU's memory).
+of bytes, and a pool per full layer would exceed one GPU's memory).
 """
 from __future__ import annotations
 
@@ -31,26 +32,31 @@ from . import workloads as wl
 
 class HybridStep:
     def __init__(self, hsw, pattern=None, T=8192, P0=131072, S=128, ctx_lo=4096, ctx_hi=262144, seed=5,
-                 device="cuda:0", chunk=2048):
+                 device="cuda:0", chunk=2048, model=wl.FLASH):
         self.hsw = hsw
-        self.pattern = list(wl.hybrid_pattern(seed=seed)) if pattern is None else list(pattern)
+        self.model = model
+        self.pattern = (list(wl.hybrid_pattern(seed, model.n_layers, model.n_full)) if pattern is None
+                        else list(pattern))
         self.T, self.P0, self.S, self.chunk = T, P0, S, chunk
-        self.swa, self.full = wl.swa_shape(), wl.full_shape()
+        hq, hs, hf = model.n_q_heads, model.swa_kv_heads, model.full_kv_heads
+        self.hq, self.hkv_swa, self.hkv_full = hq, hs, hf
+        self.swa = wl.swa_shape(hq, hs, value_scale=model.value_scale)
+        self.full = wl.full_shape(hq, hf, value_scale=model.value_scale)
         g = wl.gen(seed)
         self.L = torch.randint(ctx_lo, ctx_hi + 1, (S,), generator=g, dtype=torch.int64)
         gd = wl.gen(seed * 1000, device)
         self.layers = []
         for kind in self.pattern:
-            hkv = 8 if kind == 1 else 4
-            d = dict(qc=wl.randn((T, 64, 192), gd, device=device), kc=wl.randn((T, hkv, 192), gd, device=device),
-                     vc=wl.randn((T, hkv, 128), gd, device=device), qd=wl.randn((S, 64, 192), gd, device=device),
+            hkv = hs if kind == 1 else hf
+            d = dict(qc=wl.randn((T, hq, 192), gd, device=device), kc=wl.randn((T, hkv, 192), gd, device=device),
+                     vc=wl.randn((T, hkv, 128), gd, device=device), qd=wl.randn((S, hq, 192), gd, device=device),
                      kd=wl.randn((S, hkv, 192), gd, device=device), vd=wl.randn((S, hkv, 128), gd, device=device))
             if kind == 1:
                 # rings: decode sequences 0..S-1, the chunk's sequence at index S
-                d["kring"] = wl.randn((S + 1, 8, 128, 192), gd, device=device)
-                d["vring"] = wl.randn((S + 1, 8, 128, 128), gd, device=device)
+                d["kring"] = wl.randn((S + 1, hs, 128, 192), gd, device=device)
+                d["vring"] = wl.randn((S + 1, hs, 128, 128), gd, device=device)
             self.layers.append(d)
-        self.sinks = wl.sinks(64, g).to(device)
+        self.sinks = wl.sinks(hq, g).to(device)
         # shared full-attention pool: the chunk sequence at rows [0, P0 + T),
         # then the decode sequences
         base = torch.zeros(S, dtype=torch.int64)
@@ -58,8 +64,8 @@ class HybridStep:
         base[1:] = P0 + T + torch.cumsum(self.L, 0)[:-1]
         self.base_dec = base
         self.rows = int(P0 + T + self.L.sum())
-        self.kpool = wl.randn((self.rows, 4, 192), gd, device=device)
-        self.vpool = wl.randn((self.rows, 4, 128), gd, device=device)
+        self.kpool = wl.randn_rows((self.rows, hf, 192), gd, device=device)
+        self.vpool = wl.randn_rows((self.rows, hf, 128), gd, device=device)
         self.d_L, self.d_base_dec = self.L.to(device), base.to(device)
         self.d_pos_dec = (self.L - 1).to(device)
         self.d_seq_dec = torch.arange(S, dtype=torch.int32, device=device)
@@ -69,12 +75,12 @@ class HybridStep:
         self.d_start = torch.tensor([P0], dtype=torch.int64, device=device)
         self.d_base_c = torch.zeros(1, dtype=torch.int64, device=device)
         bf = torch.bfloat16
-        self.q_rot = torch.empty((T, 64, 192), dtype=bf, device=device)
-        self.q_rot_d = torch.empty((S, 64, 192), dtype=bf, device=device)
-        self.kst = torch.empty((T, 8, 192), dtype=bf, device=device)
-        self.vst = torch.empty((T, 8, 128), dtype=bf, device=device)
-        self.out = torch.empty((T, 64, 128), dtype=bf, device=device)
-        self.out_d = torch.empty((S, 64, 128), dtype=bf, device=device)
+        self.q_rot = torch.empty((T, hq, 192), dtype=bf, device=device)
+        self.q_rot_d = torch.empty((S, hq, 192), dtype=bf, device=device)
+        self.kst = torch.empty((T, hs, 192), dtype=bf, device=device)
+        self.vst = torch.empty((T, hs, 128), dtype=bf, device=device)
+        self.out = torch.empty((T, hq, 128), dtype=bf, device=device)
+        self.out_d = torch.empty((S, hq, 128), dtype=bf, device=device)
         self.max_ctx = int(self.L.max())
         self.wsb = hsw.hsw_full_decode_workspace_bytes(self.full, S, self.max_ctx, chunk)
         self.ws = torch.empty(self.wsb // 4 + 4, dtype=torch.float32, device=device)
@@ -130,4 +136,4 @@ class HybridStep:
 
     @property
     def pool_gb(self):
-        return self.rows * 4 * 320 * 2 / 1e9
+        return self.rows * self.hkv_full * 320 * 2 / 1e9

@@ -8,9 +8,12 @@ Shapes follow the pages: MiMo-V2.6-Flash windowed layers have 8 KV heads and
 full layers 4 (colibri "What the engine implements"), q/k heads are 192 wide
 and v heads 128, the window/ring is 128 positions, 48 layers of which 39 are
 windowed (colibri, model table).  The query head count of Flash is not printed
-on the pages; 64 is used.  Prefill chunks of 8192 tokens and contexts up to
-512K come from the gaudi-cookbook page ("At a glance", "Tiled global-attention
-prefill").
+on the pages; 64 is used.  MiMo-V2.6-Pro has 70 layers, 60 windowed + 10 full
+(colibri, model table), 128 query and 8 KV heads, one KV head per rank on both
+layer kinds at TP8 (gaudi-cookbook, "MiMo-V2.6-Pro"), and value scale 0.612
+against Flash's 0.707 (colibri, "What the engine implements").  Prefill
+chunks of 8192 tokens and contexts up to 512K come from the gaudi-cookbook
+page ("At a glance", "Tiled global-attention prefill").
 
 Recipes (every draw comes from a torch.Generator seeded as stated):
   * values: standard normal fp32, rounded to bf16 (round-to-nearest-even) for
@@ -33,6 +36,23 @@ THETA_SWA, THETA_FULL = 1.0e4, 1.0e7
 VALUE_SCALE_FLASH, VALUE_SCALE_PRO = 0.707, 0.612
 SOFTMAX_SCALE = 1.0 / math.sqrt(D_QK)
 LOGIT_SHIFT_Q, LOGIT_SHIFT_K = 38.12, 9.09
+
+
+@dataclasses.dataclass(frozen=True)
+class Model:
+    """Head counts, value scale and layer mix of one model of the family."""
+    name: str
+    n_q_heads: int
+    swa_kv_heads: int
+    full_kv_heads: int
+    value_scale: float
+    n_layers: int
+    n_full: int
+
+
+FLASH = Model("MiMo-V2.6-Flash", 64, 8, 4, VALUE_SCALE_FLASH, 48, 9)
+PRO = Model("MiMo-V2.6-Pro", 128, 8, 8, VALUE_SCALE_PRO, 70, 10)
+MODELS = {"flash": FLASH, "pro": PRO}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -73,6 +93,21 @@ def randn(shape, g: torch.Generator, dtype=torch.bfloat16, device="cpu") -> torc
     return x.to(dtype)
 
 
+def randn_rows(shape, g: torch.Generator, dtype=torch.bfloat16, device="cpu",
+               max_elems=1 << 28) -> torch.Tensor:
+    """randn() drawn slice by slice along the first dimension (at most
+    max_elems per slice), so a pool far larger than free memory / 3 can be
+    filled without one fp32 temporary of its whole size.  Deterministic for a
+    given generator state and max_elems."""
+    out = torch.empty(tuple(shape), dtype=dtype, device=device)
+    per_row = max(1, math.prod(shape[1:]))
+    step = max(1, max_elems // per_row)
+    for r0 in range(0, shape[0], step):
+        r1 = min(shape[0], r0 + step)
+        out[r0:r1] = randn((r1 - r0, *shape[1:]), g, dtype, device)
+    return out
+
+
 def sinks(n_q_heads: int, g: torch.Generator) -> torch.Tensor:
     return (1.0 + 0.25 * torch.randn((n_q_heads,), generator=g, dtype=torch.float32))
 
@@ -99,7 +134,7 @@ def logit_shift_layer(seed=1, n_tok=512, hq=4, hkv=1, dtype=torch.float32, start
 # Workload 2: windowed prefill, S sequences x T tokens from position `start`.
 # --------------------------------------------------------------------------
 def swa_prefill_batch(seed=2, n_seqs=4, seqlens=(8192,) * 4, start_pos=None, hq=64, hkv=8,
-                      dtype=torch.bfloat16, device="cpu"):
+                      dtype=torch.bfloat16, device="cpu", value_scale=VALUE_SCALE_FLASH):
     """q/k/v for a prefill chunk of `n_seqs` sequences (ragged lengths allowed)
     plus, for each sequence, a ring already holding the 127 positions before
     its start (zeros where the position would be < 0 are never read)."""
@@ -117,7 +152,7 @@ def swa_prefill_batch(seed=2, n_seqs=4, seqlens=(8192,) * 4, start_pos=None, hq=
     cu[1:] = torch.cumsum(torch.tensor(seqlens, dtype=torch.int64), 0)
     pos = torch.cat([torch.arange(s, s + n, dtype=torch.int64) for s, n in zip(start, seqlens)])
     seq = torch.cat([torch.full((n,), i, dtype=torch.int32) for i, n in enumerate(seqlens)])
-    return dict(shape=swa_shape(hq, hkv, dtype=dtype), q=q, k=k, v=v, kring=kring,
+    return dict(shape=swa_shape(hq, hkv, dtype=dtype, value_scale=value_scale), q=q, k=k, v=v, kring=kring,
                 vring=vring, pos=pos, seq=seq, cu_seqlens=cu,
                 start_pos=torch.tensor(start, dtype=torch.int64), sinks=sinks(hq, g))
 
@@ -126,7 +161,7 @@ def swa_prefill_batch(seed=2, n_seqs=4, seqlens=(8192,) * 4, start_pos=None, hq=
 # Workload 3: windowed decode, S sequences at positions U{lo .. hi}.
 # --------------------------------------------------------------------------
 def swa_decode_batch(seed=3, n_seqs=256, pos_lo=128, pos_hi=524288, hq=64, hkv=8,
-                     dtype=torch.bfloat16, device="cpu", positions=None):
+                     dtype=torch.bfloat16, device="cpu", positions=None, value_scale=VALUE_SCALE_FLASH):
     g = gen(seed)
     if positions is None:
         pos = torch.randint(pos_lo, pos_hi + 1, (n_seqs,), generator=g, dtype=torch.int64)
@@ -139,8 +174,8 @@ def swa_decode_batch(seed=3, n_seqs=256, pos_lo=128, pos_hi=524288, hq=64, hkv=8
     q = randn((n_seqs, hq, D_QK), gd, dtype, device)
     k = randn((n_seqs, hkv, D_QK), gd, dtype, device)
     v = randn((n_seqs, hkv, D_V), gd, dtype, device)
-    return dict(shape=swa_shape(hq, hkv, dtype=dtype), q=q, k=k, v=v, kring=kring, vring=vring,
-                pos=pos, seq=torch.arange(n_seqs, dtype=torch.int32), sinks=s)
+    return dict(shape=swa_shape(hq, hkv, dtype=dtype, value_scale=value_scale), q=q, k=k, v=v, kring=kring,
+                vring=vring, pos=pos, seq=torch.arange(n_seqs, dtype=torch.int32), sinks=s)
 
 
 # --------------------------------------------------------------------------
@@ -149,7 +184,8 @@ def swa_decode_batch(seed=3, n_seqs=256, pos_lo=128, pos_hi=524288, hq=64, hkv=8
 # are prior context, the new token (position L_s - 1) is appended by RoPE.
 # --------------------------------------------------------------------------
 def full_decode_batch(seed=4, n_seqs=64, len_lo=32768, len_hi=131072, hq=64, hkv=4,
-                      dtype=torch.bfloat16, device="cpu", lengths=None, with_sinks=False):
+                      dtype=torch.bfloat16, device="cpu", lengths=None, with_sinks=False,
+                      value_scale=VALUE_SCALE_FLASH):
     g = gen(seed)
     if lengths is None:
         L = torch.randint(len_lo, len_hi + 1, (n_seqs,), generator=g, dtype=torch.int64)
@@ -165,8 +201,8 @@ def full_decode_batch(seed=4, n_seqs=64, len_lo=32768, len_hi=131072, hq=64, hkv
     q = randn((n_seqs, hq, D_QK), gd, dtype, device)
     k = randn((n_seqs, hkv, D_QK), gd, dtype, device)
     v = randn((n_seqs, hkv, D_V), gd, dtype, device)
-    return dict(shape=full_shape(hq, hkv, dtype=dtype), q=q, k=k, v=v, kpool=kpool, vpool=vpool,
-                ctx_len=L, seq_base=base, pos=L - 1, seq=torch.arange(n_seqs, dtype=torch.int32),
+    return dict(shape=full_shape(hq, hkv, dtype=dtype, value_scale=value_scale), q=q, k=k, v=v, kpool=kpool,
+                vpool=vpool, ctx_len=L, seq_base=base, pos=L - 1, seq=torch.arange(n_seqs, dtype=torch.int32),
                 sinks=s)
 
 
@@ -174,7 +210,7 @@ def full_decode_batch(seed=4, n_seqs=64, len_lo=32768, len_hi=131072, hq=64, hkv
 # Workload 5 pieces: full-attention prefill chunk with prior context.
 # --------------------------------------------------------------------------
 def full_prefill_batch(seed=5, n_seqs=1, seqlens=(8192,), start_pos=(131072,), hq=64, hkv=4,
-                       dtype=torch.bfloat16, device="cpu"):
+                       dtype=torch.bfloat16, device="cpu", value_scale=VALUE_SCALE_FLASH):
     """One chunk per sequence: prior rows 0..start-1 in the pool, the chunk's
     own q/k/v at positions start .. start+T-1 (appended by RoPE)."""
     g = gen(seed)
@@ -195,9 +231,16 @@ def full_prefill_batch(seed=5, n_seqs=1, seqlens=(8192,), start_pos=(131072,), h
     cu[1:] = torch.cumsum(torch.tensor(seqlens, dtype=torch.int64), 0)
     pos = torch.cat([torch.arange(s, s + n, dtype=torch.int64) for s, n in zip(start, seqlens)])
     seq = torch.cat([torch.full((n,), i, dtype=torch.int32) for i, n in enumerate(seqlens)])
-    return dict(shape=full_shape(hq, hkv, dtype=dtype), q=q, k=k, v=v, kpool=kpool, vpool=vpool,
-                cu_seqlens=cu, start_pos=torch.tensor(start, dtype=torch.int64), seq_base=base,
+    return dict(shape=full_shape(hq, hkv, dtype=dtype, value_scale=value_scale), q=q, k=k, v=v, kpool=kpool,
+                vpool=vpool, cu_seqlens=cu, start_pos=torch.tensor(start, dtype=torch.int64), seq_base=base,
                 ctx_len=L, pos=pos, seq=seq)
+
+
+def model_kw(model: Model, kind: str) -> dict:
+    """Head counts and value scale of `model` for a batch generator of layer
+    kind "swa" or "full"."""
+    hkv = model.swa_kv_heads if kind == "swa" else model.full_kv_heads
+    return dict(hq=model.n_q_heads, hkv=hkv, value_scale=model.value_scale)
 
 
 def hybrid_pattern(seed=5, n_layers=48, n_full=9):

@@ -2,8 +2,10 @@
 
 One windowed and one full layer of the hybrid step (8192-token chunk at
 positions 131072..139263, 128 decode sequences with contexts
-U{4096..262144}, 64 q heads; 8 / 4 KV heads) run through the same driver the
-bench times (hybrid_sliding_window_amd.hybrid.HybridStep).  After each call
+U{4096..262144}) run through the same driver the bench times
+(hybrid_sliding_window_amd.hybrid.HybridStep), once per model: MiMo-V2.6-Flash
+(64 q heads; 8 / 4 KV heads; value scale 0.707) and MiMo-V2.6-Pro (128 q
+heads, 8 KV heads on both kinds, value scale 0.612).  After each call
 its sampled outputs are checked against the fp64 oracle fed the exact tensors
 the call consumed: RoPE rows within one bf16 ulp, written cache rows exact,
 attention rows to max_abs 2e-2 / mean_rel 2e-3.
@@ -21,6 +23,7 @@ from parity import assert_close
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 hsw = pytest.importorskip("hybrid_sliding_window_amd.hsw")
+from hybrid_sliding_window_amd import workloads as wl  # noqa: E402
 from hybrid_sliding_window_amd.hybrid import HybridStep  # noqa: E402
 
 
@@ -31,10 +34,11 @@ def check_rope(x_in, y, pos, theta, what):
     assert np.all(err <= tol), f"{what}: rope off by up to {float((err - tol).max()):.3e} beyond one bf16 ulp"
 
 
-@pytest.fixture(scope="module")
-def hs():
-    note("hybrid step: building one windowed + one full layer at full size")
-    h = HybridStep(hsw, pattern=[1, 0])
+@pytest.fixture(scope="module", params=["flash", "pro"])
+def hs(request):
+    model = wl.MODELS[request.param]
+    note(f"hybrid step {model.name}: building one windowed + one full layer at full size")
+    h = HybridStep(hsw, pattern=[1, 0], model=model)
     yield h
     del h
     torch.cuda.empty_cache()

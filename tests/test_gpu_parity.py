@@ -50,10 +50,13 @@ def check_rope_values(x_in, y_gpu, pos, theta, rope_dim=64, what=""):
 
 
 # ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("model", ["flash", "pro"])
 @pytest.mark.parametrize("kind", [RING, POOL, STAGING])
-def test_rope_kv_write(kind):
-    note(f"rope kind={kind}")
-    shape = wl.full_shape() if kind == POOL else wl.swa_shape()
+def test_rope_kv_write(kind, model):
+    note(f"rope kind={kind} {model}")
+    m = wl.MODELS[model]
+    shape = (wl.full_shape(m.n_q_heads, m.full_kv_heads, value_scale=m.value_scale) if kind == POOL
+             else wl.swa_shape(m.n_q_heads, m.swa_kv_heads, value_scale=m.value_scale))
     hq, hkv = shape.n_q_heads, shape.n_kv_heads
     g = wl.gen(21 + kind)
     special = [0, 1, 127, 128, 196608, 200000, 205000, 262143, 524287, 524288]
@@ -128,7 +131,7 @@ def test_rope_kv_write(kind):
     # everything not written keeps the sentinel bytes
     assert torch.equal(gk[torch.from_numpy(~written)], kd[torch.from_numpy(~written)])
     assert torch.equal(gv[torch.from_numpy(~written)], vd[torch.from_numpy(~written)])
-    print(f"rope kind={kind}: q_rot bitwise-equal fraction {frac_q:.3f}")
+    print(f"rope kind={kind} {model}: q_rot bitwise-equal fraction {frac_q:.3f}")
 
 
 def test_rope_fp32_logit_shift_layer():
@@ -167,14 +170,16 @@ def run_swa_decode(batch):
     return q_rot, kring, vring, out, idx
 
 
+@pytest.mark.parametrize("model", ["flash", "pro"])
 @pytest.mark.parametrize("case", ["small_positions", "decode_256_seqs"])
-def test_swa_decode(case):
+def test_swa_decode(case, model):
+    mk = wl.model_kw(wl.MODELS[model], "swa")
     if case == "small_positions":
         positions = [0, 1, 2, 5, 63, 126, 127, 128, 129, 255, 1000, 524288]
-        batch = wl.swa_decode_batch(seed=31, n_seqs=len(positions), positions=positions)
+        batch = wl.swa_decode_batch(seed=31, n_seqs=len(positions), positions=positions, **mk)
     else:
-        batch = wl.swa_decode_batch(seed=3)   # 256 sequences at positions U{128..524288}
-    note(f"swa_decode {case}")
+        batch = wl.swa_decode_batch(seed=3, **mk)   # 256 sequences at positions U{128..524288}
+    note(f"swa_decode {case} {model}")
     shape = batch["shape"]
     ring_before = batch["kring"].clone()
     q_rot, kring, vring, out, idx = run_swa_decode(batch)
@@ -197,7 +202,7 @@ def test_swa_decode(case):
         vring64[s, :, P[s] % 128] = f64(batch["v"])[s]
     chain = oracle.ring_decode(qr, P, kring64, vring64, sinks=f64(batch["sinks"]), **shape_kw(shape))
     cma, cmr = errors(f64(out), chain)
-    print(f"swa_decode {case}: bf16-in max_abs={ma:.2e} mean_rel={mr:.2e}; chain max_abs={cma:.2e} mean_rel={cmr:.2e}")
+    print(f"swa_decode {case} {model}: bf16-in max_abs={ma:.2e} mean_rel={mr:.2e}; chain max_abs={cma:.2e} mean_rel={cmr:.2e}")
 
 
 def test_swa_decode_batch_order_bitwise():
@@ -289,11 +294,12 @@ def test_swa_prefill_values_beyond_fp16_range():
     print(f"swa_prefill large V: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
-@pytest.mark.parametrize("hq,hkv", [(64, 8), (128, 8), (32, 8)])
-def test_swa_prefill_ragged(hq, hkv):
+@pytest.mark.parametrize("hq,hkv,lam", [(64, 8, wl.VALUE_SCALE_FLASH), (128, 8, wl.VALUE_SCALE_PRO),
+                                        (32, 8, wl.VALUE_SCALE_FLASH)])
+def test_swa_prefill_ragged(hq, hkv, lam):
     note(f"swa_prefill ragged hq={hq} hkv={hkv}")
     batch = wl.swa_prefill_batch(seed=41, n_seqs=3, seqlens=(300, 17, 1000), start_pos=(0, 5000, 130),
-                                 hq=hq, hkv=hkv)
+                                 hq=hq, hkv=hkv, value_scale=lam)
     q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
     check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
     got = f64(out)
@@ -302,11 +308,12 @@ def test_swa_prefill_ragged(hq, hkv):
     print(f"swa_prefill ragged hq={hq}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
-def test_swa_prefill_full_size_sampled():
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_swa_prefill_full_size_sampled(model):
     """4 x 8192 from position 0: every head of sampled rows (the first 130,
     the last 2 and 124 random per sequence), plus the ring commit."""
-    note("swa_prefill 4x8192 sampled")
-    batch = wl.swa_prefill_batch(seed=2)
+    note(f"swa_prefill 4x8192 sampled {model}")
+    batch = wl.swa_prefill_batch(seed=2, **wl.model_kw(wl.MODELS[model], "swa"))
     q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
     check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
     cu = batch["cu_seqlens"].tolist()
@@ -319,8 +326,8 @@ def test_swa_prefill_full_size_sampled():
     outs = oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb, rows)
     got = np.concatenate([f64(out[torch.from_numpy(sel)]) for sel, _ in outs])
     ref = np.concatenate([o for _, o in outs])
-    ma, mr = assert_close(got, ref, what="swa_prefill 4x8192")
-    print(f"swa_prefill 4x8192 sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    ma, mr = assert_close(got, ref, what=f"swa_prefill 4x8192 {model}")
+    print(f"swa_prefill 4x8192 sampled {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 def test_logit_shift_layer_fp32_chain():
@@ -398,28 +405,31 @@ def oracle_full_decode(batch, q_rot, kpool, vpool, seqs, sinks=None):
     return np.stack(res)
 
 
+@pytest.mark.parametrize("model", ["flash", "pro"])
 @pytest.mark.parametrize("chunk,with_sink", [(2048, False), (1024, False), (2048, True), (128, True)])
-def test_full_decode_small(chunk, with_sink):
-    note(f"full_decode small chunk={chunk} sink={with_sink}")
+def test_full_decode_small(chunk, with_sink, model):
+    note(f"full_decode small chunk={chunk} sink={with_sink} {model}")
     lengths = [1, 2, 127, 2047, 2048, 2049, 9000, 4097]
-    batch = wl.full_decode_batch(seed=61, n_seqs=len(lengths), lengths=lengths, with_sinks=with_sink)
+    batch = wl.full_decode_batch(seed=61, n_seqs=len(lengths), lengths=lengths, with_sinks=with_sink,
+                                 **wl.model_kw(wl.MODELS[model], "full"))
     q_rot, kpool, vpool, out = run_full_decode(batch, chunk, batch["sinks"])
     ref = oracle_full_decode(batch, q_rot, kpool, vpool, range(len(lengths)), batch["sinks"])
     ma, mr = assert_close(f64(out), ref, what="full_decode small")
-    print(f"full_decode chunk={chunk} sink={with_sink}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"full_decode chunk={chunk} sink={with_sink} {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
-def test_full_decode_full_size_sampled():
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_full_decode_full_size_sampled(model):
     """64 sequences with contexts U{32768..131072}: the shortest, the longest
     and two random sequences checked against the oracle, all heads."""
-    note("full_decode 64 seqs sampled")
-    batch = wl.full_decode_batch(seed=4, device=DEV)
+    note(f"full_decode 64 seqs sampled {model}")
+    batch = wl.full_decode_batch(seed=4, device=DEV, **wl.model_kw(wl.MODELS[model], "full"))
     q_rot, kpool, vpool, out = run_full_decode(batch)
     L = batch["ctx_len"].numpy()
     seqs = sorted({int(L.argmin()), int(L.argmax()), 17, 42})
     ref = oracle_full_decode(batch, q_rot, kpool, vpool, seqs)
     ma, mr = assert_close(f64(out[seqs]), ref, what="full_decode 64 seqs")
-    print(f"full_decode 64 seqs (sampled {seqs}): max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"full_decode 64 seqs {model} (sampled {seqs}): max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 # ------------------------------------------------------ full prefill
@@ -460,24 +470,27 @@ def oracle_full_prefill(batch, q_rot, kpool, vpool, rows_per_seq):
     return np.concatenate(got_idx), np.concatenate(refs)
 
 
-def test_full_prefill_ragged():
-    note("full_prefill ragged")
-    batch = wl.full_prefill_batch(seed=71, n_seqs=3, seqlens=(300, 77, 129), start_pos=(3000, 100, 0))
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_full_prefill_ragged(model):
+    note(f"full_prefill ragged {model}")
+    batch = wl.full_prefill_batch(seed=71, n_seqs=3, seqlens=(300, 77, 129), start_pos=(3000, 100, 0),
+                                  **wl.model_kw(wl.MODELS[model], "full"))
     q_rot, kpool, vpool, out = run_full_prefill(batch)
     cu = batch["cu_seqlens"].tolist()
     idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(3)])
     ma, mr = assert_close(f64(out)[idx], ref, what="full_prefill ragged")
-    print(f"full_prefill ragged: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"full_prefill ragged {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
-def test_full_prefill_chunk_8192_after_131072_sampled():
-    note("full_prefill 8192 @ 131072 sampled")
-    batch = wl.full_prefill_batch(seed=5, device=DEV)
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_full_prefill_chunk_8192_after_131072_sampled(model):
+    note(f"full_prefill 8192 @ 131072 sampled {model}")
+    batch = wl.full_prefill_batch(seed=5, device=DEV, **wl.model_kw(wl.MODELS[model], "full"))
     q_rot, kpool, vpool, out = run_full_prefill(batch)
     rows = [np.array([0, 1, 2, 1000, 4095, 6000, 8190, 8191])]
     idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, rows)
     ma, mr = assert_close(f64(out[torch.from_numpy(idx)]), ref, what="full_prefill 8192")
-    print(f"full_prefill 8192@131072 sampled: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"full_prefill 8192@131072 sampled {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 def test_full_prefill_values_beyond_fp16_range():
