@@ -131,13 +131,35 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
     warm(call, stream)
     t_call = ev_time(call, steps, stream)
     t_rope = ev_time(rope, max(steps, 20), stream)
+
+    # the fused chain: K/V-only RoPE into staging, then the prefill that
+    # rotates q itself (no q_rot written or read)
+    def rope_kv(i):
+        hsw.hsw_rope_partial_kv_write(sh, T, None, d["k"], d["v"], d["pos"], None, hsw.HSW_DST_STAGING,
+                                      kst, vst, T, None, None, None, stream)
+
+    def fused(i):
+        hsw.hsw_swa_prefill_qrope(sh, S, T1, d["cu_seqlens"], d["start_pos"], d["q"], kst, vst, d["kring"],
+                                  d["vring"], d["sinks"], out, stream)
+    fused(0)
+    warm(fused, stream)
+    t_fused = ev_time(fused, steps, stream)
+    t_rope_kv = ev_time(rope_kv, max(steps, 20), stream)
     pairs = swa_prefill_pairs([T1] * S, [0] * S)
     flops = pairs * hq * 2 * (192 + 128)
     # algorithmic bytes: q_rot, staged K/V read once, out written once, the
     # ring commit (last 128 rows of K and V per sequence) written once
     bytes_ = T * hq * 192 * 2 + T * hkv * (192 + 128) * 2 + T * hq * 128 * 2 + S * hkv * 128 * (192 + 128) * 2
     rope_bytes = T * 2 * (hq * 192 + hkv * 192 + hkv * 128) * 2
+    rope_kv_bytes = T * 2 * (hkv * 192 + hkv * 128) * 2
+    fused_res = dict(ms=t_fused, gbs=bytes_ / t_fused / 1e6, tflops=flops / t_fused / 1e9,
+                     rope_kv_ms=t_rope_kv, rope_kv_gbs=rope_kv_bytes / t_rope_kv / 1e6,
+                     chain_ms=t_rope_kv + t_fused, unfused_chain_ms=t_rope + t_call,
+                     chain_bytes=rope_kv_bytes + bytes_, unfused_chain_bytes=rope_bytes + bytes_,
+                     workload="K/V-only RoPE + hsw_swa_prefill_qrope (q rotated in the kernel) against "
+                              "RoPE + hsw_swa_prefill, same workload")
     return dict(
+        fused=fused_res,
         ms=t_call, flops=flops, bytes=bytes_, tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
         frac_mfma_peak=flops / t_call / 1e9 / BF16_PEAK_TFLOPS, frac_hbm_peak=bytes_ / t_call / 1e6 / HBM_PEAK_GBS,
         workload=f"windowed prefill, 4 x 8192 tokens from position 0, {heads(model)}, window 128",
@@ -181,15 +203,37 @@ def bench_swa_decode(hsw, wl, steps, stream, replicas=8, model=None):
     def call(i):
         d = reps[i % replicas]
         hsw.hsw_swa_decode(sh, S, d["pos"], d["q_rot"], d["kring"], d["vring"], d["sinks"], d["out"], stream)
+
+    def fused(i):
+        d = reps[i % replicas]
+        hsw.hsw_swa_decode_qrope(sh, S, d["pos"], d["q"], d["kring"], d["vring"], d["sinks"], d["out"], stream)
+
+    def rope(i):
+        d = reps[i % replicas]
+        hsw.hsw_rope_partial_kv_write(sh, S, d["q"], d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_RING,
+                                      d["kring"], d["vring"], S, None, d["q_rot"], None, stream)
+
+    def rope_kv(i):
+        d = reps[i % replicas]
+        hsw.hsw_rope_partial_kv_write(sh, S, None, d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_RING,
+                                      d["kring"], d["vring"], S, None, None, None, stream)
     for i in range(2 * replicas):
         call(i)
+        fused(i)
     warm(call, stream)
     n = max(steps, 25) * replicas
     t = ev_time(call, n, stream)
+    t_fused = ev_time(fused, n, stream)
+    t_rope = ev_time(rope, n, stream)
+    t_rope_kv = ev_time(rope_kv, n, stream)
     bytes_ = S * (hkv * 128 * (192 + 128) * 2 + hq * 192 * 2 + hq * 128 * 2)
     flops = S * hq * 128 * 2 * (192 + 128)
+    fused_res = dict(ms=t_fused, gbs=bytes_ / t_fused / 1e6, rope_kv_ms=t_rope_kv, rope_ms=t_rope,
+                     chain_ms=t_rope_kv + t_fused, unfused_chain_ms=t_rope + t,
+                     workload="K/V-only RoPE into the rings + hsw_swa_decode_qrope (q rotated in the "
+                              "kernel, kept in fp32) against RoPE + hsw_swa_decode, same workload")
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
-                flops=flops, launches=n, replicas=replicas,
+                flops=flops, launches=n, replicas=replicas, fused=fused_res,
                 workload=f"windowed decode, 256 sequences at positions U{{128..524288}}, {heads(model)}, "
                          "128-slot ring")
 
@@ -295,10 +339,12 @@ def bench_pro(hsw, wl, args, stream):
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream, m)
     print(f"[bench] pro swa_prefill {pre['ms']:.3f} ms {pre['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     out["rope_partial_kv_write"] = rounded(pre.pop("rope"))
+    out["swa_prefill_qrope"] = rounded(pre.pop("fused"))
     out["swa_prefill"] = rounded(pre)
     torch.cuda.empty_cache()
     dec = bench_swa_decode(hsw, wl, args.steps, stream, model=m)
     print(f"[bench] pro swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    out["swa_decode_qrope"] = rounded(dec.pop("fused"))
     out["swa_decode"] = rounded(dec)
     torch.cuda.empty_cache()
     fd = bench_full_decode(hsw, wl, args.steps, stream, m)
@@ -378,11 +424,16 @@ def main():
         return
 
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
-    print(f"[bench] swa_prefill {pre['ms']:.3f} ms {pre['tflops']:.1f} TFLOP/s {pre['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] swa_prefill {pre['ms']:.3f} ms {pre['tflops']:.1f} TFLOP/s {pre['gbs']:.0f} GB/s; fused q-RoPE "
+          f"{pre['fused']['ms']:.3f} ms, chain {pre['fused']['chain_ms']:.3f} vs {pre['fused']['unfused_chain_ms']:.3f} ms",
+          file=sys.stderr, flush=True)
     dec = bench_swa_decode(hsw, wl, args.steps, stream)
-    print(f"[bench] swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s; fused q-RoPE "
+          f"{dec['fused']['ms'] * 1e3:.1f} us, chain {dec['fused']['chain_ms'] * 1e3:.1f} vs "
+          f"{dec['fused']['unfused_chain_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
-    calls = {"rope_partial_kv_write": pre.pop("rope"), "swa_decode": dec}
+    calls = {"rope_partial_kv_write": pre.pop("rope"), "swa_prefill_qrope": pre.pop("fused"),
+             "swa_decode_qrope": dec.pop("fused"), "swa_decode": dec}
     if not args.quick:
         fd = bench_full_decode(hsw, wl, args.steps, stream)
         print(f"[bench] full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s", file=sys.stderr, flush=True)

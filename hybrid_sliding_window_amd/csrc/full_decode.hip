@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void full_decode_combine_kernel(AttnArgs 
     }
     float r = z > 0.0f ? a.value_scale / z : 0.0f;
     uint16_t *out = (uint16_t *)a.out + wid * DV + 2 * lane;
-    *reinterpret_cast<uint32_t *>(out) = (uint32_t)f2bf(o0 * r) | ((uint32_t)f2bf(o1 * r) << 16);
+    *reinterpret_cast<uint32_t *>(out) = pack_bf16x2(o0 * r, o1 * r);
 }
 
 }  // namespace

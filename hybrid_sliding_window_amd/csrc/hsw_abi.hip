@@ -68,6 +68,12 @@ hsw_status launched(hipError_t e, const char *what) {
     return HSW_OK;
 }
 
+// theta^(-2i/rope_dim) in double (colibri "What the engine implements"),
+// computed once per call on the host and handed to the kernels.
+double inv_freq(const hsw_attn_shape *sh, int i) {
+    return pow(sh->rope_theta, -2.0 * (double)i / (double)sh->rope_dim);
+}
+
 hsw::AttnArgs base_args(const hsw_attn_shape *sh) {
     hsw::AttnArgs a;
     memset(&a, 0, sizeof a);
@@ -78,6 +84,8 @@ hsw::AttnArgs base_args(const hsw_attn_shape *sh) {
     a.window = sh->window;
     a.scale = sh->softmax_scale;
     a.value_scale = sh->value_scale;
+    a.rope_dim = sh->rope_dim;
+    for (int i = 0; i < sh->rope_dim / 2 && i < 32; ++i) a.inv_freq[i] = inv_freq(sh, i);
     return a;
 }
 
@@ -117,8 +125,12 @@ hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens,
     if (dst_capacity < 0) return fail(HSW_E_SHAPE, "dst_capacity < 0");
     if (sh->rope_dim / 2 > 128) return fail(HSW_E_SHAPE, "rope_dim > 256 is not supported");
     if (n_tokens > 0x7fffffffLL) return fail(HSW_E_SHAPE, "n_tokens exceeds 2^31 - 1");
-    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(pos);
-    REQUIRE_PTR(k_dst); REQUIRE_PTR(v_dst); REQUIRE_PTR(q_rot);
+    // q and q_rot both NULL: write K/V only (for the calls that rotate q
+    // themselves); one without the other is an error.
+    if (!q != !q_rot) return fail(HSW_E_NULL, "%s is NULL (q and q_rot must both be given, or both NULL)",
+                                  q ? "q_rot" : "q");
+    REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(pos);
+    REQUIRE_PTR(k_dst); REQUIRE_PTR(v_dst);
     if (dst_kind != HSW_DST_STAGING) REQUIRE_PTR(seq);
     if (dst_kind == HSW_DST_POOL) REQUIRE_PTR(seq_base);
     REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(k_dst, 16);
@@ -129,7 +141,8 @@ hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens,
     memset(&a, 0, sizeof a);
     a.q = q; a.k = k; a.v = v; a.pos = pos; a.seq = seq; a.seq_base = seq_base;
     a.k_dst = k_dst; a.v_dst = v_dst; a.q_rot = q_rot; a.dst_index_out = dst_index_out;
-    a.n_tokens = n_tokens; a.dst_capacity = dst_capacity; a.theta = sh->rope_theta;
+    a.n_tokens = n_tokens; a.dst_capacity = dst_capacity;
+    for (int i = 0; i < sh->rope_dim / 2; ++i) a.inv_freq[i] = inv_freq(sh, i);
     a.hq = sh->n_q_heads; a.hkv = sh->n_kv_heads; a.dqk = sh->d_qk; a.dv = sh->d_v;
     a.rope_dim = sh->rope_dim; a.window = sh->window; a.dst_kind = dst_kind;
     return launched(hsw::launch_rope(a, sh->dtype, (hipStream_t)stream), "rope_partial_kv_write");
@@ -185,6 +198,57 @@ hsw_status hsw_swa_decode(const hsw_attn_shape *sh, int32_t n_seqs, const int64_
                        ? hsw::launch_swa_decode(a, s)
                        : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
     return launched(e, "swa_decode");
+}
+
+hsw_status hsw_swa_prefill_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                                 const int64_t *cu_seqlens, const int64_t *start_pos, const void *q,
+                                 const void *k_stage, const void *v_stage, void *k_ring, void *v_ring,
+                                 const float *sinks, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, 1);
+    if (st) return st;
+    if (n_seqs < 0 || max_seqlen < 0) return fail(HSW_E_SHAPE, "n_seqs and max_seqlen must be >= 0");
+    if ((int64_t)n_seqs * max_seqlen * sh->n_q_heads > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "n_seqs * max_seqlen * n_q_heads exceeds 2^31 - 1");
+    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(start_pos); REQUIRE_PTR(q); REQUIRE_PTR(k_stage);
+    REQUIRE_PTR(v_stage); REQUIRE_PTR(k_ring); REQUIRE_PTR(v_ring); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k_stage, 16); REQUIRE_ALIGN(v_stage, 16);
+    REQUIRE_ALIGN(k_ring, 16); REQUIRE_ALIGN(v_ring, 16); REQUIRE_ALIGN(out, 16);
+    REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(start_pos, 8); REQUIRE_ALIGN(sinks, 4);
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kSwaPrefill;
+    a.qrope = 1;
+    if (!hsw::swa_qrope_ok(a, sh->dtype, sh->out_dtype, true))
+        return fail(HSW_E_SHAPE, "swa_prefill_qrope needs bf16 in and out, d_qk 192, d_v 128, rope_dim 64, "
+                                 "window 128 and 2, 4, 8 or 16 query heads per KV head");
+    if (n_seqs == 0 || max_seqlen == 0) return HSW_OK;
+    a.q = q; a.k_main = k_stage; a.v_main = v_stage; a.k_ring = k_ring; a.v_ring = v_ring;
+    a.sinks = sinks; a.cu_seqlens = cu_seqlens; a.start_pos = start_pos; a.out = out;
+    a.n_seqs = n_seqs; a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = launched(hsw::launch_swa_prefill(a, s), "swa_prefill_qrope"))) return st;
+    return launched(hsw::launch_ring_commit(a, sh->dtype, s), "swa_prefill_qrope ring commit");
+}
+
+hsw_status hsw_swa_decode_qrope(const hsw_attn_shape *sh, int32_t n_seqs, const int64_t *pos,
+                                const void *q, const void *k_ring, const void *v_ring,
+                                const float *sinks, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, 1);
+    if (st) return st;
+    if (n_seqs < 0) return fail(HSW_E_SHAPE, "n_seqs < 0");
+    if ((int64_t)n_seqs * sh->n_q_heads > 0x7fffffffLL) return fail(HSW_E_SHAPE, "n_seqs * n_q_heads exceeds 2^31 - 1");
+    REQUIRE_PTR(pos); REQUIRE_PTR(q); REQUIRE_PTR(k_ring); REQUIRE_PTR(v_ring); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k_ring, 16); REQUIRE_ALIGN(v_ring, 16);
+    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(pos, 8); REQUIRE_ALIGN(sinks, 4);
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kSwaDecode;
+    a.qrope = 1;
+    if (!hsw::swa_qrope_ok(a, sh->dtype, sh->out_dtype, false))
+        return fail(HSW_E_SHAPE, "swa_decode_qrope needs bf16 in and out, d_qk 192, d_v 128, rope_dim 64, "
+                                 "window 128, n_q_heads <= 256 and 1, 2, 4, 8 or 16 query heads per KV head");
+    if (n_seqs == 0) return HSW_OK;
+    a.q = q; a.k_main = k_ring; a.v_main = v_ring; a.sinks = sinks; a.pos = pos; a.out = out;
+    a.n_seqs = n_seqs; a.n_rows = n_seqs;
+    return launched(hsw::launch_swa_decode(a, (hipStream_t)stream), "swa_decode_qrope");
 }
 
 size_t hsw_full_decode_workspace_bytes(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,

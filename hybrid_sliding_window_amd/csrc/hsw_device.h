@@ -91,8 +91,19 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
     return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (a low, b high), round to nearest even: one
+// v_cvt_pk_bf16_f32 (converting the halves one at a time costs three
+// instructions per pair).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+
 // Split four fp32 values into bf16 hi = bf16(p) and lo = bf16(p - hi) so that
-// hi + lo carries about 16 significant bits of p.
+// hi + lo carries about 16 significant bits of p.  (Element by element: the
+// packed-pair form needs more live registers where the prefill kernels sit at
+// the 256-VGPR limit, and spilled there.)
 __device__ __forceinline__ void split_hi_lo(const float p[4], u32x2 &hi, u32x2 &lo) {
     uint16_t h[4], l[4];
 #pragma unroll
@@ -119,6 +130,59 @@ __device__ __forceinline__ float quad_max(float v) {
 __device__ __forceinline__ float quad_sum(float v) {
     v = wave_sum_xor(v, 16);
     return wave_sum_xor(v, 32);
+}
+
+// Rotate-half RoPE pieces shared by the RoPE kernel and the attention kernels
+// that rotate q as they load it, so both produce the same bits.
+// colibri "What the engine implements": pairs (i, i + rope_dim/2) of the
+// first rope_dim dims turn by pos * theta^(-2i/rope_dim); gaudi-cookbook
+// "The RoPE fix for large positions": that angle reaches 5e5 rad and must be
+// formed and reduced in double precision.  The frequencies theta^(-2i/R) come
+// from the host (libm pow in double).  Here a = pos * inv_freq in double, then
+// Cody-Waite reduction by pi/2 in double: k = rint(a * 2/pi),
+// r = (a - k * PIO2_HI) - k * PIO2_LO with PIO2_HI + PIO2_LO = pi/2 to 3.5e-27
+// (each step one fma, whose product is exact), so |r| <= pi/4 carries the
+// angle to about one double ulp of a.  cos r and sin r are then the Taylor
+// polynomials through r^10 / r^9 in fp32 (truncation below 2e-9 on
+// |r| <= pi/4) and the quadrant k mod 4 swaps / negates them.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, double inv_freq, float &c, float &s) {
+    constexpr double kTwoOverPi = 0.6366197723675814;
+    constexpr double kPio2Hi = 1.5707963267341256;      // pi/2 to 33 bits
+    constexpr double kPio2Lo = 6.077100506506192e-11;   // pi/2 - kPio2Hi
+    const double a = (double)pos * inv_freq;
+    const double k = rint(a * kTwoOverPi);
+    const double r = fma(-k, kPio2Lo, fma(-k, kPio2Hi, a));
+    const float x = (float)r, x2 = x * x;
+    float sp = fmaf(x2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+    sp = fmaf(x2, sp, 1.0f / 120.0f);
+    sp = fmaf(x2, sp, -1.0f / 6.0f);
+    const float sr = fmaf(x * x2, sp, x);
+    float cp = fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+    cp = fmaf(x2, cp, -1.0f / 720.0f);
+    cp = fmaf(x2, cp, 1.0f / 24.0f);
+    cp = fmaf(x2, cp, -0.5f);
+    const float cr = fmaf(x2, cp, 1.0f);
+    const int q = (int)((long long)k & 3);
+    c = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+    s = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
+}
+// (x_lo, x_hi) -> (x_lo c - x_hi s, x_hi c + x_lo s), with the fused
+// multiply-adds spelled out so every kernel rounds identically.
+__device__ __forceinline__ void rope_rotate(float xl, float xh, float c, float s, float &yl, float &yh) {
+    yl = fmaf(xl, c, -(xh * s));
+    yh = fmaf(xh, c, xl * s);
+}
+// The same on 8 packed bf16 pairs (16 bytes each), rounded to bf16.
+__device__ __forceinline__ void rope_rotate_bf16x8(u32x4 &lo, u32x4 &hi, const float c[8], const float s[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float yl0, yh0, yl1, yh1;
+        rope_rotate(__uint_as_float(lo[i] << 16), __uint_as_float(hi[i] << 16), c[2 * i], s[2 * i], yl0, yh0);
+        rope_rotate(__uint_as_float(lo[i] & 0xffff0000u), __uint_as_float(hi[i] & 0xffff0000u), c[2 * i + 1],
+                    s[2 * i + 1], yl1, yh1);
+        lo[i] = pack_bf16x2(yl0, yl1);
+        hi[i] = pack_bf16x2(yh0, yh1);
+    }
 }
 
 // Element access for the two storage types.

@@ -15,8 +15,8 @@ struct RopeArgs {
     void *k_dst, *v_dst, *q_rot;
     int64_t *dst_index_out;
     int64_t n_tokens, dst_capacity;
-    double theta;
     int hq, hkv, dqk, dv, rope_dim, window, dst_kind;
+    double inv_freq[128];      // theta^(-2i/rope_dim), i < rope_dim/2
 };
 
 // Attention call kinds served by the generic (any dtype / shape) kernel.
@@ -42,12 +42,16 @@ struct AttnArgs {
     int n_seqs, hq, hkv, dqk, dv, window, chunk, n_chunks;
     float scale, value_scale;
     int kind;
+    int qrope;                 // 1: q is unrotated; the kernel applies RoPE to it
+    int rope_dim;
+    double inv_freq[32];       // theta^(-2i/rope_dim), i < min(rope_dim/2, 32)
 };
 
 hipError_t launch_rope(const RopeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_generic_attn(const AttnArgs &a, int dtype, int out_dtype, hipStream_t s);
 hipError_t launch_ring_commit(const AttnArgs &a, int dtype, hipStream_t s);
 bool swa_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
+bool swa_qrope_ok(const AttnArgs &a, int dtype, int out_dtype, bool prefill);
 hipError_t launch_swa_decode(const AttnArgs &a, hipStream_t s);
 bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
 hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s);

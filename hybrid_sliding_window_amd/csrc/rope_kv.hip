@@ -6,8 +6,8 @@
 // applied to the attention output instead, equal by linearity).
 // gaudi-cookbook "MiMo-V2.6-Flash on Gaudi 2", "The RoPE fix for large
 // positions": an fp32 angle is wrong at large positions, so every angle
-// pos * theta^(-2i/R) is formed in double precision and sin/cos are taken in
-// double (full range reduction); only the rotation itself is fp32.
+// pos * theta^(-2i/R) is formed and reduced modulo pi/2 in double precision
+// (rope_cos_sin); sin/cos of the reduced angle and the rotation are fp32.
 // colibri "System One mode and prompt reuse": K/V of position p go to ring
 // slot p mod window (windowed layers) or to row seq_base + p (full layers).
 //
@@ -37,7 +37,7 @@ template <> struct Chunk8<uint16_t> {  // 8 bf16 = 16 bytes
     __device__ void set_all(const float f[8]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
+            r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     }
 };
 template <> struct Chunk8<float> {  // 8 fp32 = 32 bytes
@@ -63,13 +63,11 @@ __global__ __launch_bounds__(kThreads) void rope_kv_kernel(RopeArgs a) {
     const int64_t p = a.pos[t];
 
     if (threadIdx.x < half) {
-        // angle = p * theta^(-2i/R) in double; sincos reduces in double.
-        double inv_freq = pow(a.theta, -2.0 * (double)threadIdx.x / (double)a.rope_dim);
-        double ang = (double)p * inv_freq;
-        double s, c;
-        sincos(ang, &s, &c);
-        cs[threadIdx.x] = (float)c;
-        sn[threadIdx.x] = (float)s;
+        // angle = p * theta^(-2i/R) formed and reduced in double
+        float c, s;
+        rope_cos_sin(p, a.inv_freq[threadIdx.x], c, s);
+        cs[threadIdx.x] = c;
+        sn[threadIdx.x] = s;
     }
     if (threadIdx.x == 0) {
         int64_t idx = -1, row = -1;
@@ -99,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void rope_kv_kernel(RopeArgs a) {
     const int pass = (a.dqk - a.rope_dim) / 8;       // pass-through items per q/k head
     const int per_qk = units + pass;
     const int per_v = a.dv / 8;
-    const int n_q = a.hq * per_qk, n_k = a.hkv * per_qk, n_v = a.hkv * per_v;
+    // q == NULL: K/V only (the attention call rotates q itself)
+    const int n_q = a.q ? a.hq * per_qk : 0, n_k = a.hkv * per_qk, n_v = a.hkv * per_v;
     const int64_t row = dst_row;
     // K/V row stride between heads: ring rows interleave (head, slot).
     const int64_t head_stride = (a.dst_kind == 0) ? (int64_t)a.window : 1;
@@ -127,12 +126,8 @@ __global__ __launch_bounds__(kThreads) void rope_kv_kernel(RopeArgs a) {
                 hi.load(src + 8 * item + half);
                 float ylo[8], yhi[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float c = cs[8 * item + e], s = sn[8 * item + e];
-                    float xl = lo.get(e), xh = hi.get(e);
-                    ylo[e] = xl * c - xh * s;
-                    yhi[e] = xh * c + xl * s;
-                }
+                for (int e = 0; e < 8; ++e)
+                    rope_rotate(lo.get(e), hi.get(e), cs[8 * item + e], sn[8 * item + e], ylo[e], yhi[e]);
                 lo.set_all(ylo);
                 hi.set_all(yhi);
                 lo.store(dst + 8 * item);

@@ -25,6 +25,13 @@
 //                    (V is placed in MFMA fragment order by the loads);
 // then the four waves' (max, sum, O) partials meet in LDS (in the V buffer the
 // wave has finished with) and are combined with the sink, scaled and stored.
+//
+// With QROPE the kernel reads unrotated q and applies the rotate-half RoPE
+// itself (colibri "What the engine implements"; angle formed and reduced in
+// double as the gaudi-cookbook "The RoPE fix for large positions" requires):
+// the rotated rotary dims stay fp32 and enter S^T as bf16 hi + lo (two MFMAs
+// on those two of the six steps), so q loses nothing to a bf16 q_rot and no
+// q_rot is written or read.
 #include "hsw_device.h"
 #include "hsw_launch.h"
 
@@ -92,13 +99,14 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-template <int G>
+template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
     // V of the current and the next item, each wave's 32 slots in its own
     // 8 KiB; after a wave's PV it holds that wave's O partial [G][PS] fp32.
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[VBUF], vb1[VBUF];
     __shared__ float ml[2][4][16][2];  // (max, sum) per buffer, wave, head
     __shared__ float sk[MAX_HQ];       // sinks in log2 units
+    __shared__ float qcs[QROPE ? 4 : 1][64];  // per wave: cos, sin of the item's 32 angles
     constexpr int PS = G * (DV + 4) * 4 <= KEYS * DV * 2 ? DV + 4 : DV;  // partial row stride (floats)
 
     const int lane = threadIdx.x & 63;
@@ -107,6 +115,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
     const int n_items = a.n_seqs * a.hkv;
 
     for (int i = threadIdx.x; i < a.hq; i += kThreads) sk[i] = a.sinks ? a.sinks[i] * kLog2e : -INFINITY;
+    // frequency (lane mod 32) of the rotary pairs
+    const double invf = QROPE ? a.inv_freq[lane & 31] : 0.0;
 
     // Per-lane constant parts of the load addresses.  K: A operand of the
     // S^T MFMA, lane (quad, col) takes slot 32w + 16h + col, dims 32st + 8quad.
@@ -146,10 +156,55 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
         const int pc = P < W - 1 ? (int)P : W - 1;  // slot positions >= 0 iff (P - slot) mod W <= pc
 
         f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        if constexpr (QROPE) {
+            // The item's 32 (cos, sin) pairs through the wave's LDS row, then
+            // lane (quad, col) rotates dims 8 quad .. +7 (step 0) against
+            // their partners 32 + 8 quad .. (step 1) in fp32 and splits the
+            // results into bf16 hi + lo.
+            float cv, sv;
+            rope_cos_sin(P, invf, cv, sv);
+            if (lane < 32) {
+                qcs[w][lane] = cv;
+                qcs[w][32 + lane] = sv;
+            }
+            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&qcs[w][8 * quad]);
+            const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&qcs[w][8 * quad + 4]);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&qcs[w][32 + 8 * quad]);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(&qcs[w][32 + 8 * quad + 4]);
+            const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            float yl[8], yh[8];
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st)
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wl = qb[0][e >> 1], wh = qb[1][e >> 1];
+                const float xl = __uint_as_float((e & 1) ? (wl & 0xffff0000u) : (wl << 16));
+                const float xh = __uint_as_float((e & 1) ? (wh & 0xffff0000u) : (wh << 16));
+                rope_rotate(xl, xh, cc[e], ss[e], yl[e], yh[e]);
+            }
+            u32x2 lh0, ll0, lh1, ll1, hh0, hl0, hh1, hl1;
+            split_hi_lo(yl, lh0, ll0);
+            split_hi_lo(yl + 4, lh1, ll1);
+            split_hi_lo(yh, hh0, hl0);
+            split_hi_lo(yh + 4, hh1, hl1);
+            const u32x4 q0h = u32x4{lh0[0], lh0[1], lh1[0], lh1[1]}, q0l = u32x4{ll0[0], ll0[1], ll1[0], ll1[1]};
+            const u32x4 q1h = u32x4{hh0[0], hh0[1], hh1[0], hh1[1]}, q1l = u32x4{hl0[0], hl0[1], hl1[0], hl1[1]};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) sacc[h] = mfma_16x16x32_bf16(ka[h][st], qb[st], sacc[h]);
+            for (int h = 0; h < 2; ++h) {
+                sacc[h] = mfma_16x16x32_bf16(ka[h][0], q0h, sacc[h]);
+                sacc[h] = mfma_16x16x32_bf16(ka[h][0], q0l, sacc[h]);
+                sacc[h] = mfma_16x16x32_bf16(ka[h][1], q1h, sacc[h]);
+                sacc[h] = mfma_16x16x32_bf16(ka[h][1], q1l, sacc[h]);
+            }
+#pragma unroll
+            for (int st = 2; st < STEPS; ++st)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) sacc[h] = mfma_16x16x32_bf16(ka[h][st], qb[st], sacc[h]);
+        } else {
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) sacc[h] = mfma_16x16x32_bf16(ka[h][st], qb[st], sacc[h]);
+        }
 
         float sv[8], mx = -INFINITY;
 #pragma unroll
@@ -224,8 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
                 o += f * *reinterpret_cast<const f32x4 *>(pbase + ww * (KEYS * DV / 2) + hd * PS + d4);
             }
             const float r = a.value_scale / L;
-            const u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * r) | ((uint32_t)f2bf(o[1] * r) << 16),
-                                   (uint32_t)f2bf(o[2] * r) | ((uint32_t)f2bf(o[3] * r) << 16)};
+            const u32x2 pk = u32x2{pack_bf16x2(o[0] * r, o[1] * r), pack_bf16x2(o[2] * r, o[3] * r)};
             *reinterpret_cast<u32x2 *>(out + hd * DV + d4) = pk;
         }
         // Every wave is done with this buffer before the loads of the item
@@ -295,12 +349,22 @@ hipError_t launch_swa_decode(const AttnArgs &a, hipStream_t s) {
     const int64_t items = (int64_t)a.n_seqs * a.hkv;
     const int64_t nb = items < 2 * cu_count() ? items : 2 * cu_count();
     dim3 grid((unsigned)nb), block(kThreads);
+    if (a.qrope) {
+        switch (a.hq / a.hkv) {
+            case 1: hipLaunchKernelGGL((swa_decode_kernel<1, true>), grid, block, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((swa_decode_kernel<2, true>), grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((swa_decode_kernel<4, true>), grid, block, 0, s, a); break;
+            case 8: hipLaunchKernelGGL((swa_decode_kernel<8, true>), grid, block, 0, s, a); break;
+            default: hipLaunchKernelGGL((swa_decode_kernel<16, true>), grid, block, 0, s, a); break;
+        }
+        return hipGetLastError();
+    }
     switch (a.hq / a.hkv) {
-        case 1: hipLaunchKernelGGL(swa_decode_kernel<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(swa_decode_kernel<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(swa_decode_kernel<4>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(swa_decode_kernel<8>, grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(swa_decode_kernel<16>, grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((swa_decode_kernel<1, false>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((swa_decode_kernel<2, false>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((swa_decode_kernel<4, false>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((swa_decode_kernel<8, false>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((swa_decode_kernel<16, false>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -30,6 +30,15 @@
 // run in lane order, free of bank conflicts.  Block ids are remapped so consecutive query
 // blocks of one (sequence, KV head) run on one XCD and re-read their
 // overlapping bands from its L2.
+//
+// With QROPE the kernel reads unrotated q and applies the rotate-half RoPE
+// itself (colibri "What the engine implements"; the angle in double as the
+// gaudi-cookbook "The RoPE fix for large positions" requires), with the same
+// helpers and rounding as the RoPE kernel, so the rotated q -- and therefore
+// the output -- is bit-identical to RoPE followed by the plain kernel, without
+// q_rot's write and re-read.  Each wave puts the cos/sin of its rows'
+// positions into its own part of the third pipeline stage, which no load
+// reaches before the first step's barrier.
 #include "hsw_device.h"
 #include "hsw_launch.h"
 
@@ -73,6 +82,14 @@ __device__ __forceinline__ void load_lds16_s(const void *sbase, uint32_t voff, c
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
+// 16-byte global load into v, untracked like the loads above: were the
+// compiler to track q, its waits for it (merged over the chunk loop) would be
+// vmcnt(0) inside every step and drain the chunk pipeline.  The first wait of
+// the pipeline covers q, as q is issued first; v keeps its register.
+__device__ __forceinline__ void load_q16(u32x4 &v, const void *src) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(v) : "v"(src) : "memory");
+}
+
 // Max / sum over the four quads (lanes c, c+16, c+32, c+48) with the gfx950
 // half-wave and row swaps (VALU, no LDS round trip).
 __device__ __forceinline__ float quad_max_swap(float v) {
@@ -112,7 +129,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 //    4q .. 4q+3 (16 lanes) / 8 rows (32 lanes) at two logical pieces; the xor
 //    gives each row its own pair of pieces.
 
-template <int G>
+template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, int nqb) {
     constexpr int BQ = 128 / G;
     // Three stages, each its own LDS object so the compiler can tell that a
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     const int p0 = start + qb * BQ;                 // first query position
     const int plast = start + min(len, qb * BQ + BQ) - 1;
     const int kstart = max(0, p0 - (W - 1));        // band: kstart .. plast
-    const int nch = (plast - kstart + KC) / KC;
+    const int nch = max((plast - kstart + KC) / KC, 1);  // >= 1 (stated so the compiler knows the loop runs)
 
     // q of this wave's rows (row r = 32w + 16n + col -> position r / G, head
     // r % G), from a clamped row so the load is unconditional; rows past the
@@ -156,7 +173,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+            qv[n][st] = u32x4{0, 0, 0, 0};
+            load_q16(qv[n][st], qrow + 32 * st + 8 * quad);
         }
     }
 
@@ -415,6 +433,46 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
 
     issue(0, ks0, vs0);
     if (nch > 1) issue(1, ks1, vs1);
+    if constexpr (QROPE) {
+        // The wave's 32 rows cover NP positions; table entry e = 32 i + f is
+        // frequency f at position pw + i (cos in ks2, sin in vs2; the first
+        // loads into either are issued after the first step's barrier, which
+        // each wave reaches only after its reads below have completed).
+        constexpr int NP = 32 / G;
+        static_assert(4 * NP * 32 <= KC * DQK / 2 && 4 * NP * 32 <= KC * DV / 2, "cos/sin table too large");
+        float *tc = reinterpret_cast<float *>(ks2) + w * (NP * 32);
+        float *ts = reinterpret_cast<float *>(vs2) + w * (NP * 32);
+        const double invf = a.inv_freq[lane & 31];
+        const int pw = p0 + (32 * w) / G;
+#pragma unroll
+        for (int e = lane; e < NP * 32; e += 64) {
+            float cv, sv;
+            rope_cos_sin((int64_t)(pw + e / 32), invf, cv, sv);
+            tc[e] = cv;
+            ts[e] = sv;
+        }
+        // q has landed once at most the chunk loads issued after it are
+        // outstanding (loads complete in order); the table above was built
+        // while they were in flight.
+        if (nch > 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        __asm__ volatile("" ::: "memory");
+        // Lane (quad, col) holds dims 8 quad .. +7 (step 0) and their
+        // partners 32 + 8 quad .. (step 1) of row 32w + 16n + col.
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int pi = (16 * n + col) / G;
+            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad);
+            const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad + 4);
+            const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            rope_rotate_bf16x8(qv[n][0], qv[n][1], cc, ss);
+        }
+    }
     for (int c = 0; c < nch; c += 3) {
         step(c, ks0, vs0, ks2, vs2, vflag[0]);
         if (c + 1 < nch) step(c + 1, ks1, vs1, ks0, vs0, vflag[1]);
@@ -446,8 +504,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const f32x4 o = oacc[n][dt];
-            const u32x2 pk = u32x2{(uint32_t)f2bf(o[0] * rs) | ((uint32_t)f2bf(o[1] * rs) << 16),
-                                   (uint32_t)f2bf(o[2] * rs) | ((uint32_t)f2bf(o[3] * rs) << 16)};
+            const u32x2 pk = u32x2{pack_bf16x2(o[0] * rs, o[1] * rs), pack_bf16x2(o[2] * rs, o[3] * rs)};
             const int unit = (2 * dt + (quad >> 1)) ^ (row & 15);
             *reinterpret_cast<u32x2 *>(ep + row * DV + unit * 8 + 4 * (quad & 1)) = pk;
         }
@@ -472,18 +529,36 @@ bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
            (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
+// Shapes the kernels that rotate q themselves take: the bf16 fast shapes with
+// a 64-dim rotary part, and (prefill, for the per-wave cos/sin table) at least
+// two query heads per KV head.
+bool swa_qrope_ok(const AttnArgs &a, int dtype, int out_dtype, bool prefill) {
+    const int G = a.hq / a.hkv;
+    const bool fast = prefill ? swa_prefill_fast_ok(a, dtype, out_dtype) : swa_decode_fast_ok(a, dtype, out_dtype);
+    return fast && a.rope_dim == 64 && (!prefill || G >= 2);
+}
+
 hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int BQ = 128 / G;
     const int64_t nqb = (a.max_seqlen + BQ - 1) / BQ;
     dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(kThreads);
     const int nq = (int)nqb;
+    if (a.qrope) {
+        switch (G) {
+            case 2: hipLaunchKernelGGL((swa_prefill_kernel<2, true>), grid, block, 0, s, a, nq); break;
+            case 4: hipLaunchKernelGGL((swa_prefill_kernel<4, true>), grid, block, 0, s, a, nq); break;
+            case 8: hipLaunchKernelGGL((swa_prefill_kernel<8, true>), grid, block, 0, s, a, nq); break;
+            default: hipLaunchKernelGGL((swa_prefill_kernel<16, true>), grid, block, 0, s, a, nq); break;
+        }
+        return hipGetLastError();
+    }
     switch (G) {
-        case 1: hipLaunchKernelGGL(swa_prefill_kernel<1>, grid, block, 0, s, a, nq); break;
-        case 2: hipLaunchKernelGGL(swa_prefill_kernel<2>, grid, block, 0, s, a, nq); break;
-        case 4: hipLaunchKernelGGL(swa_prefill_kernel<4>, grid, block, 0, s, a, nq); break;
-        case 8: hipLaunchKernelGGL(swa_prefill_kernel<8>, grid, block, 0, s, a, nq); break;
-        default: hipLaunchKernelGGL(swa_prefill_kernel<16>, grid, block, 0, s, a, nq); break;
+        case 1: hipLaunchKernelGGL((swa_prefill_kernel<1, false>), grid, block, 0, s, a, nq); break;
+        case 2: hipLaunchKernelGGL((swa_prefill_kernel<2, false>), grid, block, 0, s, a, nq); break;
+        case 4: hipLaunchKernelGGL((swa_prefill_kernel<4, false>), grid, block, 0, s, a, nq); break;
+        case 8: hipLaunchKernelGGL((swa_prefill_kernel<8, false>), grid, block, 0, s, a, nq); break;
+        default: hipLaunchKernelGGL((swa_prefill_kernel<16, false>), grid, block, 0, s, a, nq); break;
     }
     return hipGetLastError();
 }

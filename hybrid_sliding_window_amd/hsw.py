@@ -58,14 +58,16 @@ def _load() -> ctypes.CDLL:
     lib.hsw_rope_partial_kv_write.argtypes = [SH, I64, P, P, P, P, P, I32, P, P, I64, P, P, P, P]
     lib.hsw_swa_prefill.argtypes = [SH, I32, I64, P, P, P, P, P, P, P, P, P, P]
     lib.hsw_swa_decode.argtypes = [SH, I32, P, P, P, P, P, P, P]
+    lib.hsw_swa_prefill_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, P, P, P, P, P]
+    lib.hsw_swa_decode_qrope.argtypes = [SH, I32, P, P, P, P, P, P, P]
     lib.hsw_full_decode_workspace_bytes.argtypes = [SH, I32, I64, I32]
     lib.hsw_full_decode_workspace_bytes.restype = SZ
     lib.hsw_full_decode_splitk.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, SZ, P, P]
     lib.hsw_full_prefill_chunk.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
     lib.hsw_kv_bytes.argtypes = [I32, I64, I64, I32, I32, I32, I32, I32, I32]
     lib.hsw_kv_bytes.restype = I64
-    for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode",
-              "hsw_full_decode_splitk", "hsw_full_prefill_chunk"):
+    for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope",
+              "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_prefill_chunk"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -73,7 +75,8 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_rope_partial_kv_write",
-            "hsw_swa_prefill", "hsw_swa_decode", "hsw_full_decode_workspace_bytes",
+            "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope", "hsw_swa_decode_qrope",
+            "hsw_full_decode_workspace_bytes",
             "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_kv_bytes")
 
 
@@ -123,6 +126,20 @@ def hsw_swa_decode(shape, n_seqs, pos, q_rot, k_ring, v_ring, sinks, out, stream
     _check(lib.hsw_swa_decode(_sh(shape), int(n_seqs), _ptr(pos), _ptr(q_rot), _ptr(k_ring),
                               _ptr(v_ring), _ptr(sinks), _ptr(out), _stream(stream)),
            "hsw_swa_decode")
+
+
+def hsw_swa_prefill_qrope(shape, n_seqs, max_seqlen, cu_seqlens, start_pos, q, k_stage, v_stage,
+                          k_ring, v_ring, sinks, out, stream=None):
+    _check(lib.hsw_swa_prefill_qrope(_sh(shape), int(n_seqs), int(max_seqlen), _ptr(cu_seqlens),
+                                     _ptr(start_pos), _ptr(q), _ptr(k_stage), _ptr(v_stage),
+                                     _ptr(k_ring), _ptr(v_ring), _ptr(sinks), _ptr(out), _stream(stream)),
+           "hsw_swa_prefill_qrope")
+
+
+def hsw_swa_decode_qrope(shape, n_seqs, pos, q, k_ring, v_ring, sinks, out, stream=None):
+    _check(lib.hsw_swa_decode_qrope(_sh(shape), int(n_seqs), _ptr(pos), _ptr(q), _ptr(k_ring),
+                                    _ptr(v_ring), _ptr(sinks), _ptr(out), _stream(stream)),
+           "hsw_swa_decode_qrope")
 
 
 def hsw_full_decode_workspace_bytes(shape, n_seqs, max_ctx, chunk) -> int:

@@ -119,7 +119,9 @@ const char *hsw_version(void);
  *   dst_kind: HSW_DST_RING / POOL / STAGING (see the enum for layouts; V is
  *      the same with d_v).  dst_capacity: sequences in the ring, rows in the
  *      pool, or rows in staging.  seq_base [n_seqs] int64: POOL only.
- *   q_rot [n_tokens][Hq][d_qk] in dtype (written).
+ *   q_rot [n_tokens][Hq][d_qk] in dtype (written).  q and q_rot may both be
+ *      NULL: then only K/V are rotated and written (for the *_qrope calls,
+ *      which rotate q themselves); one of them NULL alone is HSW_E_NULL.
  *   dst_index_out [n_tokens] int64 or NULL: the slot / row written for each
  *      token, or -1 when its destination was outside dst_capacity.
  */
@@ -171,6 +173,41 @@ hsw_status hsw_swa_prefill(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max
 hsw_status hsw_swa_decode(const hsw_attn_shape *sh, int32_t n_seqs, const int64_t *pos,
                           const void *q_rot, const void *k_ring, const void *v_ring,
                           const float *sinks, void *out, hsw_stream_t stream);
+
+/*
+ * hsw_swa_prefill with the q-RoPE fused in: q is the unrotated query
+ * [T][Hq][d_qk] (the K/V staging rows must already be rotated, e.g. by
+ * hsw_rope_partial_kv_write with q = q_rot = NULL), and the kernel rotates q
+ * as it loads it (colibri "What the engine implements": rotate-half on the
+ * first rope_dim dims; gaudi-cookbook "The RoPE fix for large positions":
+ * the angle is formed and reduced in double) at positions start_pos[s] + t.
+ * The rotation and its bf16 rounding are those of hsw_rope_partial_kv_write,
+ * so out is bit-identical to that call followed by hsw_swa_prefill; no q_rot
+ * is written or read.  Every other argument, the ring commit and the error
+ * behaviour are those of hsw_swa_prefill.  Supported shapes: bf16 in and
+ * out, d_qk 192, d_v 128, rope_dim 64, window 128, 2/4/8/16 query heads per
+ * KV head; others give HSW_E_SHAPE.
+ */
+hsw_status hsw_swa_prefill_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                                 const int64_t *cu_seqlens, const int64_t *start_pos, const void *q,
+                                 const void *k_stage, const void *v_stage, void *k_ring, void *v_ring,
+                                 const float *sinks, void *out, hsw_stream_t stream);
+
+/*
+ * hsw_swa_decode with the q-RoPE fused in: q [n_seqs][Hq][d_qk] is
+ * unrotated and is rotated at pos[s] in the kernel (same sources as
+ * hsw_swa_prefill_qrope).  The rotated rotary dims are kept in fp32 (split
+ * into bf16 hi + lo for the products), so the result is at least as accurate
+ * as RoPE to a bf16 q_rot followed by hsw_swa_decode, without q_rot's bytes.
+ * The ring must already hold the new token's K/V (hsw_rope_partial_kv_write
+ * with q = q_rot = NULL).  Supported shapes: bf16 in and out, d_qk 192, d_v
+ * 128, rope_dim 64, window 128, n_q_heads <= 256, 1/2/4/8/16 query heads per
+ * KV head; others give HSW_E_SHAPE.  Other arguments and errors as
+ * hsw_swa_decode.
+ */
+hsw_status hsw_swa_decode_qrope(const hsw_attn_shape *sh, int32_t n_seqs, const int64_t *pos,
+                                const void *q, const void *k_ring, const void *v_ring,
+                                const float *sinks, void *out, hsw_stream_t stream);
 
 /*
  * Full-attention decode, split over key chunks with a log-sum-exp combine.

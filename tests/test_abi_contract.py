@@ -110,6 +110,36 @@ def test_attention_argument_errors():
     hsw.hsw_full_prefill_chunk(fs, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE)
 
 
+def test_fused_qrope_argument_errors():
+    """The calls that rotate q themselves: shapes outside their kernels and
+    missing pointers are rejected on the host; K/V-only RoPE takes q and
+    q_rot both NULL, not one of them."""
+    sh, fs = swa(), full()
+    pre = (1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    hsw.hsw_swa_prefill_qrope(sh, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)  # empty
+    expect(2, hsw.hsw_swa_prefill_qrope, fs, *pre)
+    expect(1, hsw.hsw_swa_prefill_qrope, sh, 1, 8, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(3, hsw.hsw_swa_prefill_qrope, sh, 1, 8, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    mha = hsw.make_shape(wl.swa_shape(8, 8))          # one q head per KV head: no prefill table
+    expect(2, hsw.hsw_swa_prefill_qrope, mha, *pre)
+    r32 = swa()
+    r32.rope_dim = 32
+    expect(2, hsw.hsw_swa_prefill_qrope, r32, *pre)
+    expect(2, hsw.hsw_swa_decode_qrope, r32, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    f32 = hsw.make_shape(wl.swa_shape(dtype=__import__("torch").float32))
+    expect(2, hsw.hsw_swa_prefill_qrope, f32, *pre)
+    expect(2, hsw.hsw_swa_decode_qrope, f32, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(1, hsw.hsw_swa_decode_qrope, sh, 2, FAKE, None, FAKE, FAKE, None, FAKE)
+    expect(2, hsw.hsw_swa_decode_qrope, fs, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    hsw.hsw_swa_decode_qrope(sh, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    hsw.hsw_swa_decode_qrope(mha, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE)   # G = 1 decode is supported
+    args = dict(n_tokens=0, q=None, k=FAKE, v=FAKE, pos=FAKE, seq=FAKE, dst_kind=hsw.HSW_DST_RING,
+                k_dst=FAKE, v_dst=FAKE, dst_capacity=4, seq_base=None, q_rot=None)
+    hsw.hsw_rope_partial_kv_write(sh, **args)                              # K/V only, empty
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "q_rot": FAKE})
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "q": FAKE})
+
+
 def test_workspace_size_formula():
     fs = full()
     for S, L, C in [(64, 131072, 2048), (3, 1, 2048), (1, 4097, 1024)]:

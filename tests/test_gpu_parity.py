@@ -623,3 +623,124 @@ def test_zero_sizes_launch_nothing():
     for name, t in [("q_rot", q_rot), ("out", out), ("ring_k", ring_k), ("ring_v", ring_v),
                     ("pool_k", pool_k), ("pool_v", pool_v), ("ws", ws)]:
         assert bool((t == SENTINEL).all()), f"{name} was written by a zero-size call"
+
+
+# ------------------------------------------------------- fused q-RoPE
+def test_rope_cos_sin_fp32_against_fp64():
+    """The angle code itself: an fp32 RoPE call on unit vectors (x_lo = 1,
+    x_hi = 0) returns exactly the fp32 cos and sin it formed, for every
+    frequency at positions up to 2^24 + 5; each within 3e-7 of the fp64
+    rotation (angle formed and reduced in double, gaudi-cookbook 'The RoPE fix
+    for large positions')."""
+    note("rope cos/sin fp32 vs fp64")
+    positions = [0, 1, 2, 3, 100, 127, 128, 4095, 65536, 131071, 196608, 200000, 205000, 262143,
+                 524287, 524288, 1_000_003, 2 ** 24 + 5]
+    T = len(positions)
+    for theta in (wl.THETA_SWA, wl.THETA_FULL):
+        shape = wl.Shape(1, 1, 0, theta, dtype=torch.float32)
+        q = torch.zeros((T, 1, 192), dtype=torch.float32)
+        q[:, :, :32] = 1.0
+        k = torch.zeros((T, 1, 192), dtype=torch.float32)
+        v = torch.zeros((T, 1, 128), dtype=torch.float32)
+        pos = torch.tensor(positions, dtype=torch.int64)
+        q_rot = torch.empty((T, 1, 192), dtype=torch.float32, device=DEV)
+        kd = torch.empty((T, 1, 192), dtype=torch.float32, device=DEV)
+        vd = torch.empty((T, 1, 128), dtype=torch.float32, device=DEV)
+        hsw.hsw_rope_partial_kv_write(shape, T, dev(q), dev(k), dev(v), dev(pos), None, STAGING, kd, vd, T,
+                                      None, q_rot)
+        torch.cuda.synchronize()
+        ref = oracle.rope(f64(q), pos.numpy(), theta)
+        got = f64(q_rot)
+        err = np.abs(got[..., :64] - ref[..., :64])
+        assert err.max() <= 3e-7, f"theta={theta}: cos/sin off by {err.max():.2e} (worst position " \
+                                  f"{positions[int(np.unravel_index(err.argmax(), err.shape)[0])]})"
+        print(f"rope cos/sin theta={theta:.0e}: max |err| {err.max():.2e}, mean {err.mean():.2e}")
+
+
+def run_swa_prefill_qrope(batch):
+    """K/V-only RoPE into staging, then the prefill that rotates q itself."""
+    shape = batch["shape"]
+    T = batch["q"].shape[0]
+    S = batch["start_pos"].shape[0]
+    lens = (batch["cu_seqlens"][1:] - batch["cu_seqlens"][:-1])
+    kst = torch.empty_like(dev(batch["k"]))
+    vst = torch.empty_like(dev(batch["v"]))
+    hsw.hsw_rope_partial_kv_write(shape, T, None, dev(batch["k"]), dev(batch["v"]), dev(batch["pos"]), None,
+                                  STAGING, kst, vst, T, None, None)
+    kring, vring = dev(batch["kring"]), dev(batch["vring"])
+    out = torch.full((T, shape.n_q_heads, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_swa_prefill_qrope(shape, S, int(lens.max()) + 3, dev(batch["cu_seqlens"]), dev(batch["start_pos"]),
+                              dev(batch["q"]), kst, vst, kring, vring, dev(batch["sinks"]), out)
+    torch.cuda.synchronize()
+    return kst, vst, kring, vring, out
+
+
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_swa_prefill_qrope_bitwise_equals_rope_then_prefill(model):
+    """The fused call rotates q with the RoPE call's own arithmetic, so its
+    output, staging rows and ring commit are byte-identical to RoPE then
+    hsw_swa_prefill (which the other prefill tests hold to the oracle); the
+    error of the chain from the raw inputs (rotation in fp64, colibri 'What
+    the engine implements') is reported."""
+    note(f"swa_prefill_qrope bitwise {model}")
+    batch = wl.swa_prefill_batch(seed=81, n_seqs=4, seqlens=(300, 17, 1000, 129),
+                                 start_pos=(0, 5000, 130, 524000), **wl.model_kw(wl.MODELS[model], "swa"))
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    kst2, vst2, kring2, vring2, out2 = run_swa_prefill_qrope(batch)
+    assert torch.equal(kst2.cpu(), kst.cpu()) and torch.equal(vst2.cpu(), vst.cpu())
+    assert torch.equal(kring2.cpu(), kring.cpu()) and torch.equal(vring2.cpu(), vring.cpu())
+    assert torch.equal(out2.cpu(), out.cpu()), "fused prefill differs from RoPE + prefill"
+    # chain from the raw inputs: q and k rotated in fp64
+    shape = batch["shape"]
+    P = batch["pos"].numpy()
+    qr = oracle.rope(f64(batch["q"]), P, shape.rope_theta)
+    kr = oracle.rope(f64(batch["k"]), P, shape.rope_theta)
+    cu, st = batch["cu_seqlens"].tolist(), batch["start_pos"].tolist()
+    refs = []
+    for s in range(len(st)):
+        k, v, kpos0 = linear_kv_from_ring(f64(kb[s]), f64(vb[s]), st[s], kr[cu[s]:cu[s + 1]],
+                                          f64(batch["v"][cu[s]:cu[s + 1]]))
+        refs.append(oracle.attn_linear(qr[cu[s]:cu[s + 1]], P[cu[s]:cu[s + 1]], k, v, kpos0, window=128,
+                                       sinks=f64(batch["sinks"]), **shape_kw(shape)))
+    # reported, not gated: it adds the bf16 storage of the rotated q and k,
+    # which the bitwise match above already ties to the gated unfused path
+    ma, mr = errors(f64(out2), np.concatenate(refs))
+    print(f"swa_prefill_qrope {model}: bitwise equal to RoPE + prefill; chain max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_swa_decode_qrope_against_raw_chain(model):
+    """K/V-only RoPE into the rings, then the decode that rotates q itself in
+    fp32: against the oracle fed the raw q rotated in fp64 and the exact ring
+    bytes, at the bar, and no less accurate than RoPE to a bf16 q_rot followed
+    by hsw_swa_decode on the same rings."""
+    note(f"swa_decode_qrope {model}")
+    positions = [0, 1, 2, 5, 63, 126, 127, 128, 129, 255, 1000, 196608, 205000, 524287, 524288]
+    small = wl.swa_decode_batch(seed=82, n_seqs=len(positions), positions=positions,
+                                **wl.model_kw(wl.MODELS[model], "swa"))
+    big = wl.swa_decode_batch(seed=83, **wl.model_kw(wl.MODELS[model], "swa"))
+    for name, batch in (("small positions", small), ("256 sequences", big)):
+        shape = batch["shape"]
+        S = batch["pos"].shape[0]
+        kring, vring = dev(batch["kring"]), dev(batch["vring"])
+        hsw.hsw_rope_partial_kv_write(shape, S, None, dev(batch["k"]), dev(batch["v"]), dev(batch["pos"]),
+                                      dev(batch["seq"]), RING, kring, vring, S, None, None)
+        out = torch.full((S, shape.n_q_heads, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
+        hsw.hsw_swa_decode_qrope(shape, S, dev(batch["pos"]), dev(batch["q"]), kring, vring,
+                                 dev(batch["sinks"]), out)
+        # the unfused path on the same rings (RoPE of q only through a scratch K/V destination)
+        q_rot = torch.empty_like(dev(batch["q"]))
+        kd, vd = torch.empty_like(dev(batch["k"])), torch.empty_like(dev(batch["v"]))
+        hsw.hsw_rope_partial_kv_write(shape, S, dev(batch["q"]), dev(batch["k"]), dev(batch["v"]),
+                                      dev(batch["pos"]), None, STAGING, kd, vd, S, None, q_rot)
+        out_u = torch.empty_like(out)
+        hsw.hsw_swa_decode(shape, S, dev(batch["pos"]), q_rot, kring, vring, dev(batch["sinks"]), out_u)
+        torch.cuda.synchronize()
+        P = batch["pos"].numpy()
+        ref = oracle.ring_decode(oracle.rope(f64(batch["q"]), P, shape.rope_theta), P, f64(kring), f64(vring),
+                                 sinks=f64(batch["sinks"]), **shape_kw(shape))
+        ma, mr = assert_close(f64(out), ref, what=f"swa_decode_qrope {model} {name}")
+        mau, mru = errors(f64(out_u), ref)
+        print(f"swa_decode_qrope {model} {name}: max_abs={ma:.2e} mean_rel={mr:.2e} "
+              f"(bf16 q_rot path: max_abs={mau:.2e} mean_rel={mru:.2e})")
+        assert mr <= mru * 1.02, "fp32 rotated q should not be less accurate than a bf16 q_rot"
