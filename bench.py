@@ -47,9 +47,9 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_
 # profiles/swa_decode_256seq_hbm_traffic.md hold the runs.  Reported as null
 # once those sources differ from the ones measured.
 MEASURED_TRAFFIC = {
-    # band kernel 1510.2 MB + ring commit 2.7 MB read / 2.6 MB written
-    "swa_prefill": (1515.5e6, ("swa_prefill.hip", "generic_attn.hip"), "0d5a6933c06a5bb7"),
-    "swa_decode": (178.47e6, ("swa_decode.hip",), "f65d449858588a56"),
+    # band kernel 1510.3 MB + ring commit 2.7 MB read / 2.6 MB written
+    "swa_prefill": (1515.6e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "628bb097d248014f"),
+    "swa_decode": (178.45e6, ("swa_decode.hip", "hsw_device.h"), "cdb01983eb797dc6"),
 }
 
 
