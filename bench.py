@@ -298,6 +298,40 @@ def bench_full_prefill(hsw, wl, steps, stream, model=None):
                 workload=f"full-attention prefill, 8192 tokens after 131072 prior rows, {hq} q / {hkv} KV heads")
 
 
+def bench_kvm_snapshot(hsw, wl, steps, stream, model=None):
+    """Ring snapshot and restore of one sequence (hsw_kvm_snapshot /
+    hsw_kvm_restore): every windowed layer's ring block (model's windowed
+    layers, 128 slots, K and V) copied out to a snapshot slot and back, on
+    rings of 129 sequences per layer."""
+    model = model or wl.FLASH
+    n_swa = model.n_layers - model.n_full
+    hkv = model.swa_kv_heads
+    S = 129
+    k = [torch.empty((S, hkv, 128, 192), dtype=torch.bfloat16, device=DEV) for _ in range(n_swa)]
+    v = [torch.empty((S, hkv, 128, 128), dtype=torch.bfloat16, device=DEV) for _ in range(n_swa)]
+    cfg = hsw.KvmConfig(n_swa, hkv, 128, 192, 128, 2, S, 1 << 20, 2)
+    sb = hsw.hsw_kvm_snapshot_bytes(cfg)
+    snap_buf = torch.empty((2 * sb // 2,), dtype=torch.bfloat16, device=DEV)
+    kv = hsw.KvManager(cfg, k, v, snap_buf)
+    seq, _ = kv.admit(1024)
+    kv.append(seq, [1, 2, 3])
+    sid = kv.snapshot(seq, stream)
+    warm(lambda i: kv.restore(sid, stream), stream)
+    n = max(steps, 20)
+    t_restore = ev_time(lambda i: kv.restore(sid, stream), n, stream)
+    t_snap = ev_time(lambda i: _snap_cycle(kv, seq, stream), n, stream)
+    kv.close()
+    del k, v, snap_buf
+    return dict(ms=t_snap, restore_ms=t_restore, bytes=2 * sb, gbs=2 * sb / t_snap / 1e6,
+                restore_gbs=2 * sb / t_restore / 1e6, snapshot_bytes=sb,
+                workload=f"ring snapshot of one sequence, {n_swa} windowed layers x {hkv} KV heads x 128 slots x "
+                         f"(192 + 128) bf16 ({sb / 1e6:.1f} MB each way)")
+
+
+def _snap_cycle(kv, seq, stream):
+    kv.drop_snapshot(kv.snapshot(seq, stream))
+
+
 def bench_hybrid(hsw, wl, steps, stream, model=None):
     """One hybrid step (hybrid_sliding_window_amd.hybrid.HybridStep) over the
     model's attention-only layers (Flash: 39 windowed + 9 full, Pro: 60 + 10,
@@ -396,7 +430,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="only the two metric calls")
-    ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid", "copy"],
+    ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid", "copy",
+                                       "kvm_snapshot"],
                     help="run one call's timing only (for profiling) and print its numbers")
     ap.add_argument("--model", choices=["flash", "pro"], default="flash", help="shapes for --only")
     ap.add_argument("--no-pro", action="store_true", help="skip the MiMo-V2.6-Pro section")
@@ -417,7 +452,8 @@ def main():
               "full_decode": lambda: bench_full_decode(hsw, wl, args.steps, stream, m),
               "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream, m),
               "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m),
-              "copy": lambda: bench_copy(args.steps, stream)}[args.only]
+              "copy": lambda: bench_copy(args.steps, stream),
+              "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m)}[args.only]
         r = fn()
         print(json.dumps({"only": args.only, "model": m.name,
                           **{k: v for k, v in r.items() if not isinstance(v, dict)}}))
@@ -443,6 +479,11 @@ def main():
         calls["full_decode_splitk"] = fd
         calls["full_prefill_chunk"] = fp
         del fd, fp
+        torch.cuda.empty_cache()
+        snap = bench_kvm_snapshot(hsw, wl, args.steps, stream)
+        print(f"[bench] kvm snapshot {snap['ms'] * 1e3:.1f} us restore {snap['restore_ms'] * 1e3:.1f} us "
+              f"({snap['gbs']:.0f} / {snap['restore_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+        calls["kvm_snapshot"] = snap
         torch.cuda.empty_cache()
         hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream)
         print(f"[bench] hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}",

@@ -14,16 +14,25 @@
 #include "hsw_launch.h"
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
+namespace hsw {
+hsw_status vfail(hsw_status st, const char *fmt, va_list ap) {
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    return st;
+}
 hsw_status fail(hsw_status st, const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    vfail(st, fmt, ap);
     va_end(ap);
     return st;
 }
+}  // namespace hsw
+
+namespace {
+using hsw::fail;
 
 bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
@@ -102,6 +111,8 @@ const char *hsw_status_str(hsw_status s) {
         case HSW_E_DTYPE: return "HSW_E_DTYPE: unsupported dtype";
         case HSW_E_WORKSPACE: return "HSW_E_WORKSPACE: workspace too small";
         case HSW_E_LAUNCH: return "HSW_E_LAUNCH: kernel launch failed";
+        case HSW_E_CAPACITY: return "HSW_E_CAPACITY: a KV pool lacks room";
+        case HSW_E_STALE: return "HSW_E_STALE: the snapshot was released";
         default: return "unknown hsw_status";
     }
 }

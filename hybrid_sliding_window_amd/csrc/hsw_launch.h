@@ -47,6 +47,20 @@ struct AttnArgs {
     double inv_freq[32];       // theta^(-2i/rope_dim), i < min(rope_dim/2, 32)
 };
 
+// Record an error message for hsw_last_error() and return st (hsw_abi.hip).
+int32_t fail(int32_t st, const char *fmt, ...);
+
+// Ring snapshots: copy one sequence's ring block of every windowed layer into
+// a snapshot (to_snap) or back (kv_manager.hip).
+constexpr int kMaxRingLayers = 128;
+struct RingCopyArgs {
+    char *k[kMaxRingLayers], *v[kMaxRingLayers];  // ring buffers, already offset to the sequence
+    char *snap;                                    // the snapshot's first byte
+    int64_t kb, vb;                                // K / V block bytes per layer (multiples of 16)
+    int n_layers, to_snap;
+};
+hipError_t launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
+
 hipError_t launch_rope(const RopeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_generic_attn(const AttnArgs &a, int dtype, int out_dtype, hipStream_t s);
 hipError_t launch_ring_commit(const AttnArgs &a, int dtype, hipStream_t s);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libhsw.so")
 HSW_BF16, HSW_F32 = 0, 1
 HSW_DST_RING, HSW_DST_POOL, HSW_DST_STAGING = 0, 1, 2
 STATUS = {0: "HSW_OK", 1: "HSW_E_NULL", 2: "HSW_E_SHAPE", 3: "HSW_E_ALIGN", 4: "HSW_E_DTYPE",
-          5: "HSW_E_WORKSPACE", 6: "HSW_E_LAUNCH"}
+          5: "HSW_E_WORKSPACE", 6: "HSW_E_LAUNCH", 7: "HSW_E_CAPACITY", 8: "HSW_E_STALE"}
 
 
 class HswError(RuntimeError):
@@ -34,6 +34,13 @@ class AttnShape(ctypes.Structure):
                 ("window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("value_scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class KvmConfig(ctypes.Structure):
+    _fields_ = [("n_swa_layers", ctypes.c_int32), ("swa_kv_heads", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32), ("ring_seqs", ctypes.c_int32),
+                ("pool_rows", ctypes.c_int64), ("max_snapshots", ctypes.c_int32)]
 
 
 _DT = {torch.bfloat16: HSW_BF16, torch.float32: HSW_F32}
@@ -66,6 +73,28 @@ def _load() -> ctypes.CDLL:
     lib.hsw_full_prefill_chunk.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
     lib.hsw_kv_bytes.argtypes = [I32, I64, I64, I32, I32, I32, I32, I32, I32]
     lib.hsw_kv_bytes.restype = I64
+    KC = ctypes.POINTER(KvmConfig)
+    PI32, PI64, PP = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(P)
+    lib.hsw_kvm_snapshot_bytes.argtypes = [KC]
+    lib.hsw_kvm_snapshot_bytes.restype = SZ
+    lib.hsw_kvm_create.argtypes = [KC, PP, PP, P, SZ, PP]
+    lib.hsw_kvm_destroy.argtypes = [P]
+    lib.hsw_kvm_destroy.restype = None
+    lib.hsw_kvm_admit.argtypes = [P, I64, PI32, PI64]
+    lib.hsw_kvm_release.argtypes = [P, I32]
+    lib.hsw_kvm_append.argtypes = [P, I32, PI32, I64, PI64]
+    lib.hsw_kvm_truncate.argtypes = [P, I32, I64]
+    lib.hsw_kvm_info.argtypes = [P, I32, PI64, PI64, PI64]
+    lib.hsw_kvm_free_space.argtypes = [P, PI32, PI64, PI32]
+    lib.hsw_kvm_snapshot.argtypes = [P, I32, PI32, P]
+    lib.hsw_kvm_restore.argtypes = [P, I32, P]
+    lib.hsw_kvm_drop_snapshot.argtypes = [P, I32]
+    lib.hsw_kvm_window_safe_length.argtypes = [P, I32, PI32, I64, PI32]
+    lib.hsw_kvm_window_safe_length.restype = I64
+    for f in ("hsw_kvm_create", "hsw_kvm_admit", "hsw_kvm_release", "hsw_kvm_append", "hsw_kvm_truncate",
+              "hsw_kvm_info", "hsw_kvm_free_space", "hsw_kvm_snapshot", "hsw_kvm_restore",
+              "hsw_kvm_drop_snapshot"):
+        getattr(lib, f).restype = I32
     for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope",
               "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_prefill_chunk"):
         getattr(lib, f).restype = I32
@@ -77,7 +106,10 @@ lib = _load()
 EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_rope_partial_kv_write",
             "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope", "hsw_swa_decode_qrope",
             "hsw_full_decode_workspace_bytes",
-            "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_kv_bytes")
+            "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_kv_bytes",
+            "hsw_kvm_snapshot_bytes", "hsw_kvm_create", "hsw_kvm_destroy", "hsw_kvm_admit", "hsw_kvm_release",
+            "hsw_kvm_append", "hsw_kvm_truncate", "hsw_kvm_info", "hsw_kvm_free_space", "hsw_kvm_snapshot",
+            "hsw_kvm_restore", "hsw_kvm_drop_snapshot", "hsw_kvm_window_safe_length")
 
 
 def _ptr(t):
@@ -171,3 +203,89 @@ def hsw_kv_bytes(kind, n_seqs, ctx, window, n_kv_heads, d_qk, d_v_stored, elem_b
 
 def hsw_version() -> str:
     return lib.hsw_version().decode()
+
+
+def hsw_kvm_snapshot_bytes(cfg: KvmConfig) -> int:
+    return int(lib.hsw_kvm_snapshot_bytes(ctypes.byref(cfg)))
+
+
+def _ids(tokens):
+    arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+    return arr, len(tokens)
+
+
+class KvManager:
+    """The hsw_kvm_* calls on one handle (marshalling only).  swa_k / swa_v:
+    the per-layer ring tensors (device), snap_buf: a device tensor of at least
+    max_snapshots * hsw_kvm_snapshot_bytes(cfg) bytes (or None)."""
+
+    def __init__(self, cfg: KvmConfig, swa_k, swa_v, snap_buf=None):
+        n = cfg.n_swa_layers
+        self.cfg = cfg
+        self._keep = (list(swa_k), list(swa_v), snap_buf)   # the tensors outlive the handle
+        ks = (ctypes.c_void_p * n)(*[_ptr(t) for t in swa_k])
+        vs = (ctypes.c_void_p * n)(*[_ptr(t) for t in swa_v])
+        nbytes = 0 if snap_buf is None else snap_buf.numel() * snap_buf.element_size()
+        h = ctypes.c_void_p()
+        _check(lib.hsw_kvm_create(ctypes.byref(cfg), ks, vs, _ptr(snap_buf), nbytes, ctypes.byref(h)),
+               "hsw_kvm_create")
+        self.h = h
+
+    def close(self):
+        if self.h:
+            lib.hsw_kvm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, max_len):
+        seq, base = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib.hsw_kvm_admit(self.h, int(max_len), ctypes.byref(seq), ctypes.byref(base)), "hsw_kvm_admit")
+        return seq.value, base.value
+
+    def release(self, seq):
+        _check(lib.hsw_kvm_release(self.h, int(seq)), "hsw_kvm_release")
+
+    def append(self, seq, tokens):
+        arr, n = _ids(tokens)
+        start = ctypes.c_int64()
+        _check(lib.hsw_kvm_append(self.h, int(seq), arr, n, ctypes.byref(start)), "hsw_kvm_append")
+        return start.value
+
+    def truncate(self, seq, new_len):
+        _check(lib.hsw_kvm_truncate(self.h, int(seq), int(new_len)), "hsw_kvm_truncate")
+
+    def info(self, seq):
+        ln, base, mx = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.hsw_kvm_info(self.h, int(seq), ctypes.byref(ln), ctypes.byref(base), ctypes.byref(mx)),
+               "hsw_kvm_info")
+        return ln.value, base.value, mx.value
+
+    def free_space(self):
+        r, run, sn = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib.hsw_kvm_free_space(self.h, ctypes.byref(r), ctypes.byref(run), ctypes.byref(sn)),
+               "hsw_kvm_free_space")
+        return r.value, run.value, sn.value
+
+    def snapshot(self, seq, stream=None):
+        snap = ctypes.c_int32()
+        _check(lib.hsw_kvm_snapshot(self.h, int(seq), ctypes.byref(snap), _stream(stream)), "hsw_kvm_snapshot")
+        return snap.value
+
+    def restore(self, snap, stream=None):
+        _check(lib.hsw_kvm_restore(self.h, int(snap), _stream(stream)), "hsw_kvm_restore")
+
+    def drop_snapshot(self, snap):
+        _check(lib.hsw_kvm_drop_snapshot(self.h, int(snap)), "hsw_kvm_drop_snapshot")
+
+    def window_safe_length(self, seq, tokens):
+        arr, n = _ids(tokens)
+        snap = ctypes.c_int32()
+        L = int(lib.hsw_kvm_window_safe_length(self.h, int(seq), arr, n, ctypes.byref(snap)))
+        if L < 0:
+            raise HswError(2, "hsw_kvm_window_safe_length", lib.hsw_last_error().decode())
+        return L, snap.value

@@ -59,7 +59,9 @@ enum {
     HSW_E_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
     HSW_E_DTYPE = 4,     /* unsupported dtype combination */
     HSW_E_WORKSPACE = 5, /* workspace smaller than required */
-    HSW_E_LAUNCH = 6     /* the HIP runtime rejected a launch */
+    HSW_E_LAUNCH = 6,    /* the HIP runtime rejected a launch */
+    HSW_E_CAPACITY = 7,  /* a KV pool (ring slots, pool rows, snapshots) lacks room */
+    HSW_E_STALE = 8      /* a snapshot was released (its rows were rewritten) */
 };
 
 enum { HSW_BF16 = 0, HSW_F32 = 1 };
@@ -258,6 +260,101 @@ hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int6
 int64_t hsw_kv_bytes(int32_t kind, int64_t n_seqs, int64_t ctx, int32_t window,
                      int32_t n_kv_heads, int32_t d_qk, int32_t d_v_stored,
                      int32_t elem_bytes, int32_t n_layers);
+
+/*
+ * Dual-pool KV manager (host bookkeeping over caller-owned device pools).
+ *
+ * gokawiil "Full-Pipeline Inference Optimization for MiMo-V2.5 Series",
+ * section 2.1 "SWA KVCache Management": the full-attention layers and the
+ * windowed layers keep separate pools -- full layers O(N) rows per sequence,
+ * windowed layers O(W) (here the 128-slot ring of each sequence) -- and a
+ * request is admitted only if both pools have room; prefix reuse is clipped
+ * to a "window-safe length", where the windowed layers' last W positions are
+ * still held.  colibri "MiMo-V2.6 (Xiaomi)", section "System One mode and
+ * prompt reuse": a snapshot keeps the full layers' rows in place (nothing
+ * after it writes below its position; the token ids are recorded and checked
+ * before resuming, and a sequence that diverged below it releases it), copies
+ * every windowed layer's ring into the snapshot and back, and records its
+ * position.
+ *
+ * Layout the manager assumes (the same the attention calls use):
+ *   windowed layer l: K ring swa_k[l] [ring_seqs][swa_kv_heads][window][d_qk],
+ *                     V ring swa_v[l] [ring_seqs][swa_kv_heads][window][d_v];
+ *   full layers: pool rows [pool_rows][full_kv_heads][d], a sequence owning
+ *                rows seq_base .. seq_base + max_len - 1 (row = seq_base + pos);
+ *   snapshot k: bytes [k * S, (k+1) * S) of snap_buf, S =
+ *                hsw_kvm_snapshot_bytes(cfg), holding per windowed layer the
+ *                sequence's K ring block then its V ring block.
+ * The manager allocates no device memory; its host state is allocated by
+ * hsw_kvm_create and freed by hsw_kvm_destroy.  One handle must not be used
+ * from two host threads at once.  Snapshot and restore are stream-ordered
+ * copies on `stream`; bookkeeping calls only touch host state.
+ */
+typedef struct hsw_kvm hsw_kvm;
+
+typedef struct {
+    int32_t n_swa_layers;   /* windowed layers (1..128) */
+    int32_t swa_kv_heads;
+    int32_t window;         /* ring slots per sequence and layer */
+    int32_t d_qk, d_v;      /* head widths (multiples of 8) */
+    int32_t elem_bytes;     /* 2 (bf16) or 4 (fp32) */
+    int32_t ring_seqs;      /* sequences each ring buffer holds */
+    int64_t pool_rows;      /* rows each full-layer pool holds */
+    int32_t max_snapshots;  /* snapshots snap_buf holds */
+} hsw_kvm_config;
+
+/* Bytes of one snapshot: n_swa_layers * swa_kv_heads * window * (d_qk + d_v)
+ * * elem_bytes (colibri: "about 50 MB per snapshot on Flash" in fp32; 25.6 MB
+ * in bf16).  0 on bad input. */
+size_t hsw_kvm_snapshot_bytes(const hsw_kvm_config *cfg);
+
+/* swa_k, swa_v: host arrays of n_swa_layers device pointers (16-byte
+ * aligned); snap_buf: device, at least max_snapshots * snapshot bytes
+ * (HSW_E_WORKSPACE otherwise; may be NULL when max_snapshots is 0). */
+hsw_status hsw_kvm_create(const hsw_kvm_config *cfg, void *const *swa_k, void *const *swa_v,
+                          void *snap_buf, size_t snap_buf_bytes, hsw_kvm **out);
+void hsw_kvm_destroy(hsw_kvm *kvm);
+
+/* Admit a sequence that will hold at most max_len positions: takes a free ring
+ * slot and the first free run of max_len pool rows, or takes nothing and
+ * returns HSW_E_CAPACITY when either pool lacks room.  *seq (ring slot and
+ * sequence id) and *seq_base (first pool row) are written on success. */
+hsw_status hsw_kvm_admit(hsw_kvm *kvm, int64_t max_len, int32_t *seq, int64_t *seq_base);
+/* Return the sequence's ring slot and pool rows; its snapshots are released. */
+hsw_status hsw_kvm_release(hsw_kvm *kvm, int32_t seq);
+
+/* Record host token ids for positions len .. len+n-1 of the sequence (the
+ * caller then writes their K/V with hsw_rope_partial_kv_write and runs the
+ * attention at *start_pos = len).  HSW_E_CAPACITY past max_len.  A token that
+ * differs from the one its row held before releases the sequence's snapshots
+ * at positions above it. */
+hsw_status hsw_kvm_append(hsw_kvm *kvm, int32_t seq, const int32_t *tokens, int64_t n, int64_t *start_pos);
+/* Move the sequence's length back to new_len <= len (the rows beyond keep
+ * their contents and token ids until rewritten). */
+hsw_status hsw_kvm_truncate(hsw_kvm *kvm, int32_t seq, int64_t new_len);
+/* Length, first pool row and capacity of a sequence. */
+hsw_status hsw_kvm_info(hsw_kvm *kvm, int32_t seq, int64_t *len, int64_t *seq_base, int64_t *max_len);
+/* Free ring slots, largest free run of pool rows, free snapshot slots. */
+hsw_status hsw_kvm_free_space(hsw_kvm *kvm, int32_t *ring_slots, int64_t *pool_run, int32_t *snapshots);
+
+/* Copy the sequence's ring of every windowed layer into a free snapshot slot
+ * (one launch on `stream`) and record (sequence, position = len, the token
+ * ids below it).  HSW_E_CAPACITY when every slot is taken. */
+hsw_status hsw_kvm_snapshot(hsw_kvm *kvm, int32_t seq, int32_t *snap, hsw_stream_t stream);
+/* Copy the snapshot's rings back into its sequence's ring slot (one launch)
+ * and set the sequence's length to the snapshot's position.  HSW_E_STALE if
+ * the snapshot was released (the sequence diverged below its position). */
+hsw_status hsw_kvm_restore(hsw_kvm *kvm, int32_t snap, hsw_stream_t stream);
+hsw_status hsw_kvm_drop_snapshot(hsw_kvm *kvm, int32_t snap);
+
+/* Window-safe reuse length of `tokens` (host, n ids) against the sequence:
+ * the longest L <= the common prefix of tokens and the sequence's recorded
+ * ids at which the windowed layers' state is available -- L = len when the
+ * whole sequence is a prefix of tokens (the live rings hold its last
+ * positions), else the highest live snapshot position within the common
+ * prefix (*snap set to it; restore before use), else 0.  *snap = -1 unless a
+ * snapshot is needed.  Returns -1 on bad arguments. */
+int64_t hsw_kvm_window_safe_length(hsw_kvm *kvm, int32_t seq, const int32_t *tokens, int64_t n, int32_t *snap);
 
 #ifdef __cplusplus
 }

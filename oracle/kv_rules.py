@@ -1,0 +1,167 @@
+"""Plain reference model of the dual-pool KV manager's rules.
+
+TEST INFRASTRUCTURE ONLY (like the rest of ``oracle/``): only the tests may
+import it.  It shares no code with the HIP library and never imports it.
+
+Every rule is written the slow, obvious way -- the full-attention pool as one
+owner entry per row, scanned from row 0; the reuse length by trying every
+length -- so that it can be checked by eye against the pages:
+
+* gokawiil "Full-Pipeline Inference Optimization for MiMo-V2.5 Series",
+  section 2.1 "SWA KVCache Management": full-attention layers keep O(N) rows
+  per sequence, windowed layers O(W) (the ring); a request is admitted only if
+  BOTH pools have room ("validates both Full KV and SWA KV capacity
+  constraints when admitting requests"); prefix reuse is clipped to the
+  "window-safe length", the longest matched prefix whose last W positions the
+  windowed layers still hold (anything beyond is a miss).
+* colibri "MiMo-V2.6 (Xiaomi)", section "System One mode and prompt reuse":
+  a snapshot leaves the full layers' rows in place and records the token ids
+  they hold; a prompt that diverged below the snapshot rewrote them and the
+  snapshot is released; the windowed layers' rings are copied into the
+  snapshot and back, and the snapshot's position is its length.
+
+Readings where the pages leave a step open (each stated in the design notes):
+* pool rows are handed out as one contiguous run per sequence (the attention
+  calls address rows as seq_base + position), at the lowest row where
+  ``max_len`` free rows start; the ring slot is the lowest free one;
+* the windowed layers' state exists at exactly three kinds of length: 0
+  (nothing to hold), the live length (the rings hold its last W positions)
+  and a live snapshot's position; of equal lengths the live state is
+  preferred, then the lowest snapshot id;
+* a snapshot is released as soon as an append writes a token id different
+  from the one its row held at a position below the snapshot's, and never
+  comes back.
+"""
+from __future__ import annotations
+
+
+class KvModel:
+    CAPACITY, STALE, SHAPE = "capacity", "stale", "shape"
+
+    def __init__(self, ring_seqs: int, pool_rows: int, max_snapshots: int):
+        self.owner = [None] * pool_rows          # sequence owning each pool row
+        self.ring = [False] * ring_seqs          # ring slot taken?
+        self.seqs = {}                           # seq -> dict(base, max_len, len, rows)
+        self.snap_slots = [False] * max_snapshots
+        self.snaps = {}                          # id -> dict(seq, pos, slot)
+        self.next_id = 0
+
+    # -- admission / release --------------------------------------------
+    def first_run(self, n: int):
+        """Lowest row where n consecutive free rows start, or None."""
+        for start in range(0, len(self.owner) - n + 1):
+            if all(self.owner[r] is None for r in range(start, start + n)):
+                return start
+        return None
+
+    def admit(self, max_len: int):
+        if max_len < 1:
+            return self.SHAPE
+        slot = next((i for i, t in enumerate(self.ring) if not t), None)
+        start = self.first_run(max_len)
+        if slot is None or start is None:      # both pools checked, nothing taken
+            return self.CAPACITY
+        self.ring[slot] = True
+        for r in range(start, start + max_len):
+            self.owner[r] = slot
+        self.seqs[slot] = dict(base=start, max_len=max_len, len=0, rows=[])
+        return slot, start
+
+    def release(self, seq: int):
+        if seq not in self.seqs:
+            return self.SHAPE
+        s = self.seqs.pop(seq)
+        for r in range(s["base"], s["base"] + s["max_len"]):
+            self.owner[r] = None
+        self.ring[seq] = False
+        for sid in [k for k, v in self.snaps.items() if v["seq"] == seq]:
+            self._drop(sid)
+        return None
+
+    # -- token record ----------------------------------------------------
+    def append(self, seq: int, tokens):
+        if seq not in self.seqs:
+            return self.SHAPE
+        s = self.seqs[seq]
+        if s["len"] + len(tokens) > s["max_len"]:
+            return self.CAPACITY
+        start = s["len"]
+        for i, t in enumerate(tokens):
+            p = start + i
+            if p < len(s["rows"]):
+                if s["rows"][p] != t:
+                    # row p now holds another history: snapshots above it go
+                    for sid in [k for k, v in self.snaps.items() if v["seq"] == seq and v["pos"] > p]:
+                        self._drop(sid)
+                    s["rows"][p] = t
+            else:
+                s["rows"].append(t)
+        s["len"] = start + len(tokens)
+        return start
+
+    def truncate(self, seq: int, new_len: int):
+        if seq not in self.seqs or not 0 <= new_len <= self.seqs[seq]["len"]:
+            return self.SHAPE
+        self.seqs[seq]["len"] = new_len
+        return None
+
+    def info(self, seq: int):
+        if seq not in self.seqs:
+            return self.SHAPE
+        s = self.seqs[seq]
+        return s["len"], s["base"], s["max_len"]
+
+    def free_space(self):
+        run = best = 0
+        for o in self.owner:
+            run = run + 1 if o is None else 0
+            best = max(best, run)
+        return self.ring.count(False), best, self.snap_slots.count(False)
+
+    # -- snapshots -------------------------------------------------------
+    def snapshot(self, seq: int):
+        if seq not in self.seqs:
+            return self.SHAPE
+        slot = next((i for i, t in enumerate(self.snap_slots) if not t), None)
+        if slot is None:
+            return self.CAPACITY
+        self.snap_slots[slot] = True
+        sid = self.next_id
+        self.next_id += 1
+        self.snaps[sid] = dict(seq=seq, pos=self.seqs[seq]["len"], slot=slot)
+        return sid
+
+    def _drop(self, sid: int):
+        self.snap_slots[self.snaps[sid]["slot"]] = False
+        del self.snaps[sid]
+
+    def drop_snapshot(self, sid: int):
+        if sid not in self.snaps:
+            return self.STALE
+        self._drop(sid)
+        return None
+
+    def restore(self, sid: int):
+        if sid not in self.snaps:
+            return self.STALE
+        sn = self.snaps[sid]
+        self.seqs[sn["seq"]]["len"] = sn["pos"]
+        return sn["seq"], sn["slot"]
+
+    # -- reuse -----------------------------------------------------------
+    def window_safe_length(self, seq: int, tokens):
+        """Brute force over every length L: the first L ids must equal the
+        ids the rows hold, and the windowed state must exist at L."""
+        if seq not in self.seqs:
+            return None
+        s = self.seqs[seq]
+        best, snap = 0, -1
+        for L in range(0, len(tokens) + 1):
+            if L > len(s["rows"]) or list(tokens[:L]) != s["rows"][:L]:
+                continue
+            if L == s["len"] and L > best:
+                best, snap = L, -1
+            for sid in sorted(self.snaps):
+                if self.snaps[sid]["seq"] == seq and self.snaps[sid]["pos"] == L and L > best:
+                    best, snap = L, sid
+        return best, snap

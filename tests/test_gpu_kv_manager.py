@@ -1,0 +1,234 @@
+"""Dual-pool KV manager on the GPU: ring snapshots through the copy kernel,
+and a bitwise resume through the attention calls.
+
+colibri "MiMo-V2.6 (Xiaomi)", section "System One mode and prompt reuse": a
+snapshot copies every windowed layer's ring out and back, leaves the full
+layers' rows in place, and resuming from it is exact to the bit; gokawiil
+section 2.1: both pools checked at admission, reuse clipped to the
+window-safe length.  Bars: every copied or resumed byte bit-exact; the
+resumed attention outputs equal to the first run's bit for bit and, against
+the fp64 oracle fed the exact K/V rows, within max_abs 2e-2 / mean_rel 2e-3.
+"""
+from __future__ import annotations
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, f64, note, shape_kw
+from oracle.kv_rules import KvModel
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+hsw = pytest.importorskip("hybrid_sliding_window_amd.hsw")
+from hybrid_sliding_window_amd import workloads as wl  # noqa: E402
+
+BF = torch.bfloat16
+
+
+def rings(n_layers, ring_seqs, hkv, g, window=128):
+    k = [wl.randn((ring_seqs, hkv, window, 192), g, device=DEV) for _ in range(n_layers)]
+    v = [wl.randn((ring_seqs, hkv, window, 128), g, device=DEV) for _ in range(n_layers)]
+    return k, v
+
+
+def test_snapshot_holds_each_layers_ring_blocks_and_restores_them():
+    note("kvm ring snapshot / restore bytes")
+    g = wl.gen(91, DEV)
+    L, S, H = 3, 5, 8
+    k, v = rings(L, S, H, g)
+    cfg = hsw.KvmConfig(L, H, 128, 192, 128, 2, S, 1000, 2)
+    sb = hsw.hsw_kvm_snapshot_bytes(cfg)
+    snap_buf = torch.full((2 * sb // 2,), -3.0, dtype=BF, device=DEV)
+    kv = hsw.KvManager(cfg, k, v, snap_buf)
+    seq, _ = kv.admit(10)
+    seq2, _ = kv.admit(10)
+    seq3, _ = kv.admit(10)          # ring slot 2
+    kv.append(seq3, [5, 6])
+    sid = kv.snapshot(seq3)
+    torch.cuda.synchronize()
+    want = torch.cat([torch.cat([k[l][seq3].flatten(), v[l][seq3].flatten()]) for l in range(L)])
+    slot_bytes = snap_buf[:sb // 2]
+    assert torch.equal(slot_bytes.cpu(), want.cpu()), "snapshot bytes differ from the ring blocks"
+    assert bool((snap_buf[sb // 2:] == -3.0).all()), "the other snapshot slot was written"
+    before = [(kk.clone(), vv.clone()) for kk, vv in zip(k, v)]
+    for l in range(L):                                   # the ring moves on
+        k[l][seq3].normal_()
+        v[l][seq3].normal_()
+    kv.append(seq3, [7])
+    kv.restore(sid)
+    torch.cuda.synchronize()
+    for l in range(L):
+        assert torch.equal(k[l].cpu(), before[l][0].cpu()) and torch.equal(v[l].cpu(), before[l][1].cpu())
+    assert kv.info(seq3)[0] == 2
+    kv.close()
+
+
+def test_manager_matches_model_with_snapshots():
+    """Random operations including snapshots, restores and ring rewrites:
+    every result equals the reference model's, and every restore brings back
+    the exact ring bytes the snapshot saw."""
+    note("kvm random operations with snapshots")
+    rng = random.Random(92)
+    g = wl.gen(92, DEV)
+    L, S, H, R, NS = 2, 4, 2, 60, 3
+    k, v = rings(L, S, H, g, window=16)
+    k = [t[..., :16].contiguous() for t in k]
+    v = [t[..., :8].contiguous() for t in v]
+    cfg = hsw.KvmConfig(L, H, 16, 16, 8, 2, S, R, NS)
+    sb = hsw.hsw_kvm_snapshot_bytes(cfg)
+    snap_buf = torch.zeros((NS * sb // 2,), dtype=BF, device=DEV)
+    kv = hsw.KvManager(cfg, k, v, snap_buf)
+    m = KvModel(S, R, NS)
+    saved = {}                                        # snapshot id -> ring contents it saw
+    codes = {7: KvModel.CAPACITY, 8: KvModel.STALE, 2: KvModel.SHAPE}
+
+    def call(fn, *a):
+        try:
+            return fn(*a)
+        except hsw.HswError as e:
+            return codes.get(e.status, e.status)
+
+    for step in range(300):
+        live = sorted(m.seqs)
+        seq = rng.choice(live) if live else 0
+        op = rng.choice(["admit", "append", "append", "truncate", "snap", "restore", "restore", "drop",
+                         "rewrite", "release", "wsl"])
+        if op == "admit":
+            n = rng.randint(1, 20)
+            got, want = call(kv.admit, n), m.admit(n)
+        elif op == "append":
+            toks = [rng.choice([1, 2]) for _ in range(rng.randint(0, 4))]
+            got, want = call(kv.append, seq, toks), m.append(seq, toks)
+        elif op == "truncate":
+            n = rng.randint(0, 6)
+            got, want = call(kv.truncate, seq, n), m.truncate(seq, n)
+        elif op == "snap":
+            got, want = call(kv.snapshot, seq), m.snapshot(seq)
+            if isinstance(want, int):
+                saved[want] = [(k[l][seq].clone(), v[l][seq].clone()) for l in range(L)]
+        elif op in ("restore", "drop"):
+            sid = rng.choice(sorted(m.snaps) + [m.next_id]) if m.snaps else m.next_id
+            if op == "restore":
+                got, want = call(kv.restore, sid), m.restore(sid)
+                if isinstance(want, tuple):
+                    torch.cuda.synchronize()
+                    tgt = want[0]
+                    for l in range(L):
+                        assert torch.equal(k[l][tgt], saved[sid][l][0]), (step, "K ring not restored")
+                        assert torch.equal(v[l][tgt], saved[sid][l][1]), (step, "V ring not restored")
+                    want = None
+            else:
+                got, want = call(kv.drop_snapshot, sid), m.drop_snapshot(sid)
+        elif op == "rewrite":
+            for l in range(L):
+                k[l][seq].normal_()
+                v[l][seq].normal_()
+            got = want = None
+        elif op == "release":
+            got, want = call(kv.release, seq), m.release(seq)
+        else:
+            if seq not in m.seqs:
+                continue
+            toks = m.seqs[seq]["rows"][:rng.randint(0, 8)] + [rng.choice([1, 2]) for _ in range(rng.randint(0, 3))]
+            got, want = kv.window_safe_length(seq, toks), m.window_safe_length(seq, toks)
+        assert got == want, (step, op, got, want)
+        assert kv.free_space() == m.free_space(), step
+    kv.close()
+
+
+def chunk_inputs(seed, T, hq, hkv):
+    g = wl.gen(seed)
+    return (wl.randn((T, hq, 192), g), wl.randn((T, hkv, 192), g), wl.randn((T, hkv, 128), g))
+
+
+def test_bitwise_resume_through_the_attention_calls():
+    """One windowed and one full layer (Flash shapes).  Prompt of 300 tokens,
+    snapshot, option A (40 tokens), restore, option B, restore, option A
+    again: A's outputs and caches come back bit for bit, and A's outputs match
+    the oracle over the true history."""
+    note("kvm bitwise resume")
+    swa, full = wl.swa_shape(), wl.full_shape()
+    hq = 64
+    S, R = 2, 2048
+    kring = torch.zeros((S, 8, 128, 192), dtype=BF, device=DEV)
+    vring = torch.zeros((S, 8, 128, 128), dtype=BF, device=DEV)
+    kpool = torch.zeros((R, 4, 192), dtype=BF, device=DEV)
+    vpool = torch.zeros((R, 4, 128), dtype=BF, device=DEV)
+    cfg = hsw.KvmConfig(1, 8, 128, 192, 128, 2, S, R, 2)
+    sb = hsw.hsw_kvm_snapshot_bytes(cfg)
+    snap_buf = torch.zeros((2 * sb // 2,), dtype=BF, device=DEV)
+    kv = hsw.KvManager(cfg, [kring], [vring], snap_buf)
+    other, _ = kv.admit(100)                 # another sequence first: the chunk's rows start at 100
+    seq, base = kv.admit(1024)
+    assert base == 100
+    sinks = wl.sinks(hq, wl.gen(93)).to(DEV)
+    staging = {}
+
+    def run(tokens, inputs):
+        """Append tokens, then RoPE + windowed prefill and RoPE + full prefill
+        of the chunk at the sequence's current position."""
+        start = kv.append(seq, tokens)
+        T = len(tokens)
+        qs, ks, vs = (t.to(DEV) for t in inputs[0])
+        qf, kf, vf = (t.to(DEV) for t in inputs[1])
+        pos = torch.arange(start, start + T, dtype=torch.int64, device=DEV)
+        cu = torch.tensor([0, T], dtype=torch.int64, device=DEV)
+        st = torch.tensor([start], dtype=torch.int64, device=DEV)
+        q_rot = torch.empty_like(qs)
+        kst, vst = torch.empty_like(ks), torch.empty_like(vs)
+        hsw.hsw_rope_partial_kv_write(swa, T, qs, ks, vs, pos, None, hsw.HSW_DST_STAGING, kst, vst, T, None, q_rot)
+        out_w = torch.empty((T, hq, 128), dtype=BF, device=DEV)
+        hsw.hsw_swa_prefill(swa, 1, T, cu, st, q_rot, kst, vst, kring[seq:seq + 1], vring[seq:seq + 1], sinks, out_w)
+        q_rotf = torch.empty_like(qf)
+        seq_ids = torch.zeros(T, dtype=torch.int32, device=DEV)
+        b = torch.tensor([base], dtype=torch.int64, device=DEV)
+        hsw.hsw_rope_partial_kv_write(full, T, qf, kf, vf, pos, seq_ids, hsw.HSW_DST_POOL, kpool, vpool, R, b, q_rotf)
+        out_f = torch.empty((T, hq, 128), dtype=BF, device=DEV)
+        hsw.hsw_full_prefill_chunk(full, 1, T, cu, st, b, q_rotf, kpool, vpool, R, None, out_f)
+        torch.cuda.synchronize()
+        staging[tuple(tokens)] = (q_rot.cpu(), kst.cpu(), vst.cpu(), q_rotf.cpu(), start)
+        return out_w.cpu(), out_f.cpu()
+
+    prompt = list(range(1000, 1300))
+    A = list(range(2000, 2040))
+    B = list(range(3000, 3040))
+    inp = {"P": [chunk_inputs(94, 300, hq, 8), chunk_inputs(95, 300, hq, 4)],
+           "A": [chunk_inputs(96, 40, hq, 8), chunk_inputs(97, 40, hq, 4)],
+           "B": [chunk_inputs(98, 40, hq, 8), chunk_inputs(99, 40, hq, 4)]}
+    run(prompt, inp["P"])
+    ring_at_p = (kring[seq].cpu(), vring[seq].cpu())
+    sid = kv.snapshot(seq)
+    assert kv.window_safe_length(seq, prompt + A) == (300, -1)
+    a1 = run(A, inp["A"])
+    caches_a1 = (kring[seq].cpu(), vring[seq].cpu(), kpool[base:base + 340].cpu(), vpool[base:base + 340].cpu())
+    assert kv.window_safe_length(seq, prompt + B) == (300, sid)     # A's rings cannot serve B
+    kv.restore(sid)
+    torch.cuda.synchronize()
+    assert torch.equal(kring[seq].cpu(), ring_at_p[0]) and torch.equal(vring[seq].cpu(), ring_at_p[1])
+    run(B, inp["B"])
+    assert kv.window_safe_length(seq, prompt + A)[0] == 300          # the snapshot survived B (it is at 300)
+    kv.restore(sid)
+    a2 = run(A, inp["A"])
+    assert torch.equal(a2[0], a1[0]) and torch.equal(a2[1], a1[1]), "resumed outputs differ"
+    caches_a2 = (kring[seq].cpu(), vring[seq].cpu(), kpool[base:base + 340].cpu(), vpool[base:base + 340].cpu())
+    assert all(torch.equal(x, y) for x, y in zip(caches_a1, caches_a2)), "resumed caches differ"
+
+    # A's outputs against the oracle over the true history (prompt then A)
+    qw, kst_a, vst_a, qf, start = staging[tuple(A)]
+    _, kst_p, vst_p, _, _ = staging[tuple(prompt)]
+    kall = torch.cat([kst_p, kst_a]).double().numpy()
+    vall = torch.cat([vst_p, vst_a]).double().numpy()
+    P = np.arange(300, 340)
+    ref_w = oracle.attn_linear(f64(qw), P, kall, vall, 0, window=128, sinks=f64(sinks), **shape_kw(swa))
+    assert_close(f64(a2[0]), ref_w, what="resumed windowed prefill")
+    kp = f64(kpool[base:base + 340])
+    vp = f64(vpool[base:base + 340])
+    ref_f = oracle.attn_linear(f64(qf), P, kp, vp, 0, window=0, **shape_kw(full))
+    ma, mr = assert_close(f64(a2[1]), ref_f, what="resumed full prefill")
+    print(f"bitwise resume: windowed and full outputs equal after restore; full max_abs={ma:.2e} mean_rel={mr:.2e}")
+    kv.close()
