@@ -120,6 +120,12 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     // per stage and wave: 1 if the wave's block of V columns stayed bf16
     // (a value beyond the fp16 range), 0 if it was converted to fp16
     __shared__ int vflag[3][4];
+    // Raw bf16 copies of the V column blocks kept out of fp16 (rare), by
+    // chunk parity: the stage itself then holds zeros there, so the fp16
+    // product of every tile runs unconditionally and a kept block's tiles are
+    // added from here afterwards.  convert_v of chunk c runs after every wave
+    // passed the barrier of chunk c-1, so no wave still reads chunk c-2's copy.
+    __shared__ __attribute__((aligned(1024))) uint16_t vbk[2][KC * DV];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();  // the intrinsics, so no library call is needed
     const int lane = tid & 63;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     // fp16 cannot hold): then they stay bf16 and the wave's flag says so.
     // The wave's own loads of those pieces must have landed; the barrier
     // after it publishes the result (the flags are read after it too).
-    auto convert_v = [&](uint16_t *vst, int (&vf)[4]) {
+    auto convert_v = [&](uint16_t *vst, int (&vf)[4], uint16_t *vb) {
         u32x4 raw[V_LOADS];
         float big = 0.0f;
 #pragma unroll
@@ -258,6 +264,13 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(raw[i][e]);
                 *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(vst) + (4 * i + w) * 1024 + lane * 16) = h;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                const int off = (4 * i + w) * 1024 + lane * 16;
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(vb) + off) = raw[i];
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(vst) + off) = u32x4{0, 0, 0, 0};
             }
         }
         if (lane == 0) vf[w] = keep ? 1 : 0;
@@ -286,7 +299,8 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
         __asm__ volatile("" ::: "memory");
-        convert_v(vsc, vf);
+        uint16_t *vbc = vbk[c & 1];
+        convert_v(vsc, vf, vbc);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
@@ -370,25 +384,25 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
         // O^T += V^T P^T: slots 0-3 of a quad are keys 4quad.. of the first
         // 16-key half, slots 4-7 the same keys of the second half, on both
         // operands.
-        if (!kept) {
+        // fp16 product of every tile (a kept block reads zeros here)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+            u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
+            u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+            for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf16[n], oacc[n][dt]);
+        }
+        if (kept) {
+            // A kept block's tiles add the same fp16-rounded P, split exactly
+            // into bf16 hi + lo (11 significant bits fit in two bf16), times
+            // the raw bf16 V saved by convert_v.
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
-                u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
-                u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-                for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf16[n], oacc[n][dt]);
-            }
-        } else {
-            // A kept block's tiles multiply the same fp16-rounded P, split
-            // exactly into bf16 hi + lo (11 significant bits fit in two
-            // bf16), by the bf16 V.
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
-                u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
-                u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
                 if ((kept >> (dt / 2)) & 1) {
+                    u32x2 a0 = ds_read_tr16(vbc + (dt * 64 + lane) * 4);
+                    u32x2 a1 = ds_read_tr16(vbc + ((DT + dt) * 64 + lane) * 4);
+                    u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
                     for (int n = 0; n < 2; ++n) {
                         float pf[8];
@@ -407,9 +421,6 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
                         oacc[n][dt] = mfma_16x16x32_bf16(av, u32x4{h0[0], h0[1], h1[0], h1[1]}, oacc[n][dt]);
                         oacc[n][dt] = mfma_16x16x32_bf16(av, u32x4{l0[0], l0[1], l1[0], l1[1]}, oacc[n][dt]);
                     }
-                } else {
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf16[n], oacc[n][dt]);
                 }
             }
         }
