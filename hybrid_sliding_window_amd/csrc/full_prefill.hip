@@ -195,23 +195,34 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     // Chunk c's loads.  Keys past the last one are clamped to it (finite
     // data, masked); past the band a dummy set (the first row, again) keeps
     // the number of loads per step constant.
-    auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd) {
+    // Wave-uniform byte offsets of this wave's loads within a chunk (key
+    // half and 64-byte column of each), computed once: an interior chunk's
+    // load is then its chunk base plus one of these.
+    int64_t kl_off[K_LOADS], vl_off[V_LOADS];
+#pragma unroll
+    for (int i = 0; i < K_LOADS; ++i) {
+        const int j = 4 * i + w;
+        kl_off[i] = (int64_t)(16 * (j / STEPS)) * krow + 64 * (j % STEPS);
+    }
+#pragma unroll
+    for (int i = 0; i < V_LOADS; ++i) {
+        const int j = 4 * i + w;
+        vl_off[i] = (int64_t)(16 * (j / 4)) * vrow + 64 * (j % 4);
+    }
+    // kco / vco: byte offset from kseq / vseq of chunk c's first row, carried
+    // as running sums by the loop.
+    auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd, int64_t kco, int64_t vco) {
         const int k0 = c * KC;
         const char *ksrc[K_LOADS], *vsrc[V_LOADS];
         if (c < nch && k0 + KC - 1 <= klast) {
             // whole chunk inside the band: uniform base + per-lane offset
+            const char *kb = kseq + kco, *vb = vseq + vco;
 #pragma unroll
-            for (int i = 0; i < V_LOADS; ++i) {
-                const int j = 4 * i + w, hh = j / 4;
-                load_lds16_s(vseq + (int64_t)(k0 + 16 * hh) * vrow + 64 * (j % 4), voff_l,
-                             (const char *)vsd + (4 * i + w) * 1024);
-            }
+            for (int i = 0; i < V_LOADS; ++i)
+                load_lds16_s(vb + vl_off[i], voff_l, (const char *)vsd + (4 * i + w) * 1024);
 #pragma unroll
-            for (int i = 0; i < K_LOADS; ++i) {
-                const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
-                load_lds16_s(kseq + (int64_t)(k0 + 16 * h) * krow + 64 * st, koff_l,
-                             (const char *)ksd + (4 * i + w) * 1024);
-            }
+            for (int i = 0; i < K_LOADS; ++i)
+                load_lds16_s(kb + kl_off[i], koff_l, (const char *)ksd + (4 * i + w) * 1024);
             return;
         }
         if (c >= nch) {
@@ -290,7 +301,8 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     // last key visible to the wave's rows / to its first row
     const int vis_hi = min(wpos_hi, nkeys - 1), vis_lo = min(wpos_lo, nkeys - 1);
 
-    auto step = [&](int c, const uint16_t *ksc, uint16_t *vsc, uint16_t *ksn, uint16_t *vsn, int (&vf)[4]) {
+    auto step = [&](int c, const uint16_t *ksc, uint16_t *vsc, uint16_t *ksn, uint16_t *vsn, int (&vf)[4],
+                    int64_t kco_next, int64_t vco_next) {
         // Own loads of chunk c done (chunk c+1's, the last LOADS issued, may
         // still fly); the wave converts its V pieces of chunk c; the barrier
         // makes every wave's K, V and flags visible.  The stage chunk c+2
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
-        issue(c + 2, ksn, vsn);
+        issue(c + 2, ksn, vsn, kco_next, vco_next);
 
         const int k0 = c * KC;
         // skip a chunk no row of this wave can see (wave-uniform)
@@ -428,17 +440,21 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
 
     // No key row in the pool (base outside it): no load at all.
     if (nkeys > 0) {
-        issue(0, ks0, vs0);
-        issue(1, ks1, vs1);
+        const int64_t kchunk = (int64_t)KC * krow, vchunk = (int64_t)KC * vrow;
+        issue(0, ks0, vs0, 0, 0);
+        issue(1, ks1, vs1, kchunk, vchunk);
+        int64_t kco = 2 * kchunk, vco = 2 * vchunk;   // chunk 2, the first one a step issues
         // Unrolled by the three stages; nested so that each step is reached
         // only through the one before it (the compiler then knows which loads
         // into a stage have landed).
         for (int c = 0; c < nch; c += 3) {
-            step(c, ks0, vs0, ks2, vs2, vflag[0]);
+            step(c, ks0, vs0, ks2, vs2, vflag[0], kco, vco);
             if (c + 1 < nch) {
-                step(c + 1, ks1, vs1, ks0, vs0, vflag[1]);
-                if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1, vflag[2]);
+                step(c + 1, ks1, vs1, ks0, vs0, vflag[1], kco + kchunk, vco + vchunk);
+                if (c + 2 < nch) step(c + 2, ks2, vs2, ks1, vs1, vflag[2], kco + 2 * kchunk, vco + 2 * vchunk);
             }
+            kco += 3 * kchunk;
+            vco += 3 * vchunk;
         }
         // The dummy loads past the band must land before a stage is reused
         // below (and before the workgroup's LDS is released).
