@@ -262,12 +262,36 @@ def bench_full_decode(hsw, wl, steps, stream, model=None):
         call(i)
     torch.cuda.synchronize()
     t = ev_time(call, max(steps // 2, 10), stream)
+
+    # the fused chain: K/V-only RoPE into the pool, then the decode that
+    # rotates q itself (fp32 rotated dims, no q_rot written or read)
+    def fused(i):
+        hsw.hsw_full_decode_splitk_qrope(sh, S, max_ctx, d["ctx_len"], d["seq_base"], d["q"], d["kpool"],
+                                         d["vpool"], rows, None, 2048, ws, wsb, out, stream)
+
+    def rope(i):
+        hsw.hsw_rope_partial_kv_write(sh, S, d["q"], d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
+                                      d["kpool"], d["vpool"], rows, d["seq_base"], q_rot, None, stream)
+
+    def rope_kv(i):
+        hsw.hsw_rope_partial_kv_write(sh, S, None, d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
+                                      d["kpool"], d["vpool"], rows, d["seq_base"], None, None, stream)
+    for i in range(3):
+        fused(i)
+    torch.cuda.synchronize()
+    t_fused = ev_time(fused, max(steps // 2, 10), stream)
+    t_rope = ev_time(rope, max(steps, 20), stream)
+    t_rope_kv = ev_time(rope_kv, max(steps, 20), stream)
     L = int(b["ctx_len"].sum())
     bytes_ = L * hkv * (192 + 128) * 2 + S * hq * (192 + 128) * 2
     flops = L * hq * 2 * (192 + 128)
     del d, ws
+    fused_res = dict(ms=t_fused, gbs=bytes_ / t_fused / 1e6, rope_kv_ms=t_rope_kv, rope_ms=t_rope,
+                     chain_ms=t_rope_kv + t_fused, unfused_chain_ms=t_rope + t,
+                     workload="K/V-only RoPE into the pool + hsw_full_decode_splitk_qrope (q rotated in the "
+                              "kernel, kept in fp32) against RoPE + hsw_full_decode_splitk, same workload")
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
-                tflops=flops / t / 1e9,
+                tflops=flops / t / 1e9, fused=fused_res,
                 workload=f"full-attention decode, 64 sequences, contexts U{{32768..131072}}, {hq} q / {hkv} KV "
                          "heads, split-K 2048")
 
@@ -292,9 +316,33 @@ def bench_full_prefill(hsw, wl, steps, stream, model=None):
     call(0)
     torch.cuda.synchronize()
     t = ev_time(call, max(2, steps // 10), stream)
+
+    # the fused chain: K/V-only RoPE into the pool, then the prefill that
+    # rotates q itself (no q_rot written or read)
+    def fused(i):
+        hsw.hsw_full_prefill_chunk_qrope(sh, 1, T, d["cu_seqlens"], d["start_pos"], d["seq_base"], d["q"],
+                                         d["kpool"], d["vpool"], rows, None, out, stream)
+
+    def rope(i):
+        hsw.hsw_rope_partial_kv_write(sh, T, d["q"], d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
+                                      d["kpool"], d["vpool"], rows, d["seq_base"], q_rot, None, stream)
+
+    def rope_kv(i):
+        hsw.hsw_rope_partial_kv_write(sh, T, None, d["k"], d["v"], d["pos"], d["seq"], hsw.HSW_DST_POOL,
+                                      d["kpool"], d["vpool"], rows, d["seq_base"], None, None, stream)
+    fused(0)
+    torch.cuda.synchronize()
+    t_fused = ev_time(fused, max(2, steps // 10), stream)
+    t_rope = ev_time(rope, max(steps, 20), stream)
+    t_rope_kv = ev_time(rope_kv, max(steps, 20), stream)
     pairs = T * 131072 + T * (T + 1) // 2
     flops = pairs * hq * 2 * (192 + 128)
+    fused_res = dict(ms=t_fused, tflops=flops / t_fused / 1e9, rope_kv_ms=t_rope_kv, rope_ms=t_rope,
+                     chain_ms=t_rope_kv + t_fused, unfused_chain_ms=t_rope + t,
+                     workload="K/V-only RoPE into the pool + hsw_full_prefill_chunk_qrope (q rotated in the "
+                              "kernel) against RoPE + hsw_full_prefill_chunk, same workload")
     return dict(ms=t, flops=flops, tflops=flops / t / 1e9, frac_mfma_peak=flops / t / 1e9 / BF16_PEAK_TFLOPS,
+                fused=fused_res,
                 workload=f"full-attention prefill, 8192 tokens after 131072 prior rows, {hq} q / {hkv} KV heads")
 
 
@@ -345,6 +393,12 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
     torch.cuda.synchronize()
     n = max(1, steps)
     t = ev_time(lambda i: hs.step(stream), n, stream)
+    # the same step with every attention call rotating q itself
+    hs.qrope = True
+    hs.step(stream)
+    torch.cuda.synchronize()
+    t_q = ev_time(lambda i: hs.step(stream), n, stream)
+    hs.qrope = False
     timer = []
     hs.step(stream, timer)
     torch.cuda.synchronize()
@@ -354,6 +408,7 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
     T, S = hs.T, hs.S
     nl, nf = len(hs.pattern), len(hs.pattern) - sum(hs.pattern)
     res = dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps=n, per_call_ms={k: round(v, 3) for k, v in kinds.items()},
+               qrope_ms=t_q, qrope_tokens_per_s=(T + S) / (t_q / 1e3),
                layers=f"{nl - nf} windowed + {nf} full (seeded pattern)", pool_gb=round(hs.pool_gb, 1),
                workload=f"hybrid step {model.name}: {nl} layers, 8192-token chunk at 131072 + 128 decode "
                         "sequences U{4096..262144}")
@@ -383,14 +438,17 @@ def bench_pro(hsw, wl, args, stream):
     torch.cuda.empty_cache()
     fd = bench_full_decode(hsw, wl, args.steps, stream, m)
     print(f"[bench] pro full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    out["full_decode_splitk_qrope"] = rounded(fd.pop("fused"))
     out["full_decode_splitk"] = rounded(fd)
     torch.cuda.empty_cache()
     fp = bench_full_prefill(hsw, wl, args.steps, stream, m)
     print(f"[bench] pro full_prefill {fp['ms']:.2f} ms {fp['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    out["full_prefill_chunk_qrope"] = rounded(fp.pop("fused"))
     out["full_prefill_chunk"] = rounded(fp)
     torch.cuda.empty_cache()
     hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m)
-    print(f"[bench] pro hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}",
+    print(f"[bench] pro hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "
+          f"fused q-RoPE step {hy['qrope_ms']:.1f} ms",
           file=sys.stderr, flush=True)
     out["hybrid_step"] = rounded(hy)
     torch.cuda.empty_cache()
@@ -456,7 +514,7 @@ def main():
               "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m)}[args.only]
         r = fn()
         print(json.dumps({"only": args.only, "model": m.name,
-                          **{k: v for k, v in r.items() if not isinstance(v, dict)}}))
+                          **{k: v for k, v in r.items() if not isinstance(v, dict) or k == "fused"}}))
         return
 
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
@@ -472,11 +530,17 @@ def main():
              "swa_decode_qrope": dec.pop("fused"), "swa_decode": dec}
     if not args.quick:
         fd = bench_full_decode(hsw, wl, args.steps, stream)
-        print(f"[bench] full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        print(f"[bench] full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s; fused q-RoPE {fd['fused']['ms']:.3f} ms, "
+              f"chain {fd['fused']['chain_ms']:.3f} vs {fd['fused']['unfused_chain_ms']:.3f} ms",
+              file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         fp = bench_full_prefill(hsw, wl, args.steps, stream)
-        print(f"[bench] full_prefill {fp['ms']:.2f} ms {fp['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        print(f"[bench] full_prefill {fp['ms']:.2f} ms {fp['tflops']:.1f} TFLOP/s; fused q-RoPE "
+              f"{fp['fused']['ms']:.2f} ms, chain {fp['fused']['chain_ms']:.2f} vs "
+              f"{fp['fused']['unfused_chain_ms']:.2f} ms", file=sys.stderr, flush=True)
+        calls["full_decode_splitk_qrope"] = fd.pop("fused")
         calls["full_decode_splitk"] = fd
+        calls["full_prefill_chunk_qrope"] = fp.pop("fused")
         calls["full_prefill_chunk"] = fp
         del fd, fp
         torch.cuda.empty_cache()
@@ -486,7 +550,8 @@ def main():
         calls["kvm_snapshot"] = snap
         torch.cuda.empty_cache()
         hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream)
-        print(f"[bench] hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}",
+        print(f"[bench] hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "
+              f"fused q-RoPE step {hy['qrope_ms']:.1f} ms",
               file=sys.stderr, flush=True)
         calls["hybrid_step"] = hy
         torch.cuda.empty_cache()

@@ -21,6 +21,12 @@
 //   M = max m_c,  Z = sum 2^(m_c - M) l_c (+ 2^(sink - M) once),
 //   o = value_scale * sum 2^(m_c - M) acc_c / Z.
 // HBM-bound: every K/V row is read exactly once.
+//
+// With QROPE the partial kernel reads unrotated q and rotates it at the new
+// token's position ctx_len - 1 (colibri "What the engine implements"; angle
+// in double per the gaudi-cookbook "The RoPE fix for large positions"); the
+// rotated rotary dims stay fp32 and enter S^T as bf16 hi + lo, so no bf16
+// q_rot is written, read or rounded.
 #include "hsw_device.h"
 #include "hsw_launch.h"
 
@@ -46,10 +52,11 @@ struct StepRegs {
     u32x4 v[8];
 };
 
-template <int G>
+template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t vt[4 * DV * VT_STRIDE];
     __shared__ float red_m[4][16], red_l[4][16];
+    __shared__ float qcs[QROPE ? 4 : 1][64];  // per wave: cos, sin of the 32 angles
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int quad = lane >> 4, col = lane & 15;
@@ -78,6 +85,42 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
 #pragma unroll
     for (int st = 0; st < STEPS; ++st)
         qb[st] = col < G ? ld16(Q + col * DQK + 32 * st + 8 * quad) : u32x4{0, 0, 0, 0};
+    // QROPE: steps 0 and 1 (dims 8 quad .. and their partners 32 + 8 quad ..)
+    // become the rotated values split into bf16 hi (qb) + lo (ql).
+    u32x4 ql[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+    if constexpr (QROPE) {
+        float cv, sv;
+        rope_cos_sin(L - 1, a.inv_freq[lane & 31], cv, sv);
+        if (lane < 32) {
+            qcs[w][lane] = cv;
+            qcs[w][32 + lane] = sv;
+        }
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&qcs[w][8 * quad]);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&qcs[w][8 * quad + 4]);
+        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&qcs[w][32 + 8 * quad]);
+        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(&qcs[w][32 + 8 * quad + 4]);
+        const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        float yl[8], yh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t wl = qb[0][e >> 1], wh = qb[1][e >> 1];
+            const float xl = __uint_as_float((e & 1) ? (wl & 0xffff0000u) : (wl << 16));
+            const float xh = __uint_as_float((e & 1) ? (wh & 0xffff0000u) : (wh << 16));
+            rope_rotate(xl, xh, cc[e], ss[e], yl[e], yh[e]);
+        }
+        u32x2 lh0, ll0, lh1, ll1, hh0, hl0, hh1, hl1;
+        split_hi_lo(yl, lh0, ll0);
+        split_hi_lo(yl + 4, lh1, ll1);
+        split_hi_lo(yh, hh0, hl0);
+        split_hi_lo(yh + 4, hh1, hl1);
+        if (col < G) {
+            qb[0] = u32x4{lh0[0], lh0[1], lh1[0], lh1[1]};
+            ql[0] = u32x4{ll0[0], ll0[1], ll1[0], ll1[1]};
+            qb[1] = u32x4{hh0[0], hh0[1], hh1[0], hh1[1]};
+            ql[1] = u32x4{hl0[0], hl0[1], hl1[0], hl1[1]};
+        }
+    }
 
     auto load_step = [&](int i, StepRegs &r) {
         const int64_t k0 = w0 + (int64_t)i * KS;
@@ -114,6 +157,12 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
         for (int st = 0; st < STEPS; ++st)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) sacc[kt] = mfma_16x16x32_bf16(cur.k[kt][st], qb[st], sacc[kt]);
+        if constexpr (QROPE) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) sacc[kt] = mfma_16x16x32_bf16(cur.k[kt][st], ql[st], sacc[kt]);
+        }
         // V^T of this step into the wave's LDS tile (DS ops of one wave run
         // in order, so the reads below see these writes and the writes of the
         // next step come after these reads).
@@ -241,12 +290,22 @@ bool full_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
 
 hipError_t launch_full_decode(const AttnArgs &a, hipStream_t s) {
     dim3 grid((unsigned)(a.n_seqs * a.hkv * a.n_chunks)), block(kThreads);
-    switch (a.hq / a.hkv) {
-        case 1: hipLaunchKernelGGL(full_decode_partial_kernel<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(full_decode_partial_kernel<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(full_decode_partial_kernel<4>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(full_decode_partial_kernel<8>, grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(full_decode_partial_kernel<16>, grid, block, 0, s, a); break;
+    if (a.qrope) {
+        switch (a.hq / a.hkv) {
+            case 1: hipLaunchKernelGGL((full_decode_partial_kernel<1, true>), grid, block, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((full_decode_partial_kernel<2, true>), grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((full_decode_partial_kernel<4, true>), grid, block, 0, s, a); break;
+            case 8: hipLaunchKernelGGL((full_decode_partial_kernel<8, true>), grid, block, 0, s, a); break;
+            default: hipLaunchKernelGGL((full_decode_partial_kernel<16, true>), grid, block, 0, s, a); break;
+        }
+    } else {
+        switch (a.hq / a.hkv) {
+            case 1: hipLaunchKernelGGL((full_decode_partial_kernel<1, false>), grid, block, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((full_decode_partial_kernel<2, false>), grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((full_decode_partial_kernel<4, false>), grid, block, 0, s, a); break;
+            case 8: hipLaunchKernelGGL((full_decode_partial_kernel<8, false>), grid, block, 0, s, a); break;
+            default: hipLaunchKernelGGL((full_decode_partial_kernel<16, false>), grid, block, 0, s, a); break;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -30,6 +30,12 @@
 // run in lane order, free of bank conflicts.  Block ids are remapped so
 // consecutive query blocks of one (sequence, KV head) run on one XCD and
 // stream the same keys through its L2.
+//
+// With QROPE the kernel reads unrotated q and applies the rotate-half RoPE
+// itself (colibri "What the engine implements"; the angle in double as the
+// gaudi-cookbook "The RoPE fix for large positions" requires) with the RoPE
+// kernel's helpers and rounding, so the output is bit-identical to RoPE
+// followed by the plain kernel, without q_rot's write and re-read.
 #include "hsw_device.h"
 #include "hsw_launch.h"
 
@@ -110,7 +116,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return (bid % 8) * (total / 8) + bid / 8;
 }
 
-template <int G>
+template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, int nqb) {
     constexpr int BQ = 128 / G;
     // Three stages, each its own LDS object so the compiler can tell that a
@@ -151,6 +157,9 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     const int klast = max(nkeys - 1, 0);
     const int nch = max((nkeys + KC - 1) / KC, 1);
 
+    // this lane's rotary frequency (fused q-RoPE), loaded before any
+    // untracked load
+    const double invf = QROPE ? pin_loaded(a.inv_freq[lane & 31]) : 0.0;
     // q of this wave's rows (row r = 32w + 16n + col -> position r / G, head
     // r % G), from a clamped row so the load is unconditional; rows past the
     // block only affect their own column and are never stored.
@@ -163,8 +172,16 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
         const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            qv[n][st] = u32x4{0, 0, 0, 0};
-            load_q16(qv[n][st], qrow + 32 * st + 8 * quad);
+            // (tracked when the kernel rotates q: its first use, the
+            // rotation, then waits for it before the loop; untracked ones
+            // could be copied or reused by the register allocator before
+            // the rotation's wait)
+            if constexpr (QROPE) {
+                qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+            } else {
+                qv[n][st] = u32x4{0, 0, 0, 0};
+                load_q16(qv[n][st], qrow + 32 * st + 8 * quad);
+            }
         }
     }
 
@@ -443,6 +460,40 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
         const int64_t kchunk = (int64_t)KC * krow, vchunk = (int64_t)KC * vrow;
         issue(0, ks0, vs0, 0, 0);
         issue(1, ks1, vs1, kchunk, vchunk);
+        if constexpr (QROPE) {
+            // Rotate the unrotated q in registers with the RoPE kernel's own
+            // helpers (so the result equals RoPE then this kernel, bit for
+            // bit).  The wave's 32 rows cover NP positions; entry e = 32 i + f
+            // of the table is frequency f at position pw + i (cos in ks2, sin
+            // in vs2: the first loads into either are issued after the first
+            // step's barrier, which each wave reaches after these reads).
+            constexpr int NP = 32 / G;
+            static_assert(4 * NP * 32 <= KC * DQK / 2 && 4 * NP * 32 <= KC * DV / 2, "cos/sin table too large");
+            float *tc = reinterpret_cast<float *>(ks2) + w * (NP * 32);
+            float *ts = reinterpret_cast<float *>(vs2) + w * (NP * 32);
+            const int pw = p0 + (32 * w) / G;
+#pragma unroll
+            for (int e = lane; e < NP * 32; e += 64) {
+                float cv, sv;
+                rope_cos_sin((int64_t)(pw + e / 32), invf, cv, sv);
+                tc[e] = cv;
+                ts[e] = sv;
+            }
+            // (q's loads are tracked here: the compiler waits for them
+            // before the first use below; the table was built while they flew)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int pi = (16 * n + col) / G;
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad);
+                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad + 4);
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad);
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad + 4);
+                const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                rope_rotate_bf16x8(qv[n][0], qv[n][1], cc, ss);
+            }
+            settle_q(qv);   // every q load has landed before the loop
+        }
         int64_t kco = 2 * kchunk, vco = 2 * vchunk;   // chunk 2, the first one a step issues
         // Unrolled by the three stages; nested so that each step is reached
         // only through the one before it (the compiler then knows which loads
@@ -461,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_barrier();
     } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the q loads
+        wait_vmcnt_q<0>(qv);  // the q loads, before their registers may be reused
     }
 
     // Epilogue: an optional sink joins the denominator once; scale; bf16.
@@ -511,18 +562,36 @@ bool full_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
            (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
+// Shapes the full-attention kernels that rotate q themselves take: the bf16
+// fast shapes with a 64-dim rotary part, and (prefill, for the per-wave
+// cos/sin table) at least two query heads per KV head.
+bool full_qrope_ok(const AttnArgs &a, int dtype, int out_dtype, bool prefill) {
+    const int G = a.hq / a.hkv;
+    const bool fast = prefill ? full_prefill_fast_ok(a, dtype, out_dtype) : full_decode_fast_ok(a, dtype, out_dtype);
+    return fast && a.rope_dim == 64 && (!prefill || G >= 2);
+}
+
 hipError_t launch_full_prefill(const AttnArgs &a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int BQ = 128 / G;
     const int64_t nqb = (a.max_seqlen + BQ - 1) / BQ;
     dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(kThreads);
     const int nq = (int)nqb;
+    if (a.qrope) {
+        switch (G) {
+            case 2: hipLaunchKernelGGL((full_prefill_kernel<2, true>), grid, block, 0, s, a, nq); break;
+            case 4: hipLaunchKernelGGL((full_prefill_kernel<4, true>), grid, block, 0, s, a, nq); break;
+            case 8: hipLaunchKernelGGL((full_prefill_kernel<8, true>), grid, block, 0, s, a, nq); break;
+            default: hipLaunchKernelGGL((full_prefill_kernel<16, true>), grid, block, 0, s, a, nq); break;
+        }
+        return hipGetLastError();
+    }
     switch (G) {
-        case 1: hipLaunchKernelGGL(full_prefill_kernel<1>, grid, block, 0, s, a, nq); break;
-        case 2: hipLaunchKernelGGL(full_prefill_kernel<2>, grid, block, 0, s, a, nq); break;
-        case 4: hipLaunchKernelGGL(full_prefill_kernel<4>, grid, block, 0, s, a, nq); break;
-        case 8: hipLaunchKernelGGL(full_prefill_kernel<8>, grid, block, 0, s, a, nq); break;
-        default: hipLaunchKernelGGL(full_prefill_kernel<16>, grid, block, 0, s, a, nq); break;
+        case 1: hipLaunchKernelGGL((full_prefill_kernel<1, false>), grid, block, 0, s, a, nq); break;
+        case 2: hipLaunchKernelGGL((full_prefill_kernel<2, false>), grid, block, 0, s, a, nq); break;
+        case 4: hipLaunchKernelGGL((full_prefill_kernel<4, false>), grid, block, 0, s, a, nq); break;
+        case 8: hipLaunchKernelGGL((full_prefill_kernel<8, false>), grid, block, 0, s, a, nq); break;
+        default: hipLaunchKernelGGL((full_prefill_kernel<16, false>), grid, block, 0, s, a, nq); break;
     }
     return hipGetLastError();
 }

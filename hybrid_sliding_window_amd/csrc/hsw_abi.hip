@@ -100,6 +100,79 @@ hsw::AttnArgs base_args(const hsw_attn_shape *sh) {
 
 }  // namespace
 
+namespace {
+hsw_status full_decode_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx, const int64_t *ctx_len,
+                            const int64_t *seq_base, const void *q, const void *k_pool, const void *v_pool,
+                            int64_t pool_rows, const float *sinks, int32_t chunk, void *ws, size_t ws_bytes,
+                            void *out, hipStream_t s, bool qrope, const char *what) {
+    hsw_status st = check_shape(sh, 0);
+    if (st) return st;
+    if (n_seqs < 0 || max_ctx < 0 || pool_rows < 0)
+        return fail(HSW_E_SHAPE, "n_seqs, max_ctx and pool_rows must be >= 0");
+    if (chunk <= 0 || chunk % 128 != 0) return fail(HSW_E_SHAPE, "chunk (%d) must be a positive multiple of 128", chunk);
+    if (!q) return fail(HSW_E_NULL, qrope ? "q is NULL" : "q_rot is NULL");
+    REQUIRE_PTR(ctx_len); REQUIRE_PTR(seq_base); REQUIRE_PTR(k_pool);
+    REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k_pool, 16); REQUIRE_ALIGN(v_pool, 16);
+    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(ws, 16); REQUIRE_ALIGN(ctx_len, 8);
+    REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(sinks, 4);
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kFullDecode;
+    a.qrope = qrope ? 1 : 0;
+    a.chunk = chunk;
+    if (qrope && !hsw::full_qrope_ok(a, sh->dtype, sh->out_dtype, false))
+        return fail(HSW_E_SHAPE, "full_decode_splitk_qrope needs bf16 in and out, d_qk 192, d_v 128, rope_dim 64 "
+                                 "and 1, 2, 4, 8 or 16 query heads per KV head");
+    if (n_seqs == 0) return HSW_OK;
+    size_t need = hsw_full_decode_workspace_bytes(sh, n_seqs, max_ctx, chunk);
+    if (!ws || ws_bytes < need)
+        return fail(HSW_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
+    if (max_ctx == 0) return HSW_OK;
+    int64_t nc = (max_ctx + chunk - 1) / chunk;
+    if ((int64_t)n_seqs * sh->n_kv_heads * nc > 0x7fffffffLL || (int64_t)n_seqs * sh->n_q_heads > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "grid too large");
+    a.q = q; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.ctx_len = ctx_len;
+    a.seq_base = seq_base; a.out = out; a.ws = ws; a.n_seqs = n_seqs; a.n_rows = n_seqs;
+    a.max_seqlen = max_ctx; a.pool_rows = pool_rows; a.n_chunks = (int)nc;
+    hipError_t e = (qrope || hsw::full_decode_fast_ok(a, sh->dtype, sh->out_dtype))
+                       ? hsw::launch_full_decode(a, s)
+                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
+    return launched(e, what);
+}
+
+hsw_status full_prefill_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                             const int64_t *cu_seqlens, const int64_t *start_pos, const int64_t *seq_base,
+                             const void *q, const void *k_pool, const void *v_pool, int64_t pool_rows,
+                             const float *sinks, void *out, hipStream_t s, bool qrope, const char *what) {
+    hsw_status st = check_shape(sh, 0);
+    if (st) return st;
+    if (n_seqs < 0 || max_seqlen < 0 || pool_rows < 0)
+        return fail(HSW_E_SHAPE, "n_seqs, max_seqlen and pool_rows must be >= 0");
+    if (!q) return fail(HSW_E_NULL, qrope ? "q is NULL" : "q_rot is NULL");
+    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(start_pos); REQUIRE_PTR(seq_base);
+    REQUIRE_PTR(k_pool); REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k_pool, 16); REQUIRE_ALIGN(v_pool, 16);
+    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(start_pos, 8);
+    REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(sinks, 4);
+    hsw::AttnArgs a = base_args(sh);
+    a.kind = hsw::kFullPrefill;
+    a.qrope = qrope ? 1 : 0;
+    if (qrope && !hsw::full_qrope_ok(a, sh->dtype, sh->out_dtype, true))
+        return fail(HSW_E_SHAPE, "full_prefill_chunk_qrope needs bf16 in and out, d_qk 192, d_v 128, rope_dim 64 "
+                                 "and 2, 4, 8 or 16 query heads per KV head");
+    if (n_seqs == 0 || max_seqlen == 0) return HSW_OK;
+    if ((int64_t)n_seqs * max_seqlen * sh->n_q_heads > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "n_seqs * max_seqlen * n_q_heads exceeds 2^31 - 1");
+    a.q = q; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
+    a.start_pos = start_pos; a.seq_base = seq_base; a.out = out; a.n_seqs = n_seqs;
+    a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen; a.pool_rows = pool_rows;
+    hipError_t e = (qrope || hsw::full_prefill_fast_ok(a, sh->dtype, sh->out_dtype))
+                       ? hsw::launch_full_prefill(a, s)
+                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
+    return launched(e, what);
+}
+}  // namespace
+
 extern "C" {
 
 const char *hsw_status_str(hsw_status s) {
@@ -269,39 +342,23 @@ size_t hsw_full_decode_workspace_bytes(const hsw_attn_shape *sh, int32_t n_seqs,
     return hsw::full_decode_ws_bytes(n_seqs, sh->n_q_heads, nc, sh->d_v);
 }
 
+
 hsw_status hsw_full_decode_splitk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
                                   const int64_t *ctx_len, const int64_t *seq_base,
                                   const void *q_rot, const void *k_pool, const void *v_pool,
                                   int64_t pool_rows, const float *sinks, int32_t chunk, void *ws,
                                   size_t ws_bytes, void *out, hsw_stream_t stream) {
-    hsw_status st = check_shape(sh, 0);
-    if (st) return st;
-    if (n_seqs < 0 || max_ctx < 0 || pool_rows < 0)
-        return fail(HSW_E_SHAPE, "n_seqs, max_ctx and pool_rows must be >= 0");
-    if (chunk <= 0 || chunk % 128 != 0) return fail(HSW_E_SHAPE, "chunk (%d) must be a positive multiple of 128", chunk);
-    REQUIRE_PTR(ctx_len); REQUIRE_PTR(seq_base); REQUIRE_PTR(q_rot); REQUIRE_PTR(k_pool);
-    REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
-    REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(k_pool, 16); REQUIRE_ALIGN(v_pool, 16);
-    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(ws, 16); REQUIRE_ALIGN(ctx_len, 8);
-    REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(sinks, 4);
-    if (n_seqs == 0) return HSW_OK;
-    size_t need = hsw_full_decode_workspace_bytes(sh, n_seqs, max_ctx, chunk);
-    if (!ws || ws_bytes < need)
-        return fail(HSW_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
-    if (max_ctx == 0) return HSW_OK;
-    int64_t nc = (max_ctx + chunk - 1) / chunk;
-    if ((int64_t)n_seqs * sh->n_kv_heads * nc > 0x7fffffffLL || (int64_t)n_seqs * sh->n_q_heads > 0x7fffffffLL)
-        return fail(HSW_E_SHAPE, "grid too large");
-    hsw::AttnArgs a = base_args(sh);
-    a.kind = hsw::kFullDecode;
-    a.q = q_rot; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.ctx_len = ctx_len;
-    a.seq_base = seq_base; a.out = out; a.ws = ws; a.n_seqs = n_seqs; a.n_rows = n_seqs;
-    a.max_seqlen = max_ctx; a.pool_rows = pool_rows; a.chunk = chunk; a.n_chunks = (int)nc;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hsw::full_decode_fast_ok(a, sh->dtype, sh->out_dtype)
-                       ? hsw::launch_full_decode(a, s)
-                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
-    return launched(e, "full_decode_splitk");
+    return full_decode_impl(sh, n_seqs, max_ctx, ctx_len, seq_base, q_rot, k_pool, v_pool, pool_rows, sinks, chunk,
+                            ws, ws_bytes, out, (hipStream_t)stream, false, "full_decode_splitk");
+}
+
+hsw_status hsw_full_decode_splitk_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                        const int64_t *ctx_len, const int64_t *seq_base, const void *q,
+                                        const void *k_pool, const void *v_pool, int64_t pool_rows,
+                                        const float *sinks, int32_t chunk, void *ws, size_t ws_bytes, void *out,
+                                        hsw_stream_t stream) {
+    return full_decode_impl(sh, n_seqs, max_ctx, ctx_len, seq_base, q, k_pool, v_pool, pool_rows, sinks, chunk,
+                            ws, ws_bytes, out, (hipStream_t)stream, true, "full_decode_splitk_qrope");
 }
 
 hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
@@ -309,28 +366,17 @@ hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int6
                                   const int64_t *seq_base, const void *q_rot, const void *k_pool,
                                   const void *v_pool, int64_t pool_rows, const float *sinks,
                                   void *out, hsw_stream_t stream) {
-    hsw_status st = check_shape(sh, 0);
-    if (st) return st;
-    if (n_seqs < 0 || max_seqlen < 0 || pool_rows < 0)
-        return fail(HSW_E_SHAPE, "n_seqs, max_seqlen and pool_rows must be >= 0");
-    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(start_pos); REQUIRE_PTR(seq_base); REQUIRE_PTR(q_rot);
-    REQUIRE_PTR(k_pool); REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
-    REQUIRE_ALIGN(q_rot, 16); REQUIRE_ALIGN(k_pool, 16); REQUIRE_ALIGN(v_pool, 16);
-    REQUIRE_ALIGN(out, 16); REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(start_pos, 8);
-    REQUIRE_ALIGN(seq_base, 8); REQUIRE_ALIGN(sinks, 4);
-    if (n_seqs == 0 || max_seqlen == 0) return HSW_OK;
-    if ((int64_t)n_seqs * max_seqlen * sh->n_q_heads > 0x7fffffffLL)
-        return fail(HSW_E_SHAPE, "n_seqs * max_seqlen * n_q_heads exceeds 2^31 - 1");
-    hsw::AttnArgs a = base_args(sh);
-    a.kind = hsw::kFullPrefill;
-    a.q = q_rot; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
-    a.start_pos = start_pos; a.seq_base = seq_base; a.out = out; a.n_seqs = n_seqs;
-    a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen; a.pool_rows = pool_rows;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hsw::full_prefill_fast_ok(a, sh->dtype, sh->out_dtype)
-                       ? hsw::launch_full_prefill(a, s)
-                       : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
-    return launched(e, "full_prefill_chunk");
+    return full_prefill_impl(sh, n_seqs, max_seqlen, cu_seqlens, start_pos, seq_base, q_rot, k_pool, v_pool,
+                             pool_rows, sinks, out, (hipStream_t)stream, false, "full_prefill_chunk");
+}
+
+hsw_status hsw_full_prefill_chunk_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                                        const int64_t *cu_seqlens, const int64_t *start_pos,
+                                        const int64_t *seq_base, const void *q, const void *k_pool,
+                                        const void *v_pool, int64_t pool_rows, const float *sinks, void *out,
+                                        hsw_stream_t stream) {
+    return full_prefill_impl(sh, n_seqs, max_seqlen, cu_seqlens, start_pos, seq_base, q, k_pool, v_pool,
+                             pool_rows, sinks, out, (hipStream_t)stream, true, "full_prefill_chunk_qrope");
 }
 
 int64_t hsw_kv_bytes(int32_t kind, int64_t n_seqs, int64_t ctx, int32_t window, int32_t n_kv_heads,

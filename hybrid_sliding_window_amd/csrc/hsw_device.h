@@ -185,6 +185,38 @@ __device__ __forceinline__ void rope_rotate_bf16x8(u32x4 &lo, u32x4 &hi, const f
     }
 }
 
+// Wait until at most N vector-memory operations of the wave are outstanding
+// and redefine the twelve q registers there: uses of q (filled by untracked
+// loads) cannot be scheduled above the wait, which a bare s_waitcnt does not
+// guarantee.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_q(u32x4 (&q)[2][6]) {
+    asm volatile("s_waitcnt vmcnt(%12)"
+                 : "+v"(q[0][0]), "+v"(q[0][1]), "+v"(q[0][2]), "+v"(q[0][3]), "+v"(q[0][4]), "+v"(q[0][5]),
+                   "+v"(q[1][0]), "+v"(q[1][1]), "+v"(q[1][2]), "+v"(q[1][3]), "+v"(q[1][4]), "+v"(q[1][5])
+                 : "n"(N)
+                 : "memory");
+}
+
+// Redefine the twelve q registers here (no instruction).  After q was loaded
+// by tracked loads, the compiler's waits for every one of them land before
+// this point, once, rather than at each register's first use inside a loop,
+// where, counting only its own loads, each would also wait for the untracked
+// chunk loads in flight.
+__device__ __forceinline__ void settle_q(u32x4 (&q)[2][6]) {
+    asm volatile(""
+                 : "+v"(q[0][0]), "+v"(q[0][1]), "+v"(q[0][2]), "+v"(q[0][3]), "+v"(q[0][4]), "+v"(q[0][5]),
+                   "+v"(q[1][0]), "+v"(q[1][1]), "+v"(q[1][2]), "+v"(q[1][3]), "+v"(q[1][4]), "+v"(q[1][5]));
+}
+
+// A value loaded by an ordinary (tracked) load, forced to have arrived here:
+// placed before a kernel's untracked loads, the compiler's wait for it cannot
+// land after them (where, counting only its own loads, it would be vmcnt(0)).
+__device__ __forceinline__ double pin_loaded(double x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Element access for the two storage types.
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> {

@@ -66,6 +66,7 @@ hipError_t launch_generic_attn(const AttnArgs &a, int dtype, int out_dtype, hipS
 hipError_t launch_ring_commit(const AttnArgs &a, int dtype, hipStream_t s);
 bool swa_decode_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
 bool swa_qrope_ok(const AttnArgs &a, int dtype, int out_dtype, bool prefill);
+bool full_qrope_ok(const AttnArgs &a, int dtype, int out_dtype, bool prefill);
 hipError_t launch_swa_decode(const AttnArgs &a, hipStream_t s);
 bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype);
 hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s);

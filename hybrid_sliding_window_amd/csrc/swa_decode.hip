@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
 
     for (int i = threadIdx.x; i < a.hq; i += kThreads) sk[i] = a.sinks ? a.sinks[i] * kLog2e : -INFINITY;
     // frequency (lane mod 32) of the rotary pairs
-    const double invf = QROPE ? a.inv_freq[lane & 31] : 0.0;
+    // (pinned here, before the first untracked load: see pin_loaded)
+    const double invf = QROPE ? pin_loaded(a.inv_freq[lane & 31]) : 0.0;
 
     // Per-lane constant parts of the load addresses.  K: A operand of the
     // S^T MFMA, lane (quad, col) takes slot 32w + 16h + col, dims 32st + 8quad.

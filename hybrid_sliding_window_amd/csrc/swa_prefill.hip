@@ -165,6 +165,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     const int kstart = max(0, p0 - (W - 1));        // band: kstart .. plast
     const int nch = max((plast - kstart + KC) / KC, 1);  // >= 1 (stated so the compiler knows the loop runs)
 
+    // this lane's rotary frequency (fused q-RoPE), loaded before any
+    // untracked load
+    const double invf = QROPE ? pin_loaded(a.inv_freq[lane & 31]) : 0.0;
     // q of this wave's rows (row r = 32w + 16n + col -> position r / G, head
     // r % G), from a clamped row so the load is unconditional; rows past the
     // chunk only affect their own column and are never stored.
@@ -179,8 +182,16 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            qv[n][st] = u32x4{0, 0, 0, 0};
-            load_q16(qv[n][st], qrow + 32 * st + 8 * quad);
+            // (tracked when the kernel rotates q: its first use, the
+            // rotation, then waits for it before the loop; untracked ones
+            // could be copied or reused by the register allocator before
+            // the rotation's wait)
+            if constexpr (QROPE) {
+                qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+            } else {
+                qv[n][st] = u32x4{0, 0, 0, 0};
+                load_q16(qv[n][st], qrow + 32 * st + 8 * quad);
+            }
         }
     }
 
@@ -453,7 +464,6 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
         static_assert(4 * NP * 32 <= KC * DQK / 2 && 4 * NP * 32 <= KC * DV / 2, "cos/sin table too large");
         float *tc = reinterpret_cast<float *>(ks2) + w * (NP * 32);
         float *ts = reinterpret_cast<float *>(vs2) + w * (NP * 32);
-        const double invf = a.inv_freq[lane & 31];
         const int pw = p0 + (32 * w) / G;
 #pragma unroll
         for (int e = lane; e < NP * 32; e += 64) {
@@ -462,14 +472,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
             tc[e] = cv;
             ts[e] = sv;
         }
-        // q has landed once at most the chunk loads issued after it are
-        // outstanding (loads complete in order); the table above was built
-        // while they were in flight.
-        if (nch > 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LOADS));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-        __asm__ volatile("" ::: "memory");
+        // (q's loads are tracked here: the compiler waits for them before
+        // the first use below; the table above was built while they flew)
         // Lane (quad, col) holds dims 8 quad .. +7 (step 0) and their
         // partners 32 + 8 quad .. (step 1) of row 32w + 16n + col.
 #pragma unroll
@@ -483,6 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
             const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
             rope_rotate_bf16x8(qv[n][0], qv[n][1], cc, ss);
         }
+        settle_q(qv);   // every q load has landed before the loop
     }
     for (int c = 0; c < nch; c += 3) {
         step(c, ks0, vs0, ks2, vs2, vflag[0]);

@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.hsw_full_decode_workspace_bytes.restype = SZ
     lib.hsw_full_decode_splitk.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, SZ, P, P]
     lib.hsw_full_prefill_chunk.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
+    lib.hsw_full_prefill_chunk_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
+    lib.hsw_full_decode_splitk_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, SZ, P, P]
     lib.hsw_kv_bytes.argtypes = [I32, I64, I64, I32, I32, I32, I32, I32, I32]
     lib.hsw_kv_bytes.restype = I64
     KC = ctypes.POINTER(KvmConfig)
@@ -96,7 +98,8 @@ def _load() -> ctypes.CDLL:
               "hsw_kvm_drop_snapshot"):
         getattr(lib, f).restype = I32
     for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope",
-              "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_prefill_chunk"):
+              "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_prefill_chunk",
+              "hsw_full_decode_splitk_qrope", "hsw_full_prefill_chunk_qrope"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -106,7 +109,8 @@ lib = _load()
 EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_rope_partial_kv_write",
             "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope", "hsw_swa_decode_qrope",
             "hsw_full_decode_workspace_bytes",
-            "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_kv_bytes",
+            "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_full_decode_splitk_qrope",
+            "hsw_full_prefill_chunk_qrope", "hsw_kv_bytes",
             "hsw_kvm_snapshot_bytes", "hsw_kvm_create", "hsw_kvm_destroy", "hsw_kvm_admit", "hsw_kvm_release",
             "hsw_kvm_append", "hsw_kvm_truncate", "hsw_kvm_info", "hsw_kvm_free_space", "hsw_kvm_snapshot",
             "hsw_kvm_restore", "hsw_kvm_drop_snapshot", "hsw_kvm_window_safe_length")
@@ -194,6 +198,24 @@ def hsw_full_prefill_chunk(shape, n_seqs, max_seqlen, cu_seqlens, start_pos, seq
                                       _ptr(v_pool), int(pool_rows), _ptr(sinks), _ptr(out),
                                       _stream(stream)),
            "hsw_full_prefill_chunk")
+
+
+def hsw_full_decode_splitk_qrope(shape, n_seqs, max_ctx, ctx_len, seq_base, q, k_pool, v_pool,
+                                 pool_rows, sinks, chunk, ws, ws_bytes, out, stream=None):
+    _check(lib.hsw_full_decode_splitk_qrope(_sh(shape), int(n_seqs), int(max_ctx), _ptr(ctx_len),
+                                            _ptr(seq_base), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                            int(pool_rows), _ptr(sinks), int(chunk), _ptr(ws),
+                                            int(ws_bytes), _ptr(out), _stream(stream)),
+           "hsw_full_decode_splitk_qrope")
+
+
+def hsw_full_prefill_chunk_qrope(shape, n_seqs, max_seqlen, cu_seqlens, start_pos, seq_base, q,
+                                 k_pool, v_pool, pool_rows, sinks, out, stream=None):
+    _check(lib.hsw_full_prefill_chunk_qrope(_sh(shape), int(n_seqs), int(max_seqlen), _ptr(cu_seqlens),
+                                            _ptr(start_pos), _ptr(seq_base), _ptr(q), _ptr(k_pool),
+                                            _ptr(v_pool), int(pool_rows), _ptr(sinks), _ptr(out),
+                                            _stream(stream)),
+           "hsw_full_prefill_chunk_qrope")
 
 
 def hsw_kv_bytes(kind, n_seqs, ctx, window, n_kv_heads, d_qk, d_v_stored, elem_bytes, n_layers) -> int:

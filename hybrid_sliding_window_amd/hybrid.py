@@ -16,6 +16,10 @@ batch of decode sequences on every layer:
                   the pool, RoPE + pool write of the decode tokens, split-K
                   full decode.
 
+With qrope=True the RoPE calls rotate and write K/V only and each attention
+call is its *_qrope form, which rotates the raw q itself (no q_rot round trip
+through HBM).
+
 Sizes default to the bench workload: the model's layers (MiMo-V2.6-Flash: 48,
 39 windowed + 9 full; MiMo-V2.6-Pro: 70, 60 + 10; the full layers at seeded
 indices), an 8192-token chunk at positions 131072..139263 and 128 decode
@@ -32,9 +36,10 @@ from . import workloads as wl
 
 class HybridStep:
     def __init__(self, hsw, pattern=None, T=8192, P0=131072, S=128, ctx_lo=4096, ctx_hi=262144, seed=5,
-                 device="cuda:0", chunk=2048, model=wl.FLASH):
+                 device="cuda:0", chunk=2048, model=wl.FLASH, qrope=False):
         self.hsw = hsw
         self.model = model
+        self.qrope = qrope
         self.pattern = (list(wl.hybrid_pattern(seed, model.n_layers, model.n_full)) if pattern is None
                         else list(pattern))
         self.T, self.P0, self.S, self.chunk = T, P0, S, chunk
@@ -85,8 +90,11 @@ class HybridStep:
         self.wsb = hsw.hsw_full_decode_workspace_bytes(self.full, S, self.max_ctx, chunk)
         self.ws = torch.empty(self.wsb // 4 + 4, dtype=torch.float32, device=device)
 
-    def calls(self, li, stream=None):
-        """The four calls of layer li as (name, thunk) pairs, in order."""
+    def calls(self, li, stream=None, qrope=None):
+        """The four calls of layer li as (name, thunk) pairs, in order
+        (qrope: override the instance's choice of fused q-RoPE)."""
+        if self.qrope if qrope is None else qrope:
+            return self._calls_qrope(li, stream)
         h, d, T, S = self.hsw, self.layers[li], self.T, self.S
         if self.pattern[li] == 1:
             swa = self.swa
@@ -117,6 +125,40 @@ class HybridStep:
             ("full_decode", lambda: h.hsw_full_decode_splitk(full, S, self.max_ctx, self.d_L, self.d_base_dec,
                                                              self.q_rot_d, self.kpool, self.vpool, self.rows, None,
                                                              self.chunk, self.ws, self.wsb, self.out_d, stream)),
+        ]
+
+    def _calls_qrope(self, li, stream):
+        h, d, T, S = self.hsw, self.layers[li], self.T, self.S
+        if self.pattern[li] == 1:
+            swa = self.swa
+            return [
+                ("rope", lambda: h.hsw_rope_partial_kv_write(swa, T, None, d["kc"], d["vc"], self.d_pos_c, None,
+                                                             h.HSW_DST_STAGING, self.kst, self.vst, T, None, None,
+                                                             None, stream)),
+                ("swa_prefill", lambda: h.hsw_swa_prefill_qrope(swa, 1, T, self.d_cu, self.d_start, d["qc"],
+                                                                self.kst, self.vst, d["kring"][S:], d["vring"][S:],
+                                                                self.sinks, self.out, stream)),
+                ("rope", lambda: h.hsw_rope_partial_kv_write(swa, S, None, d["kd"], d["vd"], self.d_pos_dec,
+                                                             self.d_seq_dec, h.HSW_DST_RING, d["kring"], d["vring"],
+                                                             S + 1, None, None, None, stream)),
+                ("swa_decode", lambda: h.hsw_swa_decode_qrope(swa, S, self.d_pos_dec, d["qd"], d["kring"],
+                                                              d["vring"], self.sinks, self.out_d, stream)),
+            ]
+        full = self.full
+        return [
+            ("rope", lambda: h.hsw_rope_partial_kv_write(full, T, None, d["kc"], d["vc"], self.d_pos_c,
+                                                         self.d_seq_c0, h.HSW_DST_POOL, self.kpool, self.vpool,
+                                                         self.rows, self.d_base_c, None, None, stream)),
+            ("full_prefill", lambda: h.hsw_full_prefill_chunk_qrope(full, 1, T, self.d_cu, self.d_start,
+                                                                    self.d_base_c, d["qc"], self.kpool, self.vpool,
+                                                                    self.rows, None, self.out, stream)),
+            ("rope", lambda: h.hsw_rope_partial_kv_write(full, S, None, d["kd"], d["vd"], self.d_pos_dec,
+                                                         self.d_seq_dec, h.HSW_DST_POOL, self.kpool, self.vpool,
+                                                         self.rows, self.d_base_dec, None, None, stream)),
+            ("full_decode", lambda: h.hsw_full_decode_splitk_qrope(full, S, self.max_ctx, self.d_L,
+                                                                   self.d_base_dec, d["qd"], self.kpool, self.vpool,
+                                                                   self.rows, None, self.chunk, self.ws, self.wsb,
+                                                                   self.out_d, stream)),
         ]
 
     def step(self, stream=None, timer=None):

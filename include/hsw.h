@@ -252,6 +252,39 @@ hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int6
                                   const float *sinks, void *out, hsw_stream_t stream);
 
 /*
+ * hsw_full_prefill_chunk with the q-RoPE fused in: q [T][Hq][d_qk] is
+ * unrotated (the chunk's K/V rows must already be in the pool, e.g. by
+ * hsw_rope_partial_kv_write with q = q_rot = NULL) and is rotated in the
+ * kernel at positions start_pos[s] + t with the RoPE call's own arithmetic
+ * (colibri "What the engine implements"; gaudi-cookbook "The RoPE fix for
+ * large positions"), so out is bit-identical to that call followed by
+ * hsw_full_prefill_chunk; no q_rot is written or read.  Supported shapes:
+ * bf16 in and out, d_qk 192, d_v 128, rope_dim 64, 2/4/8/16 query heads per
+ * KV head (HSW_E_SHAPE otherwise); other arguments and errors as
+ * hsw_full_prefill_chunk.
+ */
+hsw_status hsw_full_prefill_chunk_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,
+                                        const int64_t *cu_seqlens, const int64_t *start_pos,
+                                        const int64_t *seq_base, const void *q, const void *k_pool,
+                                        const void *v_pool, int64_t pool_rows, const float *sinks, void *out,
+                                        hsw_stream_t stream);
+
+/*
+ * hsw_full_decode_splitk with the q-RoPE fused in: q [n_seqs][Hq][d_qk] is
+ * unrotated and is rotated in the kernel at each sequence's new position
+ * ctx_len[s] - 1; the rotated rotary dims stay fp32 (bf16 hi + lo in the
+ * products).  The pool must already hold the new token's K/V.  Supported
+ * shapes: bf16 in and out, d_qk 192, d_v 128, rope_dim 64, 1/2/4/8/16 query
+ * heads per KV head (HSW_E_SHAPE otherwise); other arguments, the workspace
+ * and errors as hsw_full_decode_splitk.
+ */
+hsw_status hsw_full_decode_splitk_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                        const int64_t *ctx_len, const int64_t *seq_base, const void *q,
+                                        const void *k_pool, const void *v_pool, int64_t pool_rows,
+                                        const float *sinks, int32_t chunk, void *ws, size_t ws_bytes, void *out,
+                                        hsw_stream_t stream);
+
+/*
  * KV-cache bytes (host arithmetic).  kind HSW_DST_RING: every sequence holds
  * `window` positions whatever ctx is (the O(W) ring of colibri "What the
  * engine implements"); HSW_DST_POOL: ctx positions.  Per position and layer:

@@ -133,6 +133,29 @@ def test_fused_qrope_argument_errors():
     expect(2, hsw.hsw_swa_decode_qrope, fs, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE)
     hsw.hsw_swa_decode_qrope(sh, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE)
     hsw.hsw_swa_decode_qrope(mha, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE)   # G = 1 decode is supported
+    # the full-attention calls that rotate q themselves
+    fpre = (1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE)
+    hsw.hsw_full_prefill_chunk_qrope(fs, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE)  # empty
+    expect(1, hsw.hsw_full_prefill_chunk_qrope, fs, 1, 8, FAKE, FAKE, FAKE, None, FAKE, FAKE, 100, None, FAKE)
+    expect(3, hsw.hsw_full_prefill_chunk_qrope, fs, 1, 8, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 100, None, FAKE)
+    fmha = hsw.make_shape(wl.full_shape(4, 4))        # one q head per KV head: no prefill table
+    expect(2, hsw.hsw_full_prefill_chunk_qrope, fmha, *fpre)
+    fr32 = full()
+    fr32.rope_dim = 32
+    expect(2, hsw.hsw_full_prefill_chunk_qrope, fr32, *fpre)
+    ff32 = hsw.make_shape(wl.full_shape(dtype=__import__("torch").float32))
+    expect(2, hsw.hsw_full_prefill_chunk_qrope, ff32, *fpre)
+    need = hsw.hsw_full_decode_workspace_bytes(fs, 4, 10000, 2048)
+    dec = (4, 10000, FAKE, FAKE, FAKE, FAKE, FAKE, 40000, None, 2048, FAKE, need, FAKE)
+    expect(2, hsw.hsw_full_decode_splitk_qrope, fr32, *dec)
+    expect(2, hsw.hsw_full_decode_splitk_qrope, ff32, *dec)
+    expect(1, hsw.hsw_full_decode_splitk_qrope, fs, 4, 10000, FAKE, FAKE, None, FAKE, FAKE, 40000, None,
+           2048, FAKE, need, FAKE)
+    expect(5, hsw.hsw_full_decode_splitk_qrope, fs, 4, 10000, FAKE, FAKE, FAKE, FAKE, FAKE, 40000, None,
+           2048, FAKE, need - 16, FAKE)
+    hsw.hsw_full_decode_splitk_qrope(fs, 0, 10000, FAKE, FAKE, FAKE, FAKE, FAKE, 40000, None, 2048, FAKE, 0, FAKE)
+    hsw.hsw_full_decode_splitk_qrope(fmha, 0, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 400, None, 2048, FAKE, 0,
+                                     FAKE)  # G = 1 decode is supported
     args = dict(n_tokens=0, q=None, k=FAKE, v=FAKE, pos=FAKE, seq=FAKE, dst_kind=hsw.HSW_DST_RING,
                 k_dst=FAKE, v_dst=FAKE, dst_capacity=4, seq_base=None, q_rot=None)
     hsw.hsw_rope_partial_kv_write(sh, **args)                              # K/V only, empty

@@ -138,3 +138,72 @@ def test_hybrid_full_layer_sampled(hs):
         got.append(f64(hs.out_d[s]))
     ma, mr = assert_close(np.stack(got), np.stack(refs), what="hybrid full_decode")
     print(f"hybrid full_decode sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_hybrid_fused_qrope_calls(hs):
+    """The same two layers through the driver's fused q-RoPE calls (K/V-only
+    RoPE, then the *_qrope attention calls on the raw q): both prefills
+    byte-identical to the unfused calls on the same state, both decodes
+    against the oracle fed the raw q rotated in fp64."""
+    T, S, P0 = hs.T, hs.S, hs.P0
+    d0, d1 = hs.layers[0], hs.layers[1]
+    P = hs.L.numpy() - 1
+    plain = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(0, qrope=False)))
+    fused = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(0, qrope=True)))
+
+    note("hybrid fused windowed: prefill against the unfused call from the same ring")
+    kr0, vr0 = d0["kring"][S].clone(), d0["vring"][S].clone()
+    plain["rope0"]()
+    plain["swa_prefill1"]()
+    torch.cuda.synchronize()
+    out_u, kst_u = hs.out.clone(), hs.kst.clone()
+    kr_u, vr_u = d0["kring"][S].clone(), d0["vring"][S].clone()
+    d0["kring"][S].copy_(kr0)
+    d0["vring"][S].copy_(vr0)
+    fused["rope0"]()
+    fused["swa_prefill1"]()
+    torch.cuda.synchronize()
+    assert torch.equal(hs.kst, kst_u)
+    assert torch.equal(d0["kring"][S], kr_u) and torch.equal(d0["vring"][S], vr_u)
+    assert torch.equal(hs.out, out_u), "fused windowed prefill differs from the unfused call"
+    del out_u, kst_u
+
+    note("hybrid fused windowed: decode")
+    fused["rope2"]()
+    fused["swa_decode3"]()
+    torch.cuda.synchronize()
+    seqs = sorted({int(P.argmin()), int(P.argmax()), 5, 77})
+    qr = oracle.rope(f64(d0["qd"][seqs]), P[seqs], hs.swa.rope_theta)
+    ref = oracle.ring_decode(qr, P[seqs], f64(d0["kring"][seqs]), f64(d0["vring"][seqs]),
+                             sinks=f64(hs.sinks), **shape_kw(hs.swa))
+    ma, mr = assert_close(f64(hs.out_d[seqs]), ref, what="hybrid swa_decode_qrope")
+    print(f"hybrid swa_decode_qrope sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+    plain = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(1, qrope=False)))
+    fused = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(1, qrope=True)))
+    note("hybrid fused full: chunked prefill against the unfused call")
+    plain["rope0"]()
+    plain["full_prefill1"]()
+    torch.cuda.synchronize()
+    out_u = hs.out.clone()
+    fused["rope0"]()
+    fused["full_prefill1"]()
+    torch.cuda.synchronize()
+    assert torch.equal(hs.out, out_u), "fused chunked prefill differs from the unfused call"
+    del out_u
+
+    note("hybrid fused full: split-K decode")
+    fused["rope2"]()
+    fused["full_decode3"]()
+    torch.cuda.synchronize()
+    L, base = hs.L.numpy(), hs.base_dec.numpy()
+    seqs = sorted({int(L.argmin()), int(L.argmax()), 9})
+    qr = oracle.rope(f64(d1["qd"][seqs]), L[seqs] - 1, hs.full.rope_theta)
+    got, refs = [], []
+    for i, s in enumerate(seqs):
+        k = f64(hs.kpool[base[s]:base[s] + L[s]])
+        v = f64(hs.vpool[base[s]:base[s] + L[s]])
+        refs.append(oracle.attn_linear(qr[i:i + 1], [L[s] - 1], k, v, 0, window=0, **shape_kw(hs.full))[0])
+        got.append(f64(hs.out_d[s]))
+    ma, mr = assert_close(np.stack(got), np.stack(refs), what="hybrid full_decode_qrope")
+    print(f"hybrid full_decode_qrope sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")

@@ -744,3 +744,99 @@ def test_swa_decode_qrope_against_raw_chain(model):
         print(f"swa_decode_qrope {model} {name}: max_abs={ma:.2e} mean_rel={mr:.2e} "
               f"(bf16 q_rot path: max_abs={mau:.2e} mean_rel={mru:.2e})")
         assert mr <= mru * 1.02, "fp32 rotated q should not be less accurate than a bf16 q_rot"
+
+
+def run_full_prefill_qrope(batch, kpool, vpool):
+    """K/V-only RoPE into the pool, then the chunked prefill that rotates q itself."""
+    shape = batch["shape"]
+    T = batch["q"].shape[0]
+    S = batch["start_pos"].shape[0]
+    rows = kpool.shape[0]
+    hsw.hsw_rope_partial_kv_write(shape, T, None, dev(batch["k"]), dev(batch["v"]), dev(batch["pos"]),
+                                  dev(batch["seq"]), POOL, kpool, vpool, rows, dev(batch["seq_base"]), None)
+    lens = batch["cu_seqlens"][1:] - batch["cu_seqlens"][:-1]
+    out = torch.full((T, shape.n_q_heads, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_full_prefill_chunk_qrope(shape, S, int(lens.max()), dev(batch["cu_seqlens"]), dev(batch["start_pos"]),
+                                     dev(batch["seq_base"]), dev(batch["q"]), kpool, vpool, rows, None, out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("model", ["flash", "pro"])
+@pytest.mark.parametrize("case", ["ragged", "8192_after_131072"])
+def test_full_prefill_qrope_bitwise_equals_rope_then_prefill(case, model):
+    """The fused chunked prefill rotates q with the RoPE call's arithmetic and
+    stores it as bf16 in the same registers the unfused kernel loads q_rot
+    into, so its output is byte-identical to RoPE then hsw_full_prefill_chunk
+    (held to the oracle by the other full prefill tests), over ragged chunks
+    and at the full size, where every output row is compared."""
+    note(f"full_prefill_qrope bitwise {case} {model}")
+    kw = wl.model_kw(wl.MODELS[model], "full")
+    if case == "ragged":
+        batch = wl.full_prefill_batch(seed=73, n_seqs=4, seqlens=(300, 77, 129, 1),
+                                      start_pos=(3000, 100, 0, 40000), **kw)
+    else:
+        batch = wl.full_prefill_batch(seed=5, device=DEV, **kw)
+    kpool0, vpool0 = dev(batch["kpool"]).clone(), dev(batch["vpool"]).clone()
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    out2 = run_full_prefill_qrope(batch, kpool0, vpool0)
+    assert torch.equal(kpool0, kpool) and torch.equal(vpool0, vpool)
+    assert torch.equal(out2, out), "fused chunked prefill differs from RoPE + prefill"
+    print(f"full_prefill_qrope {case} {model}: bitwise equal to RoPE + prefill over {out.shape[0]} rows")
+
+
+@pytest.mark.parametrize("model", ["flash", "pro"])
+@pytest.mark.parametrize("case", ["small", "64_seqs"])
+def test_full_decode_qrope_against_raw_chain(case, model):
+    """K/V-only RoPE into the pool, then the split-K decode that rotates q
+    itself in fp32: against the oracle fed the raw q rotated in fp64 and the
+    exact pool bytes, at the bar, and no less accurate than RoPE to a bf16
+    q_rot followed by hsw_full_decode_splitk on the same pool."""
+    note(f"full_decode_qrope {case} {model}")
+    kw = wl.model_kw(wl.MODELS[model], "full")
+    if case == "small":
+        lengths = [1, 2, 127, 2047, 2048, 2049, 9000, 4097]
+        batch = wl.full_decode_batch(seed=62, n_seqs=len(lengths), lengths=lengths, with_sinks=True, **kw)
+        seqs, chunk = list(range(len(lengths))), 128
+    else:
+        batch = wl.full_decode_batch(seed=4, device=DEV, **kw)
+        L = batch["ctx_len"].numpy()
+        seqs, chunk = sorted({int(L.argmin()), int(L.argmax()), 17, 42}), 2048
+    shape = batch["shape"]
+    S = batch["ctx_len"].shape[0]
+    sinks = dev(batch.get("sinks"))
+    kpool, vpool = dev(batch["kpool"]), dev(batch["vpool"])
+    rows = kpool.shape[0]
+    hsw.hsw_rope_partial_kv_write(shape, S, None, dev(batch["k"]), dev(batch["v"]), dev(batch["pos"]),
+                                  dev(batch["seq"]), POOL, kpool, vpool, rows, dev(batch["seq_base"]), None)
+    max_ctx = int(batch["ctx_len"].max())
+    wsb = hsw.hsw_full_decode_workspace_bytes(shape, S, max_ctx, chunk)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=DEV)
+    out = torch.full((S, shape.n_q_heads, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    hsw.hsw_full_decode_splitk_qrope(shape, S, max_ctx, dev(batch["ctx_len"]), dev(batch["seq_base"]),
+                                     dev(batch["q"]), kpool, vpool, rows, sinks, chunk, ws, wsb, out)
+    # the unfused path on the same pool (RoPE of q only through a scratch K/V destination)
+    q_rot = torch.empty_like(dev(batch["q"]))
+    kd, vd = torch.empty_like(dev(batch["k"])), torch.empty_like(dev(batch["v"]))
+    hsw.hsw_rope_partial_kv_write(shape, S, dev(batch["q"]), dev(batch["k"]), dev(batch["v"]), dev(batch["pos"]),
+                                  None, STAGING, kd, vd, S, None, q_rot)
+    out_u = torch.empty_like(out)
+    hsw.hsw_full_decode_splitk(shape, S, max_ctx, dev(batch["ctx_len"]), dev(batch["seq_base"]), q_rot,
+                               kpool, vpool, rows, sinks, chunk, ws, wsb, out_u)
+    torch.cuda.synchronize()
+    q_raw = batch["q"].cpu()[seqs]
+    qr = oracle.rope(f64(q_raw), batch["pos"].cpu().numpy()[seqs], shape.rope_theta)
+    Ls = batch["ctx_len"].tolist()
+    base = batch["seq_base"].tolist()
+    refs = []
+    for i, s in enumerate(seqs):
+        k = f64(kpool[base[s]:base[s] + Ls[s]])
+        v = f64(vpool[base[s]:base[s] + Ls[s]])
+        refs.append(oracle.attn_linear(qr[i:i + 1], [Ls[s] - 1], k, v, 0, window=0,
+                                       sinks=None if sinks is None else f64(sinks), **shape_kw(shape))[0])
+    ref = np.stack(refs)
+    ma, mr = assert_close(f64(out[seqs]), ref, what=f"full_decode_qrope {case} {model}")
+    mau, mru = errors(f64(out_u[seqs]), ref)
+    print(f"full_decode_qrope {case} {model}: max_abs={ma:.2e} mean_rel={mr:.2e} "
+          f"(bf16 q_rot path: max_abs={mau:.2e} mean_rel={mru:.2e})")
+    assert mr <= mru * 1.05, "fp32 rotated q should not be less accurate than a bf16 q_rot"

@@ -90,7 +90,7 @@ def test_checker_follows_prologue_loads_into_the_loop():
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
 @pytest.mark.parametrize("src,kernel,n", [("swa_prefill.hip", "swa_prefill_kernel", 9),
-                                          ("full_prefill.hip", "full_prefill_kernel", 5)])
+                                          ("full_prefill.hip", "full_prefill_kernel", 9)])
 def test_prefill_q_loads_are_never_touched_in_flight(src, kernel, n):
     asm = avc.compile_to_asm(os.path.join(CSRC, src))
     kernels = {k: v for k, v in avc.kernel_functions(asm).items() if kernel in k}
