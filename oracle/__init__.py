@@ -70,6 +70,12 @@ def _load():
             lib.hswo_attn_partial.restype = i32
             lib.hswo_join_sink.argtypes = [i64, i32, P, P, P, P]
             lib.hswo_lse_merge.argtypes = [i64, i64, i32, P, P, P, P, P]
+            lib.hswo_vit_layout.argtypes = [i32, i32, P, P, P]
+            lib.hswo_vit_layout.restype = i32
+            lib.hswo_rope_2d.argtypes = [i64, i32, i32, f64, P, P, P, P]
+            lib.hswo_vit_attn.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, f64,
+                                          P, P, P, P, P]
+            lib.hswo_vit_attn.restype = i32
             _lib = lib
     return _lib
 
@@ -198,3 +204,49 @@ def lse_merge(m, l, acc):
     lse = np.empty(rest, np.float64)
     _load().hswo_lse_merge(C, n, dv, _p(m), _p(l), _p(acc), _p(o), _p(lse))
     return o, lse
+
+
+# ---------------------------------------------------------------- vision (ViT)
+def vit_layout(h: int, w: int):
+    """(row [h*w], col [h*w], col_order [h*w]) int32 for an h x w patch grid
+    in merge-unit order (colibri "MiMo-V2.6 (Xiaomi)", the "vision" entry:
+    row and column order of the 2x2 merge units)."""
+    n = h * w
+    row, col, co = (np.empty(n, np.int32) for _ in range(3))
+    rc = _load().hswo_vit_layout(int(h), int(w), _p(row), _p(col), _p(co))
+    if rc != 0:
+        raise ValueError("oracle vit_layout: h and w must be positive and even")
+    return row, col, co
+
+
+def rope_2d(x, row, col, theta: float = 1e4) -> np.ndarray:
+    """2D rotate-half RoPE of x [T, H, D] at patch coordinates (row, col)
+    (colibri, the "vision" entry: 2D RoPE)."""
+    x = _f64(x)
+    T, H, D = x.shape
+    row = np.ascontiguousarray(row, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    assert row.shape == (T,) and col.shape == (T,)
+    y = np.empty_like(x)
+    _load().hswo_rope_2d(T, H, D, float(theta), _p(row), _p(col), _p(x), _p(y))
+    return y
+
+
+def vit_attn(q, k, v, cu, *, window: int, tau: float, order=None, sink_key: bool = False,
+             sinks=None) -> np.ndarray:
+    """ViT attention over pictures packed by cu (bidirectional; window 0 =
+    the whole picture, else windows of `window` tokens in the order given,
+    plus the picture's first token in that order as a sink key).  colibri
+    "MiMo-V2.6 (Xiaomi)", the "vision" entry."""
+    q, k, v, cu = _f64(q), _f64(k), _f64(v), _i64(cu)
+    T, hq, d = q.shape
+    _, hkv, _ = k.shape
+    dv = v.shape[2]
+    od = None if order is None else np.ascontiguousarray(order, dtype=np.int32)
+    s = None if sinks is None else _f64(sinks)
+    o = np.empty((T, hq, dv), np.float64)
+    rc = _load().hswo_vit_attn(len(cu) - 1, _p(cu), _p(od), int(window), int(bool(sink_key)),
+                               hq, hkv, d, dv, float(tau), _p(s), _p(q), _p(k), _p(v), _p(o))
+    if rc != 0:
+        raise ValueError("oracle vit_attn: rc=%d" % rc)
+    return o

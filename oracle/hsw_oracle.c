@@ -333,3 +333,147 @@ void hswo_lse_merge(int64_t n_parts, int64_t n, int dv, const double *m,
         if (lse) lse[i] = M + log(z);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Vision encoder (ViT) attention.  colibri "MiMo-V2.6 (Xiaomi)", the model
+ * description's "vision" entry: 2D RoPE, grouped-query attention, full
+ * attention in 4 of 28 blocks and a 1D window of 64 tokens in the others,
+ * row and column order of the 2x2 merge units alternating, a sink on the
+ * first key of the window blocks; the same page ("Verifying it") has the
+ * gateway's patches equal to the Qwen2-VL processor's.
+ *
+ * Readings where the page is brief (each an explicit argument or stated
+ * here, never a hidden constant):
+ *  - a picture's tokens come in merge-unit order: the four patches of a 2x2
+ *    unit consecutive (top-left, top-right, bottom-left, bottom-right), units
+ *    row by row over the (h/2) x (w/2) unit grid (the Qwen2-VL processor's
+ *    order);
+ *  - "row order" of a window block is that order; "column order" takes the
+ *    units column by column (each unit's four patches still consecutive);
+ *  - attention is bidirectional within one picture; a window block cuts the
+ *    picture's tokens, in the block's order, into consecutive windows of
+ *    `window` tokens (the last may be shorter) and a token attends to its
+ *    window;
+ *  - the sink is a real key: the picture's first token in the block's order,
+ *    seen by every window (once: the first window already holds it); a
+ *    learned per-head sink logit (denominator only, as on the text model's
+ *    windowed layers) may be given as well;
+ *  - 2D RoPE is rotate-half over the whole head: pair (i, i + d/2), i < d/2,
+ *    turns by row * f(i) for i < d/4 and col * f(i - d/4) above, with
+ *    f(j) = theta^(-j / (d/4)) (the frequencies a 1D rotary of width d/2
+ *    uses).
+ * ------------------------------------------------------------------------ */
+
+/* Patch coordinates of each token of an h x w patch grid (h, w even) in
+ * merge-unit order, and the column-order permutation: col_order[j] is the
+ * token at position j of the column order. */
+int hswo_vit_layout(int h, int w, int32_t *row, int32_t *col, int32_t *col_order) {
+    if (h <= 0 || w <= 0 || h % 2 || w % 2) return HSWO_E_ARG;
+    int uh = h / 2, uw = w / 2;
+    for (int t = 0; t < h * w; ++t) {
+        int u = t / 4, e = t % 4;
+        row[t] = 2 * (u / uw) + e / 2;
+        col[t] = 2 * (u % uw) + e % 2;
+    }
+    for (int j = 0; j < h * w; ++j) {
+        int uc = j / 4;                      /* unit index in column order */
+        int ur = uc % uh, ucl = uc / uh;     /* its unit row and column */
+        col_order[j] = 4 * (ur * uw + ucl) + j % 4;
+    }
+    return HSWO_OK;
+}
+
+/* 2D rotate-half RoPE of x [n_tok][n_heads][d] at patch coordinates
+ * (row[t], col[t]); angles and products in fp64 (reading above). */
+void hswo_rope_2d(int64_t n_tok, int n_heads, int d, double theta,
+                  const int32_t *row, const int32_t *col, const double *x,
+                  double *y) {
+    int half = d / 2, quarter = d / 4;
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        for (int h = 0; h < n_heads; ++h) {
+            const double *xr = x + (t * n_heads + h) * (int64_t)d;
+            double *yr = y + (t * n_heads + h) * (int64_t)d;
+            for (int i = 0; i < half; ++i) {
+                int f = i < quarter ? i : i - quarter;
+                double coord = i < quarter ? (double)row[t] : (double)col[t];
+                double a = coord * pow(theta, -(double)f / (double)quarter);
+                double c = cos(a), s = sin(a);
+                yr[i] = xr[i] * c - xr[i + half] * s;
+                yr[i + half] = xr[i + half] * c + xr[i] * s;
+            }
+            for (int e = 2 * half; e < d; ++e) yr[e] = xr[e];
+        }
+    }
+}
+
+/* ViT attention over n_img pictures packed by cu[0..n_img] (token rows).
+ *   q [T][Hq][d], k [T][Hkv][d], v [T][Hkv][dv], o [T][Hq][dv]
+ *   order: NULL (row order) or per picture a permutation, order[cu[s] + j] =
+ *          the picture-local token at position j of the block's order
+ *   window 0: every token of the picture; window W > 0: the W-token window
+ *          of the token's position in the order, plus (sink_key != 0) the
+ *          token at order position 0 when it is not in that window
+ *   sinks [Hq] or NULL: learned sink logits (denominator only)
+ * Returns HSWO_E_ARG on inconsistent sizes or an order entry out of range. */
+int hswo_vit_attn(int n_img, const int64_t *cu, const int32_t *order, int window,
+                  int sink_key, int hq, int hkv, int d, int dv, double tau,
+                  const double *sinks, const double *q, const double *k,
+                  const double *v, double *o) {
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || window < 0) return HSWO_E_ARG;
+    int group = hq / hkv;
+    int64_t maxlen = 1;
+    for (int s = 0; s < n_img; ++s) {
+        int64_t n = cu[s + 1] - cu[s];
+        if (n < 0) return HSWO_E_ARG;
+        if (n > maxlen) maxlen = n;
+        if (order)
+            for (int64_t j = 0; j < n; ++j)
+                if (order[cu[s] + j] < 0 || order[cu[s] + j] >= n) return HSWO_E_ARG;
+    }
+    int err = HSWO_OK;
+    for (int s = 0; s < n_img; ++s) {
+        int64_t base = cu[s], n = cu[s + 1] - cu[s];
+        #pragma omp parallel
+        {
+            double *logit = (double *)malloc(sizeof(double) * (maxlen + 1));
+            const double **kr = (const double **)malloc(sizeof(double *) * (maxlen + 1));
+            const double **vr = (const double **)malloc(sizeof(double *) * (maxlen + 1));
+            if (!logit || !kr || !vr) {
+                #pragma omp atomic write
+                err = HSWO_E_ARG;
+            } else {
+                #pragma omp for schedule(dynamic, 4)
+                for (int64_t jh = 0; jh < n * hq; ++jh) {
+                    int64_t j = jh / hq;                 /* position in the order */
+                    int h = (int)(jh % hq), g = h / group;
+                    int64_t t = base + (order ? order[base + j] : j);   /* the token's row */
+                    int64_t lo = 0, hi = n, nk = 0;
+                    if (window > 0) {
+                        lo = (j / window) * window;
+                        hi = lo + window < n ? lo + window : n;
+                        if (sink_key && lo > 0) {
+                            int64_t r0 = base + (order ? order[base] : 0);
+                            kr[nk] = k + (r0 * hkv + g) * (int64_t)d;
+                            vr[nk] = v + (r0 * hkv + g) * (int64_t)dv;
+                            ++nk;
+                        }
+                    }
+                    for (int64_t jj = lo; jj < hi; ++jj) {
+                        int64_t r = base + (order ? order[base + jj] : jj);
+                        kr[nk] = k + (r * hkv + g) * (int64_t)d;
+                        vr[nk] = v + (r * hkv + g) * (int64_t)dv;
+                        ++nk;
+                    }
+                    attend_row(d, dv, tau, 1.0, sinks != NULL, sinks ? sinks[h] : 0.0,
+                               q + (t * hq + h) * (int64_t)d, nk, kr, vr, logit,
+                               o + (t * hq + h) * (int64_t)dv, NULL);
+                }
+            }
+            free(logit);
+            free(kr);
+            free(vr);
+        }
+    }
+    return err;
+}

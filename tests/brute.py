@@ -65,3 +65,54 @@ def attention(q, qpos, k, v, kpos, *, window, tau, lam, sinks=None):
         vals = np.concatenate([np.zeros((1, vx.shape[2])), vx[:, h, :]], axis=0)
         out[:, h, :] = w @ vals
     return out
+
+
+# ---------------------------------------------------------------- vision (ViT)
+# The ViT step in another formulation (colibri "MiMo-V2.6 (Xiaomi)", the
+# "vision" entry): 2D RoPE as complex multiplication with one frequency table
+# per axis; the window blocks as a [T, T] boolean mask built from each
+# token's position in the block's order.
+def rope2d_complex(x: np.ndarray, row: np.ndarray, col: np.ndarray, theta: float) -> np.ndarray:
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    half, quarter = d // 2, d // 4
+    f = theta ** (-np.arange(quarter, dtype=np.float64) / quarter)
+    ang = np.concatenate([np.asarray(row, np.float64)[:, None] * f[None, :],
+                          np.asarray(col, np.float64)[:, None] * f[None, :]], axis=1)   # [T, half]
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * ang)[:, None, :]
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def vit_mask(n: int, window: int, order=None, sink_key: bool = False) -> np.ndarray:
+    """allowed[i, j] for picture-local tokens i (query) and j (key)."""
+    order = np.arange(n) if order is None else np.asarray(order)
+    where = np.empty(n, np.int64)
+    where[order] = np.arange(n)           # token -> its position in the order
+    if window == 0:
+        return np.ones((n, n), bool)
+    allowed = (where[:, None] // window) == (where[None, :] // window)
+    if sink_key:
+        allowed |= (where[None, :] == 0)
+    return allowed
+
+
+def vit_attention_masked(q, k, v, allowed, tau, sinks=None):
+    """Softmax attention of one picture under a [T, T] mask, GQA by explicit
+    repetition, the learned sink as an extra logit column with a zero value."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    T, hq, _ = q.shape
+    hkv = k.shape[1]
+    kk = np.repeat(k, hq // hkv, axis=1)
+    vv = np.repeat(v, hq // hkv, axis=1)
+    out = np.empty((T, hq, v.shape[2]))
+    for h in range(hq):
+        s = tau * q[:, h, :] @ kk[:, h, :].T
+        s = np.where(allowed, s, -np.inf)
+        if sinks is not None:
+            s = np.concatenate([np.full((T, 1), sinks[h]), s], axis=1)
+            vals = np.concatenate([np.zeros((1, v.shape[2])), vv[:, h, :]], axis=0)
+        else:
+            vals = vv[:, h, :]
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (p / p.sum(axis=1, keepdims=True)) @ vals
+    return out
