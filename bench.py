@@ -376,6 +376,76 @@ def bench_kvm_snapshot(hsw, wl, steps, stream, model=None):
                          f"(192 + 128) bf16 ({sb / 1e6:.1f} MB each way)")
 
 
+def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
+    """Vision-encoder attention on 16 pictures of 64 x 64 patches (65536
+    tokens, 16 q / 4 KV heads of width 64): a window block (column order of
+    the merge units, the sink key), a full block, and the 2D RoPE of q and k.
+    Two replicas of the inputs alternate, so the 0.34 GB a window block
+    moves is read from HBM rather than the 256 MB Infinity Cache."""
+    grids = wl.VIT_BENCH_GRIDS
+    lens = [h * w for h, w in grids]
+    T, S, hq, hkv = sum(lens), len(grids), 16, 4
+    order = np.concatenate([hsw.hsw_vit_layout(h, w)[2] for h, w in grids]).astype(np.int32)
+    rowcol = [np.concatenate([hsw.hsw_vit_layout(h, w)[i] for h, w in grids]) for i in (0, 1)]
+    d_order = torch.from_numpy(order).to(DEV)
+    d_row, d_col = (torch.from_numpy(x).to(DEV) for x in rowcol)
+    reps = []
+    for r in range(2):
+        b = wl.vit_batch(seed=40 + r, grids=grids, device=DEV)
+        b["out"] = torch.empty((T, hq, 64), dtype=torch.bfloat16, device=DEV)
+        b["qr"], b["kr"] = torch.empty_like(b["q"]), torch.empty_like(b["k"])
+        b["cu"] = b["cu_seqlens"].to(DEV)
+        reps.append(b)
+    win, full = wl.vit_shape(hq, hkv, 64), wl.vit_shape(hq, hkv, 0)
+    maxlen = max(lens)
+
+    def window_call(i):
+        b = reps[i % 2]
+        hsw.hsw_vit_attention(win, S, maxlen, b["cu"], d_order, 1, b["q"], b["k"], b["v"], None, b["out"], stream)
+
+    def full_call(i):
+        b = reps[i % 2]
+        hsw.hsw_vit_attention(full, S, maxlen, b["cu"], None, 0, b["q"], b["k"], b["v"], None, b["out"], stream)
+
+    def rope_call(i):
+        b = reps[i % 2]
+        hsw.hsw_vit_rope_2d(win, T, b["q"], b["k"], d_row, d_col, b["qr"], b["kr"], stream)
+    res = {"window": float("nan"), "full": float("nan"), "rope": float("nan")}
+    for name, fn, n in (("window", window_call, max(steps, 20) * 2), ("full", full_call, max(steps // 5, 4)),
+                        ("rope", rope_call, max(steps, 20) * 2)):
+        if name not in parts:
+            continue
+        fn(0)
+        fn(1)
+        warm(fn, stream)
+        res[name] = ev_time(fn, n, stream)
+    # algorithmic bytes / flops
+    tok_bytes = (2 * hq * 64 + 2 * hkv * 64) * 2            # q, out; k, v (bf16)
+    win_pairs = 0
+    for n in lens:
+        for lo in range(0, n, 64):
+            nw = min(64, n - lo)
+            win_pairs += nw * (nw + (1 if lo > 0 else 0))
+    full_pairs = sum(n * n for n in lens)
+    win_bytes = T * tok_bytes
+    win_flops = win_pairs * hq * 64 * 4
+    full_flops = full_pairs * hq * 64 * 4
+    rope_bytes = T * (hq + hkv) * 64 * 2 * 2
+    del reps
+    return dict(window=dict(ms=res["window"], bytes=win_bytes, gbs=win_bytes / res["window"] / 1e6,
+                            frac_hbm_peak=win_bytes / res["window"] / 1e6 / HBM_PEAK_GBS,
+                            tflops=win_flops / res["window"] / 1e9,
+                            workload="window block: 64-token windows in column order of the merge units + "
+                                     "the sink key"),
+                full=dict(ms=res["full"], flops=full_flops, tflops=full_flops / res["full"] / 1e9,
+                          frac_mfma_peak=full_flops / res["full"] / 1e9 / BF16_PEAK_TFLOPS,
+                          workload="full block: every picture attends to itself"),
+                rope=dict(ms=res["rope"], bytes=rope_bytes, gbs=rope_bytes / res["rope"] / 1e6,
+                          workload="2D RoPE of q and k"),
+                workload=f"vision encoder, {S} pictures of 64 x 64 patches ({T} tokens), {hq} q / {hkv} KV "
+                         "heads of width 64")
+
+
 def _snap_cycle(kv, seq, stream):
     kv.drop_snapshot(kv.snapshot(seq, stream))
 
@@ -489,9 +559,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="only the two metric calls")
     ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid", "copy",
-                                       "kvm_snapshot"],
+                                       "kvm_snapshot", "vit"],
                     help="run one call's timing only (for profiling) and print its numbers")
     ap.add_argument("--model", choices=["flash", "pro"], default="flash", help="shapes for --only")
+    ap.add_argument("--vit-part", choices=["all", "window", "full", "rope"], default="all",
+                    help="with --only vit: time one of the vision-encoder calls only (for profiling)")
     ap.add_argument("--no-pro", action="store_true", help="skip the MiMo-V2.6-Pro section")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -511,10 +583,14 @@ def main():
               "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream, m),
               "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m),
               "copy": lambda: bench_copy(args.steps, stream),
-              "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m)}[args.only]
+              "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m),
+              "vit": lambda: bench_vit(hsw, wl, args.steps, stream,
+                                       ("window", "full", "rope") if args.vit_part == "all" else (args.vit_part,))}[
+            args.only]
         r = fn()
         print(json.dumps({"only": args.only, "model": m.name,
-                          **{k: v for k, v in r.items() if not isinstance(v, dict) or k == "fused"}}))
+                          **{k: v for k, v in r.items() if not isinstance(v, dict) or k in ("fused", "window", "full",
+                                                                                            "rope")}}))
         return
 
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
@@ -548,6 +624,12 @@ def main():
         print(f"[bench] kvm snapshot {snap['ms'] * 1e3:.1f} us restore {snap['restore_ms'] * 1e3:.1f} us "
               f"({snap['gbs']:.0f} / {snap['restore_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
         calls["kvm_snapshot"] = snap
+        torch.cuda.empty_cache()
+        vit = bench_vit(hsw, wl, args.steps, stream)
+        print(f"[bench] vit window {vit['window']['ms'] * 1e3:.1f} us {vit['window']['gbs']:.0f} GB/s; full "
+              f"{vit['full']['ms']:.3f} ms {vit['full']['tflops']:.1f} TFLOP/s; rope {vit['rope']['ms'] * 1e3:.1f} us "
+              f"{vit['rope']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        calls["vit"] = vit
         torch.cuda.empty_cache()
         hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream)
         print(f"[bench] hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "

@@ -396,4 +396,76 @@ int64_t hsw_kv_bytes(int32_t kind, int64_t n_seqs, int64_t ctx, int32_t window, 
     return (int64_t)n_layers * n_seqs * positions * n_kv_heads * (int64_t)(d_qk + d_v_stored) * elem_bytes;
 }
 
+// ------------------------------------------------------------------ vision
+hsw_status hsw_vit_layout(int32_t h, int32_t w, int32_t *row, int32_t *col, int32_t *col_order) {
+    if (h <= 0 || w <= 0 || h % 2 || w % 2 || (int64_t)h * w > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "h (%d) and w (%d) must be positive and even, h * w < 2^31", h, w);
+    const int uh = h / 2, uw = w / 2;
+    const int n = h * w;
+    for (int t = 0; t < n; ++t) {
+        const int u = t >> 2, e = t & 3;
+        if (row) row[t] = 2 * (u / uw) + (e >> 1);
+        if (col) col[t] = 2 * (u % uw) + (e & 1);
+        if (col_order) {
+            const int uc = t >> 2;  // position t of the column order: unit uc taken column by column
+            col_order[t] = 4 * ((uc % uh) * uw + uc / uh) + e;
+        }
+    }
+    return HSW_OK;
+}
+
+hsw_status hsw_vit_rope_2d(const hsw_attn_shape *sh, int64_t n_tokens, const void *q, const void *k,
+                           const int32_t *row, const int32_t *col, void *q_out, void *k_out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, -1);
+    if (st) return st;
+    if (sh->dtype != HSW_BF16) return fail(HSW_E_DTYPE, "vit_rope_2d takes bf16 q and k");
+    if (sh->d_qk % 32 != 0 || sh->d_qk > 128 || sh->rope_dim != sh->d_qk)
+        return fail(HSW_E_SHAPE, "vit_rope_2d rotates whole heads: d_qk (%d) a multiple of 32, <= 128, "
+                                 "rope_dim == d_qk (is %d)", sh->d_qk, sh->rope_dim);
+    if (n_tokens < 0) return fail(HSW_E_SHAPE, "n_tokens must be >= 0");
+    if (!q != !q_out) return fail(HSW_E_NULL, "q and q_out must both be given or both be NULL");
+    if (!k != !k_out) return fail(HSW_E_NULL, "k and k_out must both be given or both be NULL");
+    if (!q && !k) return fail(HSW_E_NULL, "neither q nor k is given");
+    REQUIRE_PTR(row); REQUIRE_PTR(col);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(q_out, 16); REQUIRE_ALIGN(k_out, 16);
+    REQUIRE_ALIGN(row, 4); REQUIRE_ALIGN(col, 4);
+    if (n_tokens == 0) return HSW_OK;
+    const int64_t per_tok = (int64_t)((q ? sh->n_q_heads : 0) + (k ? sh->n_kv_heads : 0)) * (sh->d_qk / 16);
+    if (n_tokens * per_tok / 256 + 1 > 0x7fffffffLL) return fail(HSW_E_SHAPE, "grid too large");
+    hsw::VitRopeArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.q_out = q_out; a.k_out = k_out; a.row = row; a.col = col;
+    a.n_tokens = n_tokens; a.hq = sh->n_q_heads; a.hkv = sh->n_kv_heads; a.d = sh->d_qk;
+    const int quarter = sh->d_qk / 4;
+    for (int j = 0; j < quarter; ++j) a.inv_freq[j] = pow(sh->rope_theta, -(double)j / (double)quarter);
+    return launched(hsw::launch_vit_rope(a, (hipStream_t)stream), "vit_rope_2d");
+}
+
+hsw_status hsw_vit_attention(const hsw_attn_shape *sh, int32_t n_images, int64_t max_len,
+                             const int64_t *cu_seqlens, const int32_t *order, int32_t sink_key, const void *q,
+                             const void *k, const void *v, const float *sinks, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, -1);
+    if (st) return st;
+    hsw::VitArgs a;
+    memset(&a, 0, sizeof a);
+    a.hq = sh->n_q_heads; a.hkv = sh->n_kv_heads; a.window = sh->window; a.sink_key = sink_key ? 1 : 0;
+    a.scale = sh->softmax_scale;
+    if (!hsw::vit_attn_ok(a, sh->d_qk, sh->d_v, sh->dtype, sh->out_dtype))
+        return fail(HSW_E_SHAPE, "vit_attention needs bf16 in and out, d_qk = d_v = 64, window 0 or 64 and "
+                                 "1, 2, 4, 8 or 16 query heads per KV head");
+    if (sh->value_scale != 1.0f) return fail(HSW_E_SHAPE, "vit_attention has no value scale (must be 1)");
+    if (n_images < 0 || max_len < 0) return fail(HSW_E_SHAPE, "n_images and max_len must be >= 0");
+    if (max_len > 0x7fffffffLL) return fail(HSW_E_SHAPE, "max_len exceeds 2^31 - 1");
+    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(out, 16);
+    REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(order, 4); REQUIRE_ALIGN(sinks, 4);
+    if (n_images == 0 || max_len == 0) return HSW_OK;
+    const int BQ = hsw::vit_block_tokens(sh->n_q_heads / sh->n_kv_heads);
+    if ((int64_t)n_images * sh->n_kv_heads * ((max_len + BQ - 1) / BQ) > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "grid too large");
+    a.q = q; a.k = k; a.v = v; a.out = out; a.cu_seqlens = cu_seqlens; a.order = order; a.sinks = sinks;
+    a.n_images = n_images;
+    return launched(hsw::launch_vit_attn(a, max_len, (hipStream_t)stream), "vit_attention");
+}
+
 }  // extern "C"

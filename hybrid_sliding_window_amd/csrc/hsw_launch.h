@@ -61,6 +61,29 @@ struct RingCopyArgs {
 };
 hipError_t launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 
+// Vision-encoder attention (vit.hip).
+struct VitArgs {
+    const void *q, *k, *v;
+    const int64_t *cu_seqlens;  // [n_images + 1]
+    const int32_t *order;       // picture-local token at each position of the order, or null
+    const float *sinks;         // learned sink logits [Hq], or null
+    void *out;
+    int n_images, hq, hkv, window, sink_key;
+    float scale;
+};
+struct VitRopeArgs {
+    const void *q, *k;          // either may be null (then not rotated)
+    void *q_out, *k_out;
+    const int32_t *row, *col;
+    int64_t n_tokens;
+    int hq, hkv, d;
+    double inv_freq[32];        // theta^(-j / (d/4)), j < d/4
+};
+bool vit_attn_ok(const VitArgs &a, int d_qk, int d_v, int dtype, int out_dtype);
+int vit_block_tokens(int G);
+hipError_t launch_vit_attn(const VitArgs &a, int64_t max_len, hipStream_t s);
+hipError_t launch_vit_rope(const VitRopeArgs &a, hipStream_t s);
+
 hipError_t launch_rope(const RopeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_generic_attn(const AttnArgs &a, int dtype, int out_dtype, hipStream_t s);
 hipError_t launch_ring_commit(const AttnArgs &a, int dtype, hipStream_t s);

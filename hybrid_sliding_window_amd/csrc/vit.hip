@@ -1,0 +1,385 @@
+// vit.hip -- attention of the vision encoder (ViT): 2D RoPE and
+// bidirectional attention over whole pictures or 64-token windows with a
+// sink key (bf16 storage, MFMA).
+//
+// colibri "MiMo-V2.6 (Xiaomi)", the model description's "vision" entry: 2D
+// RoPE, grouped-query attention, full attention in 4 of 28 blocks and a 1D
+// window of 64 tokens in the others, row and column order of the 2x2 merge
+// units alternating, a sink on the first key of the window blocks.  Read
+// here as: a picture's tokens come in merge-unit order; a window block takes
+// the tokens in its order (row order = that order, or an index array such
+// as the column order of the units), cuts them into consecutive windows of
+// 64 and lets each token attend to its window plus the picture's first
+// token in that order (the sink key); a full block attends to the whole
+// picture; pictures never see each other.  2D RoPE is rotate-half over the
+// whole head: pair (i, i + d/2) turns by row * f(i) for i < d/4 and by
+// col * f(i - d/4) above, f(j) = theta^(-j / (d/4)).
+//
+// Attention: one workgroup per (picture, KV head, query block); a block's
+// 32 * waves rows are (rows / G) tokens x the G query heads of the KV head
+// (heads are the 16-wide MFMA columns, two column tiles per wave), all in one
+// window.  Keys stream through LDS 64 at a time (one chunk for a window, the
+// whole picture for a full block, double-buffered through registers):
+//   S^T = K Q^T      v_mfma_f32_16x16x32_bf16 (K from LDS in fragment order)
+//   softmax          online in log2 units, the reference max raised only when
+//                    a chunk's max exceeds it by more than 2^8
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P as bf16 hi + lo, V^T
+//                    read from row-major V fragments by ds_read_b64_tr_b16.
+// The sink key is a fifth 16-key tile (its first row; the rest zero and
+// masked) and a third PV step, only in windows after the first.  Queries and
+// keys are fetched through the order array, so a block in column order reads
+// its rows where they are: no permuted copy of q, k, v or the output.
+#include "hsw_device.h"
+#include "hsw_launch.h"
+
+namespace hsw {
+namespace {
+
+constexpr int D = 64;                 // q, k and v head width
+constexpr int STEPS = D / 32;         // k-steps of the S^T product
+constexpr int DT = D / 16;            // output tiles of the O^T product
+constexpr int KC = 64;                // keys per chunk (= the window)
+constexpr int K_TILES = KC / 16 + 1;  // + the sink tile
+constexpr int V_HALVES = KC / 16 + 2; // + the sink PV step (two 16-key halves)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float quad_max_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float quad_sum_swap(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+// Consecutive blocks of one (picture, KV head) on one XCD, so the blocks that
+// read the same keys share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int full = (total / 8) * 8;
+    if (bid >= full) return bid;
+    return (bid % 8) * (total / 8) + bid / 8;
+}
+
+// ---------------------------------------------------------------- 2D RoPE
+// One thread per (token, head, 8-dim piece of the first half): dims
+// 8p .. 8p+7 and their partners d/2 + 8p .. (a piece never straddles d/4).
+__global__ __launch_bounds__(256) void vit_rope_kernel(VitRopeArgs a) {
+    const int pieces = a.d / 16;
+    const int nhq = a.q ? a.hq : 0, nhk = a.k ? a.hkv : 0;
+    const int64_t per_tok = (int64_t)(nhq + nhk) * pieces;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= a.n_tokens * per_tok) return;
+    const int64_t t = idx / per_tok;
+    const int rem = (int)(idx % per_tok);
+    const int h = rem / pieces, p = rem % pieces;
+    const uint16_t *x;
+    uint16_t *y;
+    if (h < nhq) {
+        x = (const uint16_t *)a.q + (t * a.hq + h) * (int64_t)a.d;
+        y = (uint16_t *)a.q_out + (t * a.hq + h) * (int64_t)a.d;
+    } else {
+        x = (const uint16_t *)a.k + (t * a.hkv + (h - nhq)) * (int64_t)a.d;
+        y = (uint16_t *)a.k_out + (t * a.hkv + (h - nhq)) * (int64_t)a.d;
+    }
+    const int half = a.d / 2, quarter = a.d / 4;
+    u32x4 lo = ld16(x + 8 * p), hi = ld16(x + half + 8 * p);
+    const bool by_row = 8 * p < quarter;
+    const int64_t coord = by_row ? a.row[t] : a.col[t];
+    const int f0 = by_row ? 8 * p : 8 * p - quarter;
+    float c[8], s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_cos_sin(coord, a.inv_freq[f0 + e], c[e], s[e]);
+    rope_rotate_bf16x8(lo, hi, c, s);
+    st16(y + 8 * p, lo);
+    st16(y + half + 8 * p, hi);
+}
+
+// -------------------------------------------------------------- attention
+template <int G>
+__global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs a, int nqb) {
+    constexpr int NW = G == 1 ? 2 : 4;        // waves: 64 tokens per block at G = 1
+    constexpr int NT = NW * 64;
+    constexpr int BQ = 32 * NW / G;           // tokens per block; divides 64
+    constexpr int PIECES = KC * D / 8;        // 16-byte pieces of one K (or V) chunk
+    constexpr int LOADS = PIECES / NT;        // per thread and tensor
+    static_assert(64 % BQ == 0 && PIECES % NT == 0, "block shape");
+    // Two stages; a stage holds K in MFMA fragment order (16-byte unit
+    // (h * STEPS + st) * 64 + lane = K[16h + lane % 16][32st + 8 (lane / 16) ..])
+    // and V in transposing-read order (8-byte unit (hh * DT + dt) * 64 + 16q +
+    // 4k + m = V[16hh + 4q + k][16dt + 4m .. +3]): every read is one
+    // contiguous run in lane order.
+    __shared__ __attribute__((aligned(1024))) uint16_t ks[2][K_TILES * 16 * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs[2][V_HALVES * 16 * D];
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int quad = lane >> 4, col = lane & 15;
+    const int total = a.n_images * a.hkv * nqb;
+    const int bid = xcd_remap((int)__builtin_amdgcn_workgroup_id_x(), total);
+    const int qb = bid % nqb;
+    const int g = (bid / nqb) % a.hkv;
+    const int s = bid / (nqb * a.hkv);
+
+    const int64_t tok0 = a.cu_seqlens[s];
+    const int len = (int)(a.cu_seqlens[s + 1] - tok0);
+    if (qb * BQ >= len) return;
+    const int32_t *ord = a.order ? a.order + tok0 : nullptr;
+    // token row at position j of the block's order (entries clamped into the
+    // picture, so a bad index array reads wrong rows but never out of bounds)
+    auto row_of = [&](int j) -> int64_t {
+        const int t = ord ? min(max(ord[j], 0), len - 1) : j;
+        return tok0 + t;
+    };
+    const bool windowed = a.window > 0;
+    const int klo = windowed ? (qb * BQ / KC) * KC : 0;
+    const int khi = windowed ? min(len, klo + KC) : len;
+    const bool has_sink = windowed && a.sink_key && klo > 0;
+    const int nch = (khi - klo + KC - 1) / KC;
+
+    // q of this wave's rows: row r = 32w + 16n + col is token qb*BQ + r/G,
+    // head g*G + r%G (rows past the picture read its last token, never stored)
+    u32x4 qv[2][STEPS];
+    const uint16_t *qg = (const uint16_t *)a.q;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int r = 32 * w + 16 * n + col;
+        const int j = min(qb * BQ + r / G, len - 1);
+        const uint16_t *qrow = qg + (row_of(j) * a.hq + g * G + r % G) * (int64_t)D;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+    }
+
+    const uint16_t *kg = (const uint16_t *)a.k + g * D;
+    const uint16_t *vg = (const uint16_t *)a.v + g * D;
+    const int64_t rs = (int64_t)a.hkv * D;   // elements per token row of k / v
+
+    // Thread tid moves pieces pi = tid + NT i: key pi / 8, 16-byte piece pi % 8.
+    u32x4 kr[LOADS], vr[LOADS];
+    auto fetch = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int pi = tid + NT * i, key = pi >> 3, p = pi & 7;
+            const int64_t r = row_of(min(klo + c * KC + key, khi - 1));
+            kr[i] = ld16(kg + r * rs + 8 * p);
+            vr[i] = ld16(vg + r * rs + 8 * p);
+        }
+    };
+    auto put = [&](int stg) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int pi = tid + NT * i, key = pi >> 3, p = pi & 7;
+            const int ku = ((key >> 4) * STEPS + (p >> 2)) * 64 + 16 * (p & 3) + (key & 15);
+            *reinterpret_cast<u32x4 *>(&ks[stg][ku * 8]) = kr[i];
+            const int vu = ((key >> 4) * DT + (p >> 1)) * 64 + 16 * ((key & 15) >> 2) + 4 * (key & 3) + 2 * (p & 1);
+            *reinterpret_cast<u32x4 *>(&vs[stg][vu * 4]) = vr[i];
+        }
+    };
+
+    if (has_sink) {
+        // the sink tile: key slot 64 = the picture's first token in the
+        // block's order; slots 65..79 (K) and 65..95 (V) zero
+        const int64_t r0 = row_of(0);
+        for (int pi = tid; pi < 32 * 8; pi += NT) {
+            const int kk = pi >> 3, p = pi & 7;
+            const u32x4 z = u32x4{0, 0, 0, 0};
+            if (kk < 16) {
+                const int key = KC + kk;
+                const int ku = ((key >> 4) * STEPS + (p >> 2)) * 64 + 16 * (p & 3) + (key & 15);
+                *reinterpret_cast<u32x4 *>(&ks[0][ku * 8]) = kk == 0 ? ld16(kg + r0 * rs + 8 * p) : z;
+            }
+            const int key = KC + kk;
+            const int vu = ((key >> 4) * DT + (p >> 1)) * 64 + 16 * ((key & 15) >> 2) + 4 * (key & 3) + 2 * (p & 1);
+            *reinterpret_cast<u32x4 *>(&vs[0][vu * 4]) = kk == 0 ? ld16(vg + r0 * rs + 8 * p) : z;
+        }
+    }
+    fetch(0);
+    put(0);
+    __syncthreads();
+
+    const float scale2 = a.scale * kLog2e;
+    f32x4 oacc[2][DT];
+    float m[2], l[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        m[n] = -INFINITY;
+        l[n] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
+    }
+
+    auto compute = [&](int stg, int c, bool sink) {
+        const uint16_t *ksc = ks[stg];
+        const uint16_t *vsc = vs[stg];
+        const int nvalid = khi - (klo + c * KC);   // keys of this chunk in range (>= 1)
+        float sv[K_TILES][2][4];
+#pragma unroll
+        for (int h = 0; h < K_TILES; ++h) {
+            if (h == K_TILES - 1 && !sink) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][n][j] = -INFINITY;
+                continue;
+            }
+            u32x4 ak[STEPS];
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+                ak[st] = *reinterpret_cast<const u32x4 *>(ksc + ((h * STEPS + st) * 64 + lane) * 8);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st) acc = mfma_16x16x32_bf16(ak[st], qv[n][st], acc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = 16 * h + 4 * quad + j;
+                    const bool ok = h < K_TILES - 1 ? key < nvalid : key == KC;
+                    sv[h][n][j] = ok ? acc[j] : -INFINITY;
+                }
+            }
+        }
+        float pv[K_TILES + 1][2][4];   // + a zero half pairing with the sink tile
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float cm = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < K_TILES; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cm = fmaxf(cm, sv[h][n][j]);
+            cm = quad_max_swap(cm) * scale2;
+            const bool raise = cm > m[n] + kRescale;
+            if (__any(raise)) {
+                const float mn = raise ? cm : m[n];
+                if (__any(raise && m[n] != -INFINITY)) {
+                    const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
+                    l[n] *= f;
+                }
+                m[n] = mn;
+            }
+            const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
+#pragma unroll
+            for (int h = 0; h < K_TILES; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pv[h][n][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][n][j], scale2, mu));
+                    l[n] += pv[h][n][j];
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pv[K_TILES][n][j] = 0.0f;
+        }
+        // O^T += V^T P^T over 32-key steps: slots 0-3 of a quad are keys
+        // 4quad.. of the step's first 16-key half, slots 4-7 of its second
+        // half, on both operands.
+        const int nsteps = sink ? 3 : 2;
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+            if (s2 >= nsteps) break;
+            u32x4 ph[2], pl[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                u32x2 h0, l0, h1, l1;
+                split_hi_lo(pv[2 * s2][n], h0, l0);
+                split_hi_lo(pv[2 * s2 + 1][n], h1, l1);
+                ph[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+                pl[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
+                const u32x2 a1 = ds_read_tr16(vsc + (((2 * s2 + 1) * DT + dt) * 64 + lane) * 4);
+                const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    oacc[n][dt] = mfma_16x16x32_bf16(av, ph[n], oacc[n][dt]);
+                    oacc[n][dt] = mfma_16x16x32_bf16(av, pl[n], oacc[n][dt]);
+                }
+            }
+        }
+    };
+
+    if (has_sink) {
+        compute(0, 0, true);     // a window: one chunk
+    } else {
+        for (int c = 0; c < nch; ++c) {
+            const int stg = c & 1;
+            if (c + 1 < nch) fetch(c + 1);
+            compute(stg, c, false);
+            if (c + 1 < nch) put(stg ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: learned sink (if any) in the denominator, normalise, bf16.
+    uint16_t *og = (uint16_t *)a.out;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int r = 32 * w + 16 * n + col;
+        const int j = qb * BQ + r / G;
+        const int head = r % G;
+        float ll = quad_sum_swap(l[n]);
+        float fac = 1.0f;
+        if (a.sinks) {
+            const float sk = a.sinks[g * G + head] * kLog2e;
+            const float mf = fmaxf(m[n], sk);
+            fac = exp2f(m[n] - mf);
+            ll = ll * fac + exp2f(sk - mf);
+        }
+        const float sc = fac / ll;
+        if (j < len) {
+            uint16_t *orow = og + (row_of(j) * a.hq + g * G + head) * (int64_t)D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o = oacc[n][dt];
+                *reinterpret_cast<u32x2 *>(orow + 16 * dt + 4 * quad) =
+                    u32x2{pack_bf16x2(o[0] * sc, o[1] * sc), pack_bf16x2(o[2] * sc, o[3] * sc)};
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool vit_attn_ok(const VitArgs &a, int d_qk, int d_v, int dtype, int out_dtype) {
+    const int G = a.hq / a.hkv;
+    return dtype == 0 && out_dtype == 0 && d_qk == D && d_v == D && (a.window == 0 || a.window == KC) &&
+           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+int vit_block_tokens(int G) { return G == 1 ? 64 : 128 / G; }
+
+hipError_t launch_vit_attn(const VitArgs &a, int64_t max_len, hipStream_t s) {
+    const int G = a.hq / a.hkv;
+    const int BQ = vit_block_tokens(G);
+    const int nqb = (int)((max_len + BQ - 1) / BQ);
+    dim3 grid((unsigned)((int64_t)a.n_images * a.hkv * nqb));
+    switch (G) {
+        case 1: hipLaunchKernelGGL((vit_attn_kernel<1>), grid, dim3(128), 0, s, a, nqb); break;
+        case 2: hipLaunchKernelGGL((vit_attn_kernel<2>), grid, dim3(256), 0, s, a, nqb); break;
+        case 4: hipLaunchKernelGGL((vit_attn_kernel<4>), grid, dim3(256), 0, s, a, nqb); break;
+        case 8: hipLaunchKernelGGL((vit_attn_kernel<8>), grid, dim3(256), 0, s, a, nqb); break;
+        default: hipLaunchKernelGGL((vit_attn_kernel<16>), grid, dim3(256), 0, s, a, nqb); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_vit_rope(const VitRopeArgs &a, hipStream_t s) {
+    const int64_t per_tok = (int64_t)((a.q ? a.hq : 0) + (a.k ? a.hkv : 0)) * (a.d / 16);
+    const int64_t n = a.n_tokens * per_tok;
+    hipLaunchKernelGGL(vit_rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace hsw

@@ -74,6 +74,9 @@ def _load() -> ctypes.CDLL:
     lib.hsw_full_prefill_chunk_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
     lib.hsw_full_decode_splitk_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, SZ, P, P]
     lib.hsw_kv_bytes.argtypes = [I32, I64, I64, I32, I32, I32, I32, I32, I32]
+    lib.hsw_vit_layout.argtypes = [I32, I32, P, P, P]
+    lib.hsw_vit_rope_2d.argtypes = [SH, I64, P, P, P, P, P, P, P]
+    lib.hsw_vit_attention.argtypes = [SH, I32, I64, P, P, I32, P, P, P, P, P, P]
     lib.hsw_kv_bytes.restype = I64
     KC = ctypes.POINTER(KvmConfig)
     PI32, PI64, PP = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(P)
@@ -99,7 +102,8 @@ def _load() -> ctypes.CDLL:
         getattr(lib, f).restype = I32
     for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope",
               "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_prefill_chunk",
-              "hsw_full_decode_splitk_qrope", "hsw_full_prefill_chunk_qrope"):
+              "hsw_full_decode_splitk_qrope", "hsw_full_prefill_chunk_qrope", "hsw_vit_layout",
+              "hsw_vit_rope_2d", "hsw_vit_attention"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -113,7 +117,8 @@ EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_rope_partial
             "hsw_full_prefill_chunk_qrope", "hsw_kv_bytes",
             "hsw_kvm_snapshot_bytes", "hsw_kvm_create", "hsw_kvm_destroy", "hsw_kvm_admit", "hsw_kvm_release",
             "hsw_kvm_append", "hsw_kvm_truncate", "hsw_kvm_info", "hsw_kvm_free_space", "hsw_kvm_snapshot",
-            "hsw_kvm_restore", "hsw_kvm_drop_snapshot", "hsw_kvm_window_safe_length")
+            "hsw_kvm_restore", "hsw_kvm_drop_snapshot", "hsw_kvm_window_safe_length",
+            "hsw_vit_layout", "hsw_vit_rope_2d", "hsw_vit_attention")
 
 
 def _ptr(t):
@@ -311,3 +316,27 @@ class KvManager:
         if L < 0:
             raise HswError(2, "hsw_kvm_window_safe_length", lib.hsw_last_error().decode())
         return L, snap.value
+
+
+# ------------------------------------------------------------------ vision
+def hsw_vit_layout(h, w):
+    """(row, col, col_order) int32 numpy arrays of an h x w patch grid in
+    merge-unit order (host arithmetic in the library)."""
+    import numpy as np
+    n = int(h) * int(w)
+    row, col, co = (np.empty(max(n, 0), np.int32) for _ in range(3))
+    _check(lib.hsw_vit_layout(int(h), int(w), row.ctypes.data_as(ctypes.c_void_p), col.ctypes.data_as(ctypes.c_void_p),
+                              co.ctypes.data_as(ctypes.c_void_p)), "hsw_vit_layout")
+    return row, col, co
+
+
+def hsw_vit_rope_2d(shape, n_tokens, q, k, row, col, q_out, k_out, stream=None):
+    _check(lib.hsw_vit_rope_2d(_sh(shape), int(n_tokens), _ptr(q), _ptr(k), _ptr(row), _ptr(col),
+                               _ptr(q_out), _ptr(k_out), _stream(stream)), "hsw_vit_rope_2d")
+
+
+def hsw_vit_attention(shape, n_images, max_len, cu_seqlens, order, sink_key, q, k, v, sinks, out,
+                      stream=None):
+    _check(lib.hsw_vit_attention(_sh(shape), int(n_images), int(max_len), _ptr(cu_seqlens), _ptr(order),
+                                 int(sink_key), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out),
+                                 _stream(stream)), "hsw_vit_attention")

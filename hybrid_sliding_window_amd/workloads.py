@@ -253,3 +253,37 @@ def hybrid_pattern(seed=5, n_layers=48, n_full=9):
     for i in perm[:n_full].tolist():
         pat[i] = 0
     return pat
+
+
+# ------------------------------------------------------------------ vision
+# The vision encoder's attention (colibri "MiMo-V2.6 (Xiaomi)", the "vision"
+# entry).  The pages give no head sizes: 16 query / 4 KV heads of width 64
+# are used, softmax scale 1/8, RoPE theta 1e4.  Pictures are patch grids with
+# even sides (2x2 merge units); the page's own picture gives 252 merged rows,
+# i.e. 1008 patches, taken here as a 28 x 36 grid.  The token layout (patch
+# coordinates, unit orders) is method arithmetic and is not computed here.
+VIT_D, VIT_THETA = 64, 1.0e4
+VIT_PAGE_GRID = (28, 36)
+VIT_BENCH_GRIDS = ((64, 64),) * 16          # 16 pictures of 896 x 896 px at 14 px patches
+
+
+def vit_shape(hq=16, hkv=4, window=64):
+    return Shape(hq, hkv, window, VIT_THETA, d_qk=VIT_D, d_v=VIT_D, rope_dim=VIT_D,
+                 softmax_scale=1.0 / math.sqrt(VIT_D), value_scale=1.0)
+
+
+def vit_batch(seed=9, grids=(VIT_PAGE_GRID,), hq=16, hkv=4, q_scale=1.0, with_sinks=False, device="cpu"):
+    """Pictures packed by token rows: q [T, hq, 64], k, v [T, hkv, 64] bf16
+    (q optionally scaled by q_scale before rounding, for peaked attention),
+    cu_seqlens int64, the grids, and (with_sinks) sink logits ~ N(1, 0.25)."""
+    g = gen(seed)
+    lens = [h * w for h, w in grids]
+    T = sum(lens)
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0)
+    gd = gen(seed * 1000 + 1, device)
+    q = (torch.randn((T, hq, VIT_D), generator=gd, device=device) * q_scale).to(torch.bfloat16)
+    k = randn((T, hkv, VIT_D), gd, device=device)
+    v = randn((T, hkv, VIT_D), gd, device=device)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, grids=list(grids), lens=lens,
+                sinks=sinks(hq, g) if with_sinks else None)

@@ -389,6 +389,72 @@ hsw_status hsw_kvm_drop_snapshot(hsw_kvm *kvm, int32_t snap);
  * snapshot is needed.  Returns -1 on bad arguments. */
 int64_t hsw_kvm_window_safe_length(hsw_kvm *kvm, int32_t seq, const int32_t *tokens, int64_t n, int32_t *snap);
 
+/* ==================================================================
+ * Vision encoder (ViT) attention.
+ * colibri "MiMo-V2.6 (Xiaomi)", the model description's "vision" entry: 2D
+ * RoPE, grouped-query attention, full attention in 4 of 28 blocks and a 1D
+ * window of 64 tokens in the others, row and column order of the 2x2 merge
+ * units alternating, a sink on the first key of the window blocks; its
+ * "Verifying it": the gateway's patches equal the Qwen2-VL processor's.
+ * Readings: a picture's tokens come in merge-unit order (the 4 patches of a
+ * 2x2 unit consecutive: top-left, top-right, bottom-left, bottom-right;
+ * units row by row); attention is bidirectional within a picture; a window
+ * block cuts the picture's tokens, in its order, into consecutive windows of
+ * 64 (the last may be shorter) and each token attends to its window and to
+ * the sink key, the picture's first token in that order.
+ * ================================================================== */
+
+/*
+ * Host arithmetic (no device access): for an h x w patch grid (h, w > 0 and
+ * even) in merge-unit order, row[t] and col[t] are token t's patch
+ * coordinates and col_order[j] is the token at position j of the column
+ * order (units column by column, a unit's 4 patches still consecutive).
+ * Host arrays of h*w int32 each; any of them may be NULL (not written).
+ * HSW_E_SHAPE on a bad grid.
+ */
+hsw_status hsw_vit_layout(int32_t h, int32_t w, int32_t *row, int32_t *col, int32_t *col_order);
+
+/*
+ * 2D rotate-half RoPE of whole heads: pair (i, i + d/2), i < d/2, turns by
+ * row * f(i) for i < d/4 and by col * f(i - d/4) above, with
+ * f(j) = rope_theta^(-j / (d/4)) (the frequencies of a 1D rotary of width
+ * d/2; the angle formed and reduced in double, the rotation in fp32).
+ *   q [n_tokens][Hq][d], k [n_tokens][Hkv][d] bf16 (d = sh->d_qk, a multiple
+ *   of 32, <= 128; sh->rope_dim == d); row, col [n_tokens] int32 patch
+ *   coordinates (hsw_vit_layout); q_out, k_out like q, k (may equal them:
+ *   in place is allowed).  q and q_out both given or both NULL, likewise k
+ *   and k_out; at least one pair.
+ * Errors: HSW_E_NULL, HSW_E_SHAPE (d, rope_dim), HSW_E_DTYPE (not bf16),
+ * HSW_E_ALIGN.
+ */
+hsw_status hsw_vit_rope_2d(const hsw_attn_shape *sh, int64_t n_tokens, const void *q, const void *k,
+                           const int32_t *row, const int32_t *col, void *q_out, void *k_out,
+                           hsw_stream_t stream);
+
+/*
+ * ViT attention over n_images pictures packed by cu_seqlens [n_images + 1]
+ * (int64, token rows; picture s is rows cu[s] .. cu[s+1]-1, at most max_len
+ * long).  q [T][Hq][64], k, v [T][Hkv][64] bf16 (rotated q and k), out
+ * [T][Hq][64] bf16, all by token row.
+ *   sh->window == 0: every token attends to its whole picture (full block).
+ *   sh->window == 64: window block: the picture's tokens in the block's
+ *     order -- order[cu[s] + j] (int32, picture-local) is the token at
+ *     position j, or order == NULL for the tokens' own order -- cut into
+ *     consecutive 64-token windows; a token attends to its window and, if
+ *     sink_key != 0, to the token at position 0 of the order (once).
+ *   sinks [Hq] fp32 or NULL: learned sink logits, in the denominator only.
+ * softmax_scale multiplies q.k (1/8 for 64-wide heads); value_scale must be
+ * 1.  Supported: bf16 in and out, d_qk = d_v = 64, 1/2/4/8/16 query heads per
+ * KV head (HSW_E_SHAPE otherwise).  Every output row of a picture is
+ * written.  Order entries are not checked on the host; the kernel clamps
+ * them into the picture (wrong rows, never out-of-bounds accesses).
+ * Errors: HSW_E_NULL, HSW_E_SHAPE, HSW_E_ALIGN (q, k, v, out 16 B;
+ * cu_seqlens 8 B; order, sinks 4 B).
+ */
+hsw_status hsw_vit_attention(const hsw_attn_shape *sh, int32_t n_images, int64_t max_len,
+                             const int64_t *cu_seqlens, const int32_t *order, int32_t sink_key, const void *q,
+                             const void *k, const void *v, const float *sinks, void *out, hsw_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
