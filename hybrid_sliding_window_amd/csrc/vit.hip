@@ -105,21 +105,30 @@ __global__ __launch_bounds__(256) void vit_rope_kernel(VitRopeArgs a) {
 }
 
 // -------------------------------------------------------------- attention
-template <int G>
-__global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs a, int nqb) {
+// WIN: a window block (one 64-key chunk, the sink tile, one LDS stage);
+// otherwise a full block (the picture in 128-key chunks, each computed as two
+// 64-key halves, two stages, the next chunk's loads in flight while one is
+// computed).
+template <int G, bool WIN>
+__global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_kernel(VitArgs a, int nqb) {
     constexpr int NW = G == 1 ? 2 : 4;        // waves: 64 tokens per block at G = 1
     constexpr int NT = NW * 64;
     constexpr int BQ = 32 * NW / G;           // tokens per block; divides 64
-    constexpr int PIECES = KC * D / 8;        // 16-byte pieces of one K (or V) chunk
+    constexpr int KCS = WIN ? KC : 2 * KC;    // keys per stage
+    constexpr int PIECES = KCS * D / 8;       // 16-byte pieces of one K (or V) chunk
     constexpr int LOADS = PIECES / NT;        // per thread and tensor
+    constexpr int NSTG = WIN ? 1 : 2;
+    constexpr int KT = WIN ? K_TILES : KCS / 16;   // 16-key K tiles per stage
+    constexpr int VH = WIN ? V_HALVES : KCS / 16;  // 16-key V halves per stage
     static_assert(64 % BQ == 0 && PIECES % NT == 0, "block shape");
-    // Two stages; a stage holds K in MFMA fragment order (16-byte unit
-    // (h * STEPS + st) * 64 + lane = K[16h + lane % 16][32st + 8 (lane / 16) ..])
-    // and V in transposing-read order (8-byte unit (hh * DT + dt) * 64 + 16q +
-    // 4k + m = V[16hh + 4q + k][16dt + 4m .. +3]): every read is one
-    // contiguous run in lane order.
-    __shared__ __attribute__((aligned(1024))) uint16_t ks[2][K_TILES * 16 * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs[2][V_HALVES * 16 * D];
+    // A stage holds K in MFMA fragment order (16-byte unit (h * STEPS + st) *
+    // 64 + lane = K[16h + lane % 16][32st + 8 (lane / 16) ..]) and V in
+    // transposing-read order (8-byte unit (hh * DT + dt) * 64 + 16q + 4k + m
+    // = V[16hh + 4q + k][16dt + 4m .. +3]), V as fp16 unless the chunk holds
+    // a value fp16 cannot (then bf16): every read is one contiguous run in
+    // lane order.
+    __shared__ __attribute__((aligned(1024))) uint16_t ks[NSTG][KT * 16 * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs[NSTG][VH * 16 * D];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
@@ -141,11 +150,10 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs
         const int t = ord ? min(max(ord[j], 0), len - 1) : j;
         return tok0 + t;
     };
-    const bool windowed = a.window > 0;
-    const int klo = windowed ? (qb * BQ / KC) * KC : 0;
-    const int khi = windowed ? min(len, klo + KC) : len;
-    const bool has_sink = windowed && a.sink_key && klo > 0;
-    const int nch = (khi - klo + KC - 1) / KC;
+    const int klo = WIN ? (qb * BQ / KC) * KC : 0;
+    const int khi = WIN ? min(len, klo + KC) : len;
+    const bool has_sink = WIN && a.sink_key && klo > 0;
+    const int nch = WIN ? 1 : (len + KCS - 1) / KCS;
 
     // q of this wave's rows: row r = 32w + 16n + col is token qb*BQ + r/G,
     // head g*G + r%G (rows past the picture read its last token, never stored)
@@ -170,41 +178,64 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int pi = tid + NT * i, key = pi >> 3, p = pi & 7;
-            const int64_t r = row_of(min(klo + c * KC + key, khi - 1));
+            const int64_t r = row_of(min(klo + c * KCS + key, khi - 1));
             kr[i] = ld16(kg + r * rs + 8 * p);
             vr[i] = ld16(vg + r * rs + 8 * p);
         }
     };
-    auto put = [&](int stg) {
+    // any value of the thread's V pieces beyond fp16 (|v| >= 65536, the first
+    // bf16 value fp16 cannot hold, or not finite)
+    auto v_big = [&](const u32x4 &x) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m = fmaxf(m, fmaxf(fabsf(__uint_as_float(x[e] << 16)), fabsf(__uint_as_float(x[e] & 0xffff0000u))));
+        return !(m < 65536.0f);
+    };
+    auto to_f16 = [&](u32x4 x) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+        return x;
+    };
+    auto k_unit = [](int key, int p) { return ((key >> 4) * STEPS + (p >> 2)) * 64 + 16 * (p & 3) + (key & 15); };
+    auto v_unit = [](int key, int p) {
+        return ((key >> 4) * DT + (p >> 1)) * 64 + 16 * ((key & 15) >> 2) + 4 * (key & 3) + 2 * (p & 1);
+    };
+    auto put = [&](int stg, bool f16) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int pi = tid + NT * i, key = pi >> 3, p = pi & 7;
-            const int ku = ((key >> 4) * STEPS + (p >> 2)) * 64 + 16 * (p & 3) + (key & 15);
-            *reinterpret_cast<u32x4 *>(&ks[stg][ku * 8]) = kr[i];
-            const int vu = ((key >> 4) * DT + (p >> 1)) * 64 + 16 * ((key & 15) >> 2) + 4 * (key & 3) + 2 * (p & 1);
-            *reinterpret_cast<u32x4 *>(&vs[stg][vu * 4]) = vr[i];
+            *reinterpret_cast<u32x4 *>(&ks[stg][k_unit(key, p) * 8]) = kr[i];
+            *reinterpret_cast<u32x4 *>(&vs[stg][v_unit(key, p) * 4]) = f16 ? to_f16(vr[i]) : vr[i];
         }
     };
+    auto chunk_big = [&](bool extra) {
+        bool big = extra;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) big = big || v_big(vr[i]);
+        return big;
+    };
 
-    if (has_sink) {
-        // the sink tile: key slot 64 = the picture's first token in the
-        // block's order; slots 65..79 (K) and 65..95 (V) zero
+    // First chunk (and, in a window after the first, the sink key: slot 64 =
+    // the picture's first token in the block's order; slots 65..79 of K and
+    // 65..95 of V zero).
+    u32x4 sk = u32x4{0, 0, 0, 0}, svv = u32x4{0, 0, 0, 0};
+    if (has_sink && tid < 8) {
         const int64_t r0 = row_of(0);
+        sk = ld16(kg + r0 * rs + 8 * tid);
+        svv = ld16(vg + r0 * rs + 8 * tid);
+    }
+    fetch(0);
+    bool f16 = !__syncthreads_or(chunk_big(has_sink && tid < 8 && v_big(svv)));
+    put(0, f16);
+    if (WIN && has_sink) {
         for (int pi = tid; pi < 32 * 8; pi += NT) {
             const int kk = pi >> 3, p = pi & 7;
             const u32x4 z = u32x4{0, 0, 0, 0};
-            if (kk < 16) {
-                const int key = KC + kk;
-                const int ku = ((key >> 4) * STEPS + (p >> 2)) * 64 + 16 * (p & 3) + (key & 15);
-                *reinterpret_cast<u32x4 *>(&ks[0][ku * 8]) = kk == 0 ? ld16(kg + r0 * rs + 8 * p) : z;
-            }
-            const int key = KC + kk;
-            const int vu = ((key >> 4) * DT + (p >> 1)) * 64 + 16 * ((key & 15) >> 2) + 4 * (key & 3) + 2 * (p & 1);
-            *reinterpret_cast<u32x4 *>(&vs[0][vu * 4]) = kk == 0 ? ld16(vg + r0 * rs + 8 * p) : z;
+            if (kk < 16) *reinterpret_cast<u32x4 *>(&ks[0][k_unit(KC + kk, p) * 8]) = kk == 0 ? sk : z;
+            *reinterpret_cast<u32x4 *>(&vs[0][v_unit(KC + kk, p) * 4]) = kk == 0 ? (f16 ? to_f16(svv) : svv) : z;
         }
     }
-    fetch(0);
-    put(0);
     __syncthreads();
 
     const float scale2 = a.scale * kLog2e;
@@ -218,20 +249,115 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs
         for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
     }
 
-    auto compute = [&](int stg, int c, bool sink) {
+    // A window: the wave's two column tiles one after the other (fewer live
+    // registers: four waves per SIMD), the sink tile when the window has one.
+    auto compute = [&](int stg, int c, bool sink, bool vf16) {
         const uint16_t *ksc = ks[stg];
         const uint16_t *vsc = vs[stg];
         const int nvalid = khi - (klo + c * KC);   // keys of this chunk in range (>= 1)
-        float sv[K_TILES][2][4];
+        const bool interior = nvalid >= KC;
+        const int nsteps = sink ? 3 : 2;
 #pragma unroll
-        for (int h = 0; h < K_TILES; ++h) {
-            if (h == K_TILES - 1 && !sink) {
+        for (int n = 0; n < 2; ++n) {
+            float sv[K_TILES][4];
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+            for (int h = 0; h < K_TILES; ++h) {
+                if (h == K_TILES - 1 && !sink) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sv[h][n][j] = -INFINITY;
-                continue;
+                    for (int j = 0; j < 4; ++j) sv[h][j] = -INFINITY;
+                    continue;
+                }
+                f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+                    acc = mfma_16x16x32_bf16(*reinterpret_cast<const u32x4 *>(ksc + ((h * STEPS + st) * 64 + lane) * 8),
+                                             qv[n][st], acc);
+                if (h == K_TILES - 1) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][j] = (quad == 0 && j == 0) ? acc[j] : -INFINITY;
+                } else if (interior) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][j] = acc[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[h][j] = 16 * h + 4 * quad + j < nvalid ? acc[j] : -INFINITY;
+                }
             }
+            float cm = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < K_TILES; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cm = fmaxf(cm, sv[h][j]);
+            cm = quad_max_swap(cm) * scale2;
+            const bool raise = cm > m[n] + kRescale;
+            if (__any(raise)) {
+                const float mn = raise ? cm : m[n];
+                if (__any(raise && m[n] != -INFINITY)) {
+                    const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
+                    l[n] *= f;
+                }
+                m[n] = mn;
+            }
+            const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
+            float pv[K_TILES + 1][4];   // + a zero half pairing with the sink tile
+#pragma unroll
+            for (int h = 0; h < K_TILES; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pv[h][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][j], scale2, mu));
+                    l[n] += pv[h][j];
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pv[K_TILES][j] = 0.0f;
+            // O^T += V^T P^T over 32-key steps: slots 0-3 of a quad are keys
+            // 4quad.. of the step's first 16-key half, slots 4-7 of its
+            // second half, on both operands.  fp16 P (<= 2^8) x fp16 V, or,
+            // for a chunk kept in bf16, P as bf16 hi + lo x bf16 V.
+#pragma unroll
+            for (int s2 = 0; s2 < 3; ++s2) {
+                if (s2 >= nsteps) break;
+                const float *p0 = pv[2 * s2], *p1 = pv[2 * s2 + 1];
+                if (vf16) {
+                    const u32x4 pf = u32x4{pack_f16x2(p0[0], p0[1]), pack_f16x2(p0[2], p0[3]),
+                                           pack_f16x2(p1[0], p1[1]), pack_f16x2(p1[2], p1[3])};
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
+                        const u32x2 a1 = ds_read_tr16(vsc + (((2 * s2 + 1) * DT + dt) * 64 + lane) * 4);
+                        oacc[n][dt] = mfma_16x16x32_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf, oacc[n][dt]);
+                    }
+                } else {
+                    u32x2 h0, l0, h1, l1;
+                    split_hi_lo(p0, h0, l0);
+                    split_hi_lo(p1, h1, l1);
+                    const u32x4 ph = u32x4{h0[0], h0[1], h1[0], h1[1]};
+                    const u32x4 pl = u32x4{l0[0], l0[1], l1[0], l1[1]};
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
+                        const u32x2 a1 = ds_read_tr16(vsc + (((2 * s2 + 1) * DT + dt) * 64 + lane) * 4);
+                        const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                        oacc[n][dt] = mfma_16x16x32_bf16(av, ph, oacc[n][dt]);
+                        oacc[n][dt] = mfma_16x16x32_bf16(av, pl, oacc[n][dt]);
+                    }
+                }
+            }
+        }
+    };
+
+    // A full block's chunk: both column tiles together, so every K and V^T
+    // fragment read from LDS feeds two MFMAs; four key tiles, no sink.
+    auto compute_full = [&](int stg, int c, int hf, bool vf16) {
+        constexpr int NKT = KC / 16;
+        const uint16_t *ksc = ks[stg] + hf * (NKT * STEPS * 64 * 8);   // the half's K tiles
+        const uint16_t *vsc = vs[stg] + hf * (NKT * DT * 64 * 4);      // and V halves
+        const int nvalid = khi - (klo + c * KCS + hf * KC);
+        const bool interior = nvalid >= KC;
+        float sv[2][NKT][4];
+#pragma unroll
+        for (int h = 0; h < NKT; ++h) {
             u32x4 ak[STEPS];
 #pragma unroll
             for (int st = 0; st < STEPS; ++st)
@@ -241,22 +367,23 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs
                 f32x4 acc = f32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int st = 0; st < STEPS; ++st) acc = mfma_16x16x32_bf16(ak[st], qv[n][st], acc);
+                if (interior) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = 16 * h + 4 * quad + j;
-                    const bool ok = h < K_TILES - 1 ? key < nvalid : key == KC;
-                    sv[h][n][j] = ok ? acc[j] : -INFINITY;
+                    for (int j = 0; j < 4; ++j) sv[n][h][j] = acc[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[n][h][j] = 16 * h + 4 * quad + j < nvalid ? acc[j] : -INFINITY;
                 }
             }
         }
-        float pv[K_TILES + 1][2][4];   // + a zero half pairing with the sink tile
+        float pv[2][NKT][4];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             float cm = -INFINITY;
 #pragma unroll
-            for (int h = 0; h < K_TILES; ++h)
+            for (int h = 0; h < NKT; ++h)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) cm = fmaxf(cm, sv[h][n][j]);
+                for (int j = 0; j < 4; ++j) cm = fmaxf(cm, sv[n][h][j]);
             cm = quad_max_swap(cm) * scale2;
             const bool raise = cm > m[n] + kRescale;
             if (__any(raise)) {
@@ -271,53 +398,68 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs
             }
             const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
 #pragma unroll
-            for (int h = 0; h < K_TILES; ++h)
+            for (int h = 0; h < NKT; ++h)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    pv[h][n][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][n][j], scale2, mu));
-                    l[n] += pv[h][n][j];
+                    pv[n][h][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[n][h][j], scale2, mu));
+                    l[n] += pv[n][h][j];
                 }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pv[K_TILES][n][j] = 0.0f;
         }
-        // O^T += V^T P^T over 32-key steps: slots 0-3 of a quad are keys
-        // 4quad.. of the step's first 16-key half, slots 4-7 of its second
-        // half, on both operands.
-        const int nsteps = sink ? 3 : 2;
 #pragma unroll
-        for (int s2 = 0; s2 < 3; ++s2) {
-            if (s2 >= nsteps) break;
-            u32x4 ph[2], pl[2];
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                u32x2 h0, l0, h1, l1;
-                split_hi_lo(pv[2 * s2][n], h0, l0);
-                split_hi_lo(pv[2 * s2 + 1][n], h1, l1);
-                ph[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
-                pl[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
-                const u32x2 a1 = ds_read_tr16(vsc + (((2 * s2 + 1) * DT + dt) * 64 + lane) * 4);
-                const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        for (int s2 = 0; s2 < NKT / 2; ++s2) {
+            if (vf16) {
+                u32x4 pf[2];
 #pragma unroll
                 for (int n = 0; n < 2; ++n) {
-                    oacc[n][dt] = mfma_16x16x32_bf16(av, ph[n], oacc[n][dt]);
-                    oacc[n][dt] = mfma_16x16x32_bf16(av, pl[n], oacc[n][dt]);
+                    const float *p0 = pv[n][2 * s2], *p1 = pv[n][2 * s2 + 1];
+                    pf[n] = u32x4{pack_f16x2(p0[0], p0[1]), pack_f16x2(p0[2], p0[3]), pack_f16x2(p1[0], p1[1]),
+                                  pack_f16x2(p1[2], p1[3])};
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
+                    const u32x2 a1 = ds_read_tr16(vsc + (((2 * s2 + 1) * DT + dt) * 64 + lane) * 4);
+                    const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf[n], oacc[n][dt]);
+                }
+            } else {
+                u32x4 ph[2], pl[2];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    u32x2 h0, l0, h1, l1;
+                    split_hi_lo(pv[n][2 * s2], h0, l0);
+                    split_hi_lo(pv[n][2 * s2 + 1], h1, l1);
+                    ph[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+                    pl[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
+                    const u32x2 a1 = ds_read_tr16(vsc + (((2 * s2 + 1) * DT + dt) * 64 + lane) * 4);
+                    const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        oacc[n][dt] = mfma_16x16x32_bf16(av, ph[n], oacc[n][dt]);
+                        oacc[n][dt] = mfma_16x16x32_bf16(av, pl[n], oacc[n][dt]);
+                    }
                 }
             }
         }
     };
 
-    if (has_sink) {
-        compute(0, 0, true);     // a window: one chunk
+    if constexpr (WIN) {
+        compute(0, 0, has_sink, f16);
     } else {
         for (int c = 0; c < nch; ++c) {
             const int stg = c & 1;
             if (c + 1 < nch) fetch(c + 1);
-            compute(stg, c, false);
-            if (c + 1 < nch) put(stg ^ 1);
+            compute_full(stg, c, 0, f16);
+            if (c * KCS + KC < len) compute_full(stg, c, 1, f16);
+            if (c + 1 < nch) {
+                f16 = !__syncthreads_or(chunk_big(false));
+                put(stg ^ 1, f16);
+            }
             __syncthreads();
         }
     }
@@ -332,10 +474,10 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64) void vit_attn_kernel(VitArgs
         float ll = quad_sum_swap(l[n]);
         float fac = 1.0f;
         if (a.sinks) {
-            const float sk = a.sinks[g * G + head] * kLog2e;
-            const float mf = fmaxf(m[n], sk);
+            const float sk2 = a.sinks[g * G + head] * kLog2e;
+            const float mf = fmaxf(m[n], sk2);
             fac = exp2f(m[n] - mf);
-            ll = ll * fac + exp2f(sk - mf);
+            ll = ll * fac + exp2f(sk2 - mf);
         }
         const float sc = fac / ll;
         if (j < len) {
@@ -365,12 +507,22 @@ hipError_t launch_vit_attn(const VitArgs &a, int64_t max_len, hipStream_t s) {
     const int BQ = vit_block_tokens(G);
     const int nqb = (int)((max_len + BQ - 1) / BQ);
     dim3 grid((unsigned)((int64_t)a.n_images * a.hkv * nqb));
-    switch (G) {
-        case 1: hipLaunchKernelGGL((vit_attn_kernel<1>), grid, dim3(128), 0, s, a, nqb); break;
-        case 2: hipLaunchKernelGGL((vit_attn_kernel<2>), grid, dim3(256), 0, s, a, nqb); break;
-        case 4: hipLaunchKernelGGL((vit_attn_kernel<4>), grid, dim3(256), 0, s, a, nqb); break;
-        case 8: hipLaunchKernelGGL((vit_attn_kernel<8>), grid, dim3(256), 0, s, a, nqb); break;
-        default: hipLaunchKernelGGL((vit_attn_kernel<16>), grid, dim3(256), 0, s, a, nqb); break;
+    if (a.window > 0) {
+        switch (G) {
+            case 1: hipLaunchKernelGGL((vit_attn_kernel<1, true>), grid, dim3(128), 0, s, a, nqb); break;
+            case 2: hipLaunchKernelGGL((vit_attn_kernel<2, true>), grid, dim3(256), 0, s, a, nqb); break;
+            case 4: hipLaunchKernelGGL((vit_attn_kernel<4, true>), grid, dim3(256), 0, s, a, nqb); break;
+            case 8: hipLaunchKernelGGL((vit_attn_kernel<8, true>), grid, dim3(256), 0, s, a, nqb); break;
+            default: hipLaunchKernelGGL((vit_attn_kernel<16, true>), grid, dim3(256), 0, s, a, nqb); break;
+        }
+    } else {
+        switch (G) {
+            case 1: hipLaunchKernelGGL((vit_attn_kernel<1, false>), grid, dim3(128), 0, s, a, nqb); break;
+            case 2: hipLaunchKernelGGL((vit_attn_kernel<2, false>), grid, dim3(256), 0, s, a, nqb); break;
+            case 4: hipLaunchKernelGGL((vit_attn_kernel<4, false>), grid, dim3(256), 0, s, a, nqb); break;
+            case 8: hipLaunchKernelGGL((vit_attn_kernel<8, false>), grid, dim3(256), 0, s, a, nqb); break;
+            default: hipLaunchKernelGGL((vit_attn_kernel<16, false>), grid, dim3(256), 0, s, a, nqb); break;
+        }
     }
     return hipGetLastError();
 }
