@@ -43,13 +43,16 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_
 
 # HBM bytes per call read by the TCC counters (FETCH_SIZE / WRITE_SIZE, scaled
 # by a plain copy of known size) for the kernel sources whose digest is given;
-# profiles/swa_prefill_4x8192_hbm_traffic.md and
-# profiles/swa_decode_256seq_hbm_traffic.md hold the runs.  Reported as null
+# profiles/swa_prefill_4x8192_hbm_traffic.md,
+# profiles/swa_decode_256seq_hbm_traffic.md and
+# profiles/vit_window_16x4096_hbm_traffic.md hold the runs.  Reported as null
 # once those sources differ from the ones measured.
 MEASURED_TRAFFIC = {
     # band kernel 1510.3 MB + ring commit 2.7 MB read / 2.6 MB written
-    "swa_prefill": (1515.6e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "5658fb006a829f1f"),
-    "swa_decode": (178.45e6, ("swa_decode.hip", "hsw_device.h"), "cdb01983eb797dc6"),
+    "swa_prefill": (1515.6e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "8baa3af85ddcd646"),
+    "swa_decode": (178.45e6, ("swa_decode.hip", "hsw_device.h"), "83186c6fe6ff93f0"),
+    # ViT window block: 201.8 MB read, 134.2 MB written
+    "vit_window": (336.0e6, ("vit.hip", "hsw_device.h"), "3c7858915bd096a0"),
 }
 
 
@@ -433,6 +436,7 @@ def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
     rope_bytes = T * (hq + hkv) * 64 * 2 * 2
     del reps
     return dict(window=dict(ms=res["window"], bytes=win_bytes, gbs=win_bytes / res["window"] / 1e6,
+                            traffic=measured_traffic("vit_window"),
                             frac_hbm_peak=win_bytes / res["window"] / 1e6 / HBM_PEAK_GBS,
                             tflops=win_flops / res["window"] / 1e9,
                             workload="window block: 64-token windows in column order of the merge units + "

@@ -221,3 +221,26 @@ def test_vit_attention_full_size_sampled(mode):
     idx, ref = oracle_attention(bc, shape, order_ref, mode != "full", pictures=pics)
     ma, mr = assert_close(f64(out[torch.from_numpy(idx).to(DEV)]), ref, what=f"vit full size {mode}")
     print(f"vit_attention full size {mode} (pictures {pics}): max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+@pytest.mark.parametrize("window", [64, 0])
+def test_vit_attention_values_beyond_fp16_range(window):
+    """V rows with abs ~ 1e5 (outside fp16) in some chunks, the sink row
+    among them: those chunks take the exact bf16 path, the rest fp16; the
+    result still matches the oracle."""
+    note(f"vit_attention large V window={window}")
+    grids = [(20, 24), (8, 18)]
+    b = wl.vit_batch(seed=39, grids=grids)
+    v = b["v"].float()
+    v[0] *= 1.0e5 / 4           # the first picture's token 0: the sink key of its later windows
+    v[300:310] *= 1.0e5 / 4     # a run of rows inside one chunk / window
+    b["v"] = v.to(torch.bfloat16)
+    assert float(b["v"].float().abs().max()) >= 65536
+    shape = wl.vit_shape(window=window)
+    order_lib = layouts(grids, lib=True)[2]
+    order_ref = layouts(grids, lib=False)[2]
+    out = run_attention(b, shape, order_lib, True)
+    idx, ref = oracle_attention(b, shape, order_ref, True)
+    scale = float(np.abs(ref).max())
+    ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * scale, what=f"vit large V window={window}")
+    print(f"vit_attention large V window={window}: max_abs={ma:.2e} (output scale {scale:.1e}) mean_rel={mr:.2e}")
