@@ -244,3 +244,34 @@ def test_vit_attention_values_beyond_fp16_range(window):
     scale = float(np.abs(ref).max())
     ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * scale, what=f"vit large V window={window}")
     print(f"vit_attention large V window={window}: max_abs={ma:.2e} (output scale {scale:.1e}) mean_rel={mr:.2e}")
+
+
+def test_vit_attention_clamps_out_of_range_order_entries():
+    """Order entries outside the picture are clamped into it (the header's
+    contract: wrong rows, never out-of-bounds accesses): the output of every
+    token that occurs once in the clamped order matches the oracle given the
+    clamped order."""
+    note("vit_attention out-of-range order entries")
+    grids = [(8, 12), (6, 6)]
+    b = wl.vit_batch(seed=40, grids=grids)
+    order = layouts(grids, lib=True)[2].copy()
+    order[5] = -3                 # picture 0
+    order[70] = 10_000
+    order[96 + 7] = 36            # picture 1 has 36 tokens: one past the end
+    cu = b["cu_seqlens"].tolist()
+    clamped = order.copy()
+    for s in range(len(grids)):
+        clamped[cu[s]:cu[s + 1]] = np.clip(order[cu[s]:cu[s + 1]], 0, cu[s + 1] - cu[s] - 1)
+    shape = wl.vit_shape()
+    out = run_attention(b, shape, order, True)
+    idx, ref = oracle_attention(b, shape, clamped, True)
+    once = []
+    for s in range(len(grids)):
+        local = clamped[cu[s]:cu[s + 1]]
+        counts = np.bincount(local, minlength=cu[s + 1] - cu[s])
+        once += [cu[s] + t for t in range(cu[s + 1] - cu[s]) if counts[t] == 1]
+    once = np.array(once)
+    pos = {int(r): i for i, r in enumerate(idx)}
+    sel = np.array([pos[int(r)] for r in once])
+    ma, mr = assert_close(f64(out)[once], ref[sel], what="vit_attention clamped order")
+    print(f"vit_attention clamped order ({len(once)} tokens checked): max_abs={ma:.2e} mean_rel={mr:.2e}")
