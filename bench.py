@@ -472,7 +472,15 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
     hs.step(stream)
     torch.cuda.synchronize()
     t_q = ev_time(lambda i: hs.step(stream), n, stream)
+    # decode calls on a second stream beside the prefill calls (fused q-RoPE
+    # still on), then the same with the plain calls
+    hs.step(stream, overlap=True)
+    torch.cuda.synchronize()
+    t_qo = ev_time(lambda i: hs.step(stream, overlap=True), n, stream)
     hs.qrope = False
+    hs.step(stream, overlap=True)
+    torch.cuda.synchronize()
+    t_o = ev_time(lambda i: hs.step(stream, overlap=True), n, stream)
     timer = []
     hs.step(stream, timer)
     torch.cuda.synchronize()
@@ -483,6 +491,8 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
     nl, nf = len(hs.pattern), len(hs.pattern) - sum(hs.pattern)
     res = dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps=n, per_call_ms={k: round(v, 3) for k, v in kinds.items()},
                qrope_ms=t_q, qrope_tokens_per_s=(T + S) / (t_q / 1e3),
+               overlap_ms=t_o, overlap_tokens_per_s=(T + S) / (t_o / 1e3),
+               qrope_overlap_ms=t_qo, qrope_overlap_tokens_per_s=(T + S) / (t_qo / 1e3),
                layers=f"{nl - nf} windowed + {nf} full (seeded pattern)", pool_gb=round(hs.pool_gb, 1),
                workload=f"hybrid step {model.name}: {nl} layers, 8192-token chunk at 131072 + 128 decode "
                         "sequences U{4096..262144}")
@@ -522,7 +532,8 @@ def bench_pro(hsw, wl, args, stream):
     torch.cuda.empty_cache()
     hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m)
     print(f"[bench] pro hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "
-          f"fused q-RoPE step {hy['qrope_ms']:.1f} ms",
+          f"fused q-RoPE step {hy['qrope_ms']:.1f} ms; decode on a second stream {hy['overlap_ms']:.1f} ms "
+          f"(fused {hy['qrope_overlap_ms']:.1f} ms)",
           file=sys.stderr, flush=True)
     out["hybrid_step"] = rounded(hy)
     torch.cuda.empty_cache()
@@ -637,7 +648,8 @@ def main():
         torch.cuda.empty_cache()
         hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream)
         print(f"[bench] hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "
-              f"fused q-RoPE step {hy['qrope_ms']:.1f} ms",
+              f"fused q-RoPE step {hy['qrope_ms']:.1f} ms; decode on a second stream {hy['overlap_ms']:.1f} ms "
+              f"(fused {hy['qrope_overlap_ms']:.1f} ms)",
               file=sys.stderr, flush=True)
         calls["hybrid_step"] = hy
         torch.cuda.empty_cache()

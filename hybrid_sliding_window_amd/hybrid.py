@@ -20,6 +20,12 @@ With qrope=True the RoPE calls rotate and write K/V only and each attention
 call is its *_qrope form, which rotates the raw q itself (no q_rot round trip
 through HBM).
 
+step(overlap=True) issues each layer's decode calls on a second stream: the
+decode chain (RoPE + decode of the decode tokens, layer after layer) and the
+prefill chain (RoPE + prefill of the chunk, layer after layer) share no data
+-- disjoint pool rows, rings and outputs -- so the HBM-bound decodes run
+beside the compute-bound prefills; each chain keeps its own layer order.
+
 Sizes default to the bench workload: the model's layers (MiMo-V2.6-Flash: 48,
 39 windowed + 9 full; MiMo-V2.6-Pro: 70, 60 + 10; the full layers at seeded
 indices), an 8192-token chunk at positions 131072..139263 and 128 decode
@@ -90,9 +96,13 @@ class HybridStep:
         self.wsb = hsw.hsw_full_decode_workspace_bytes(self.full, S, self.max_ctx, chunk)
         self.ws = torch.empty(self.wsb // 4 + 4, dtype=torch.float32, device=device)
 
-    def calls(self, li, stream=None, qrope=None):
+    def calls(self, li, stream=None, qrope=None, dstream=None):
         """The four calls of layer li as (name, thunk) pairs, in order
-        (qrope: override the instance's choice of fused q-RoPE)."""
+        (qrope: override the instance's choice of fused q-RoPE; dstream: the
+        stream of the two decode calls, default `stream`)."""
+        if dstream is not None:
+            pre = self.calls(li, stream, qrope)[:2]
+            return pre + self.calls(li, dstream, qrope)[2:]
         if self.qrope if qrope is None else qrope:
             return self._calls_qrope(li, stream)
         h, d, T, S = self.hsw, self.layers[li], self.T, self.S
@@ -161,9 +171,21 @@ class HybridStep:
                                                                    self.out_d, stream)),
         ]
 
-    def step(self, stream=None, timer=None):
+    def step(self, stream=None, timer=None, overlap=False):
         """Every layer in order.  timer: a list that receives (name, start
-        event, end event) per call."""
+        event, end event) per call.  overlap: decode calls on a second stream
+        (joined back into `stream` at the end)."""
+        if overlap:
+            main = stream if stream is not None else torch.cuda.current_stream()
+            if getattr(self, "_dstream", None) is None:
+                self._dstream = torch.cuda.Stream(device=main.device)   # default priority
+            ds = self._dstream
+            ds.wait_stream(main)
+            for li in range(len(self.pattern)):
+                for name, fn in self.calls(li, main, dstream=ds):
+                    fn()
+            main.wait_stream(ds)
+            return
         for li in range(len(self.pattern)):
             for name, fn in self.calls(li, stream):
                 if timer is None:

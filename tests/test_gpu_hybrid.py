@@ -207,3 +207,24 @@ def test_hybrid_fused_qrope_calls(hs):
         got.append(f64(hs.out_d[s]))
     ma, mr = assert_close(np.stack(got), np.stack(refs), what="hybrid full_decode_qrope")
     print(f"hybrid full_decode_qrope sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_hybrid_overlapped_step_equals_serial_step(hs):
+    """The decode calls on a second stream beside the prefill calls give
+    byte-identical outputs, rings and pool rows: a serial step reaches the
+    steady state (the chunk's ring commit rewrites the same rows each step),
+    then one serial and one overlapped step from that state are compared."""
+    note("hybrid overlapped vs serial step")
+    torch.cuda.synchronize()
+    hs.step()
+    hs.step()
+    torch.cuda.synchronize()
+    ref = [hs.out.clone(), hs.out_d.clone()] + [hs.layers[0][k].clone() for k in ("kring", "vring")]
+    ref_pool = (hs.kpool[:hs.P0 + hs.T].clone(), hs.vpool[hs.rows - 4096:].clone())
+    hs.step(overlap=True)
+    torch.cuda.synchronize()
+    got = [hs.out, hs.out_d] + [hs.layers[0][k] for k in ("kring", "vring")]
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    assert torch.equal(ref_pool[0], hs.kpool[:hs.P0 + hs.T]) and torch.equal(ref_pool[1], hs.vpool[hs.rows - 4096:])
+    print("hybrid overlapped step: outputs, rings and pool rows bitwise equal to the serial step")
