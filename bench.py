@@ -163,10 +163,10 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
                               "RoPE + hsw_swa_prefill, same workload")
     return dict(
         fused=fused_res,
-        ms=t_call, flops=flops, bytes=bytes_, tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
+        ms=t_call, flops=flops, bytes=bytes_, tokens=T, tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
         frac_mfma_peak=flops / t_call / 1e9 / BF16_PEAK_TFLOPS, frac_hbm_peak=bytes_ / t_call / 1e6 / HBM_PEAK_GBS,
         workload=f"windowed prefill, 4 x 8192 tokens from position 0, {heads(model)}, window 128",
-        rope=dict(ms=t_rope, bytes=rope_bytes, gbs=rope_bytes / t_rope / 1e6,
+        rope=dict(ms=t_rope, bytes=rope_bytes, tokens=T, gbs=rope_bytes / t_rope / 1e6,
                   frac_hbm_peak=rope_bytes / t_rope / 1e6 / HBM_PEAK_GBS,
                   workload=f"RoPE + staging write of 32768 tokens ({heads(model)})"))
 
@@ -236,7 +236,7 @@ def bench_swa_decode(hsw, wl, steps, stream, replicas=8, model=None):
                      workload="K/V-only RoPE into the rings + hsw_swa_decode_qrope (q rotated in the "
                               "kernel, kept in fp32) against RoPE + hsw_swa_decode, same workload")
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
-                flops=flops, launches=n, replicas=replicas, fused=fused_res,
+                flops=flops, tokens=S, launches=n, replicas=replicas, fused=fused_res,
                 workload=f"windowed decode, 256 sequences at positions U{{128..524288}}, {heads(model)}, "
                          "128-slot ring")
 
@@ -294,7 +294,7 @@ def bench_full_decode(hsw, wl, steps, stream, model=None):
                      workload="K/V-only RoPE into the pool + hsw_full_decode_splitk_qrope (q rotated in the "
                               "kernel, kept in fp32) against RoPE + hsw_full_decode_splitk, same workload")
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
-                tflops=flops / t / 1e9, fused=fused_res,
+                tflops=flops / t / 1e9, flops=flops, tokens=S, fused=fused_res,
                 workload=f"full-attention decode, 64 sequences, contexts U{{32768..131072}}, {hq} q / {hkv} KV "
                          "heads, split-K 2048")
 
@@ -345,7 +345,7 @@ def bench_full_prefill(hsw, wl, steps, stream, model=None):
                      workload="K/V-only RoPE into the pool + hsw_full_prefill_chunk_qrope (q rotated in the "
                               "kernel) against RoPE + hsw_full_prefill_chunk, same workload")
     return dict(ms=t, flops=flops, tflops=flops / t / 1e9, frac_mfma_peak=flops / t / 1e9 / BF16_PEAK_TFLOPS,
-                fused=fused_res,
+                tokens=T, fused=fused_res,
                 workload=f"full-attention prefill, 8192 tokens after 131072 prior rows, {hq} q / {hkv} KV heads")
 
 
@@ -438,13 +438,13 @@ def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
     return dict(window=dict(ms=res["window"], bytes=win_bytes, gbs=win_bytes / res["window"] / 1e6,
                             traffic=measured_traffic("vit_window"),
                             frac_hbm_peak=win_bytes / res["window"] / 1e6 / HBM_PEAK_GBS,
-                            tflops=win_flops / res["window"] / 1e9,
+                            tflops=win_flops / res["window"] / 1e9, flops=win_flops, tokens=T,
                             workload="window block: 64-token windows in column order of the merge units + "
                                      "the sink key"),
-                full=dict(ms=res["full"], flops=full_flops, tflops=full_flops / res["full"] / 1e9,
+                full=dict(ms=res["full"], flops=full_flops, tflops=full_flops / res["full"] / 1e9, tokens=T,
                           frac_mfma_peak=full_flops / res["full"] / 1e9 / BF16_PEAK_TFLOPS,
                           workload="full block: every picture attends to itself"),
-                rope=dict(ms=res["rope"], bytes=rope_bytes, gbs=rope_bytes / res["rope"] / 1e6,
+                rope=dict(ms=res["rope"], bytes=rope_bytes, gbs=rope_bytes / res["rope"] / 1e6, tokens=T,
                           workload="2D RoPE of q and k"),
                 workload=f"vision encoder, {S} pictures of 64 x 64 patches ({T} tokens), {hq} q / {hkv} KV "
                          "heads of width 64")
@@ -500,7 +500,29 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
     return res
 
 
+def own_roofline(d):
+    """Add the call's own roofline fraction t_floor / t, t_floor =
+    max(flops / dense bf16 MFMA peak, bytes / HBM peak) over the algorithmic
+    work it reports, and tokens/s where it reports a token count."""
+    if not isinstance(d, dict) or not d.get("ms") or d["ms"] != d["ms"]:
+        return d
+    t = d["ms"] / 1e3
+    floors = {}
+    if d.get("flops"):
+        floors["mfma"] = d["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    if d.get("bytes"):
+        floors["hbm"] = d["bytes"] / (HBM_PEAK_GBS * 1e9)
+    if floors:
+        bound = max(floors, key=floors.get)
+        d["roofline_bound"] = bound
+        d["roofline_frac"] = floors[bound] / t
+    if d.get("tokens"):
+        d["tokens_per_s"] = d["tokens"] / t
+    return d
+
+
 def rounded(d):
+    d = own_roofline(dict(d))
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
 
 
@@ -655,7 +677,13 @@ def main():
         torch.cuda.empty_cache()
     calls["swa_prefill"] = dict(ms=pre["ms"], tflops=pre["tflops"], gbs=pre["gbs"],
                                 frac_mfma_peak=pre["tflops"] / BF16_PEAK_TFLOPS,
-                                frac_hbm_peak=pre["gbs"] / HBM_PEAK_GBS, flops=pre["flops"], bytes=pre["bytes"])
+                                frac_hbm_peak=pre["gbs"] / HBM_PEAK_GBS, flops=pre["flops"], bytes=pre["bytes"],
+                                tokens=4 * 8192)
+    for v in calls.values():
+        own_roofline(v)
+        if isinstance(v, dict):
+            for vv in v.values():
+                own_roofline(vv)
     line = {
         "metric": METRIC,
         "value": round(pre["tflops"], 3),
