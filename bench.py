@@ -604,8 +604,8 @@ def main():
     ap.add_argument("--no-pro", action="store_true", help="skip the MiMo-V2.6-Pro section")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence / KV head with no exchange; see the design notes)",
+        print(f"bench.py: the attention core is measured on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by sequence / KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     from hybrid_sliding_window_amd import hsw

@@ -20,7 +20,7 @@ length -- so that it can be checked by eye against the pages:
   snapshot is released; the windowed layers' rings are copied into the
   snapshot and back, and the snapshot's position is its length.
 
-Readings where the pages leave a step open (each stated in the design notes):
+Readings where the pages leave a step open:
 * pool rows are handed out as one contiguous run per sequence (the attention
   calls address rows as seq_base + position), at the lowest row where
   ``max_len`` free rows start; the ring slot is the lowest free one;
