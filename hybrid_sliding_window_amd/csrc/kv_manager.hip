@@ -14,6 +14,7 @@
 // Pool rows are handed out as contiguous runs (first fit over an address-
 // ordered free list, neighbours merged on release), since the attention calls
 // address a sequence's rows as seq_base + position.
+#include <algorithm>
 #include <map>
 #include <new>
 #include <vector>
@@ -63,12 +64,14 @@ struct hsw_kvm {
     struct Seq {
         bool used = false;
         int64_t base = 0, max_len = 0, len = 0;
-        std::vector<int32_t> tok;  // token id each row holds (rows 0 .. tok.size()-1 written)
+        std::vector<int32_t> tok;       // token id each row holds (rows 0 .. tok.size()-1 written)
+        std::vector<int64_t> slot_pos;  // position each ring slot holds (-1: none yet)
     };
     struct Snap {
         int32_t seq;
         int64_t pos;
         int32_t slot;
+        std::vector<int64_t> slot_pos;  // what the copied rings held
     };
     hsw_kvm_config cfg;
     std::vector<char *> k, v;
@@ -101,6 +104,33 @@ hsw_status check_seq(hsw_kvm *kvm, int32_t seq) {
     if (seq < 0 || seq >= (int32_t)kvm->seqs.size() || !kvm->seqs[seq].used)
         return fail(HSW_E_SHAPE, "sequence %d is not admitted", seq);
     return HSW_OK;
+}
+
+// The largest length L <= lim whose window the rings hold: the token at L
+// reads positions max(0, L - W + 1) .. L - 1 from the ring (colibri "System
+// One mode and prompt reuse": position p in slot p mod W).  The positions the
+// slots hold form runs of consecutive values; a run [a, b] serves L iff
+// L - 1 <= b and it reaches down to the window's first position: a == 0, or
+// a <= L - W + 1.  L = 0 needs nothing, and neither does any L when W = 1
+// (the token then attends to itself only).
+int64_t longest_held_window(const std::vector<int64_t> &slot_pos, int64_t lim) {
+    const int64_t W = (int64_t)slot_pos.size();
+    if (W == 1) return lim > 0 ? lim : 0;
+    std::vector<int64_t> held;
+    held.reserve(slot_pos.size());
+    for (int64_t p : slot_pos)
+        if (p >= 0) held.push_back(p);
+    std::sort(held.begin(), held.end());
+    int64_t best = 0;
+    for (size_t i = 0; i < held.size();) {
+        size_t j = i;
+        while (j + 1 < held.size() && held[j + 1] == held[j] + 1) ++j;
+        const int64_t a = held[i], b = held[j];
+        const int64_t lo = a == 0 ? 1 : a + W - 1, hi = b + 1 < lim ? b + 1 : lim;
+        if (hi >= lo && hi > best) best = hi;
+        i = j + 1;
+    }
+    return best;
 }
 
 void drop_snaps_above(hsw_kvm *kvm, int32_t seq, int64_t pos) {
@@ -197,6 +227,7 @@ hsw_status hsw_kvm_admit(hsw_kvm *kvm, int64_t max_len, int32_t *seq, int64_t *s
         return fail(HSW_E_CAPACITY, "no run of %lld free pool rows", (long long)max_len);
     const int64_t start = run->first, len = run->second;
     try {
+        kvm->seqs[slot].slot_pos.assign(kvm->cfg.window, -1);   // (an unused slot: nothing to undo)
         if (len > max_len) kvm->free_rows[start + max_len] = len - max_len;
     } catch (...) {
         return fail(HSW_E_CAPACITY, "out of host memory");
@@ -268,6 +299,10 @@ hsw_status hsw_kvm_append(hsw_kvm *kvm, int32_t seq, const int32_t *tokens, int6
             s.tok.push_back(tokens[i]);
         }
     }
+    // the caller's attention calls over the appended tokens write each
+    // position into its ring slot; only the last W of them stay
+    const int64_t W = (int64_t)s.slot_pos.size();
+    for (int64_t p = (n > W ? s.len + n - W : s.len); p < s.len + n; ++p) s.slot_pos[p % W] = p;
     s.len += n;
     return HSW_OK;
 }
@@ -315,7 +350,7 @@ hsw_status hsw_kvm_snapshot(hsw_kvm *kvm, int32_t seq, int32_t *snap, hsw_stream
     if (slot < 0) return fail(HSW_E_CAPACITY, "every snapshot slot (%d) is taken", (int)kvm->slot_used.size());
     const int32_t id = kvm->next_snap_id;
     try {
-        kvm->snaps[id] = hsw_kvm::Snap{seq, kvm->seqs[seq].len, slot};
+        kvm->snaps[id] = hsw_kvm::Snap{seq, kvm->seqs[seq].len, slot, kvm->seqs[seq].slot_pos};
     } catch (...) {
         return fail(HSW_E_CAPACITY, "out of host memory");
     }
@@ -338,6 +373,7 @@ hsw_status hsw_kvm_restore(hsw_kvm *kvm, int32_t snap, hsw_stream_t stream) {
     hsw_status st = copy_rings(kvm, sn.seq, sn.slot, false, (hipStream_t)stream);
     if (st) return st;
     s.len = sn.pos;
+    s.slot_pos = it->second.slot_pos;   // same size: no allocation
     return HSW_OK;
 }
 
@@ -359,10 +395,12 @@ int64_t hsw_kvm_window_safe_length(hsw_kvm *kvm, int32_t seq, const int32_t *tok
     int64_t lcp = 0;
     const int64_t lim = n < (int64_t)s.tok.size() ? n : (int64_t)s.tok.size();
     while (lcp < lim && s.tok[lcp] == tokens[lcp]) ++lcp;
-    int64_t best = lcp >= s.len ? s.len : 0;
+    // live rings: any length up to the live one (a truncate reaches it)
+    int64_t best = longest_held_window(s.slot_pos, lcp < s.len ? lcp : s.len);
+    // a snapshot: its own position, if its copied rings hold that window
     for (const auto &kv : kvm->snaps) {
         const hsw_kvm::Snap &sn = kv.second;
-        if (sn.seq == seq && sn.pos <= lcp && sn.pos > best) {
+        if (sn.seq == seq && sn.pos <= lcp && sn.pos > best && longest_held_window(sn.slot_pos, sn.pos) == sn.pos) {
             best = sn.pos;
             if (snap) *snap = kv.first;
         }

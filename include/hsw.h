@@ -358,12 +358,15 @@ hsw_status hsw_kvm_release(hsw_kvm *kvm, int32_t seq);
 
 /* Record host token ids for positions len .. len+n-1 of the sequence (the
  * caller then writes their K/V with hsw_rope_partial_kv_write and runs the
- * attention at *start_pos = len).  HSW_E_CAPACITY past max_len.  A token that
- * differs from the one its row held before releases the sequence's snapshots
- * at positions above it. */
+ * attention at *start_pos = len, which puts each of these positions into its
+ * ring slot p mod window; the manager records that the slots now hold them).
+ * HSW_E_CAPACITY past max_len.  A token that differs from the one its row
+ * held before releases the sequence's snapshots at positions above it. */
 hsw_status hsw_kvm_append(hsw_kvm *kvm, int32_t seq, const int32_t *tokens, int64_t n, int64_t *start_pos);
 /* Move the sequence's length back to new_len <= len (the rows beyond keep
- * their contents and token ids until rewritten). */
+ * their contents and token ids until rewritten; the ring slots keep the
+ * positions they hold, so the windowed state at new_len exists only if they
+ * still hold its window -- hsw_kvm_window_safe_length says where it does). */
 hsw_status hsw_kvm_truncate(hsw_kvm *kvm, int32_t seq, int64_t new_len);
 /* Length, first pool row and capacity of a sequence. */
 hsw_status hsw_kvm_info(hsw_kvm *kvm, int32_t seq, int64_t *len, int64_t *seq_base, int64_t *max_len);
@@ -382,11 +385,17 @@ hsw_status hsw_kvm_drop_snapshot(hsw_kvm *kvm, int32_t snap);
 
 /* Window-safe reuse length of `tokens` (host, n ids) against the sequence:
  * the longest L <= the common prefix of tokens and the sequence's recorded
- * ids at which the windowed layers' state is available -- L = len when the
- * whole sequence is a prefix of tokens (the live rings hold its last
- * positions), else the highest live snapshot position within the common
- * prefix (*snap set to it; restore before use), else 0.  *snap = -1 unless a
- * snapshot is needed.  Returns -1 on bad arguments. */
+ * ids at which the windowed layers' state is available.  The state at L
+ * exists where ring slots hold every position the window of the token at L
+ * reads from the ring, max(0, L - window + 1) .. L - 1 (each slot holds the
+ * last position appended into it, or the one a restored snapshot held).
+ * Candidates: every L <= the live length under the live rings (truncate to
+ * L, then append; for a sequence longer than the window that is the live
+ * length itself and the one below it, unless a truncate and re-append left
+ * other runs), and each live snapshot at its own position when its copied
+ * rings hold that window (*snap set to it; restore before use); 0 always.
+ * The live state wins over a snapshot of the same length.  *snap = -1 unless
+ * a snapshot is needed.  Returns -1 on bad arguments. */
 int64_t hsw_kvm_window_safe_length(hsw_kvm *kvm, int32_t seq, const int32_t *tokens, int64_t n, int32_t *snap);
 
 /* ==================================================================

@@ -24,10 +24,18 @@ Readings where the pages leave a step open:
 * pool rows are handed out as one contiguous run per sequence (the attention
   calls address rows as seq_base + position), at the lowest row where
   ``max_len`` free rows start; the ring slot is the lowest free one;
-* the windowed layers' state exists at exactly three kinds of length: 0
-  (nothing to hold), the live length (the rings hold its last W positions)
-  and a live snapshot's position; of equal lengths the live state is
-  preferred, then the lowest snapshot id;
+* every ring slot holds one position (colibri "System One mode": position p
+  lives in slot p mod W).  Appending tokens means the caller runs the
+  attention calls over them, which write each appended position into its
+  slot; a truncate writes nothing; a restore brings back the slots the
+  snapshot copied.  The model records, per sequence, the position each slot
+  holds, and nothing else about the rings;
+* the windowed state at length L exists when the rings hold the positions the
+  next token's window reads from them, max(0, L - W + 1) .. L - 1 (the token
+  at L goes into its own slot first).  Live candidates are the lengths up to
+  the live length (a truncate reaches them); a snapshot is a candidate at its
+  own position when its copied slots hold that window.  Of equal lengths the
+  live state is preferred, then the lowest snapshot id;
 * a snapshot is released as soon as an append writes a token id different
   from the one its row held at a position below the snapshot's, and never
   comes back.
@@ -38,12 +46,13 @@ from __future__ import annotations
 class KvModel:
     CAPACITY, STALE, SHAPE = "capacity", "stale", "shape"
 
-    def __init__(self, ring_seqs: int, pool_rows: int, max_snapshots: int):
+    def __init__(self, ring_seqs: int, pool_rows: int, max_snapshots: int, window: int = 128):
+        self.window = window
         self.owner = [None] * pool_rows          # sequence owning each pool row
         self.ring = [False] * ring_seqs          # ring slot taken?
-        self.seqs = {}                           # seq -> dict(base, max_len, len, rows)
+        self.seqs = {}                           # seq -> dict(base, max_len, len, rows, slots)
         self.snap_slots = [False] * max_snapshots
-        self.snaps = {}                          # id -> dict(seq, pos, slot)
+        self.snaps = {}                          # id -> dict(seq, pos, slot, slots)
         self.next_id = 0
 
     # -- admission / release --------------------------------------------
@@ -64,7 +73,8 @@ class KvModel:
         self.ring[slot] = True
         for r in range(start, start + max_len):
             self.owner[r] = slot
-        self.seqs[slot] = dict(base=start, max_len=max_len, len=0, rows=[])
+        # slots: the position each ring slot holds (None: nothing written yet)
+        self.seqs[slot] = dict(base=start, max_len=max_len, len=0, rows=[], slots=[None] * self.window)
         return slot, start
 
     def release(self, seq: int):
@@ -96,6 +106,7 @@ class KvModel:
                     s["rows"][p] = t
             else:
                 s["rows"].append(t)
+            s["slots"][p % self.window] = p    # the attention calls write position p's K/V
         s["len"] = start + len(tokens)
         return start
 
@@ -128,7 +139,8 @@ class KvModel:
         self.snap_slots[slot] = True
         sid = self.next_id
         self.next_id += 1
-        self.snaps[sid] = dict(seq=seq, pos=self.seqs[seq]["len"], slot=slot)
+        self.snaps[sid] = dict(seq=seq, pos=self.seqs[seq]["len"], slot=slot,
+                               slots=list(self.seqs[seq]["slots"]))
         return sid
 
     def _drop(self, sid: int):
@@ -146,9 +158,15 @@ class KvModel:
             return self.STALE
         sn = self.snaps[sid]
         self.seqs[sn["seq"]]["len"] = sn["pos"]
+        self.seqs[sn["seq"]]["slots"] = list(sn["slots"])
         return sn["seq"], sn["slot"]
 
     # -- reuse -----------------------------------------------------------
+    def holds_window(self, slots, L: int) -> bool:
+        """Do these slots hold every position the window of the token at L
+        reads from the ring, max(0, L - W + 1) .. L - 1?"""
+        return all(slots[p % self.window] == p for p in range(max(0, L - self.window + 1), L))
+
     def window_safe_length(self, seq: int, tokens):
         """Brute force over every length L: the first L ids must equal the
         ids the rows hold, and the windowed state must exist at L."""
@@ -159,9 +177,10 @@ class KvModel:
         for L in range(0, len(tokens) + 1):
             if L > len(s["rows"]) or list(tokens[:L]) != s["rows"][:L]:
                 continue
-            if L == s["len"] and L > best:
+            if L <= s["len"] and self.holds_window(s["slots"], L) and L > best:
                 best, snap = L, -1
             for sid in sorted(self.snaps):
-                if self.snaps[sid]["seq"] == seq and self.snaps[sid]["pos"] == L and L > best:
+                sn = self.snaps[sid]
+                if sn["seq"] == seq and sn["pos"] == L and self.holds_window(sn["slots"], L) and L > best:
                     best, snap = L, sid
         return best, snap

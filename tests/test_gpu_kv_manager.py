@@ -83,7 +83,7 @@ def test_manager_matches_model_with_snapshots():
     sb = hsw.hsw_kvm_snapshot_bytes(cfg)
     snap_buf = torch.zeros((NS * sb // 2,), dtype=BF, device=DEV)
     kv = hsw.KvManager(cfg, k, v, snap_buf)
-    m = KvModel(S, R, NS)
+    m = KvModel(S, R, NS, window=16)
     saved = {}                                        # snapshot id -> ring contents it saw
     codes = {7: KvModel.CAPACITY, 8: KvModel.STALE, 2: KvModel.SHAPE}
 
