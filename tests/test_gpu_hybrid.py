@@ -27,6 +27,21 @@ from hybrid_sliding_window_amd import workloads as wl  # noqa: E402
 from hybrid_sliding_window_amd.hybrid import HybridStep  # noqa: E402
 
 
+def chunk_rows(T, seed, n_random=124):
+    """The first 130 rows of the chunk, its last 2 and n_random others drawn
+    from a seeded generator."""
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(0, 130), [T - 2, T - 1],
+                                     g.choice(np.arange(130, T - 2), n_random, replace=False)]))
+
+
+def full_decode_seqs(L, n=16, seed=9):
+    """The shortest and the longest decode sequence and n - 2 others."""
+    lo, hi = int(L.argmin()), int(L.argmax())
+    rest = [s for s in range(len(L)) if s not in (lo, hi)]
+    return sorted({lo, hi, *map(int, np.random.default_rng(seed).choice(rest, n - 2, replace=False))})
+
+
 def check_rope(x_in, y, pos, theta, what):
     ref = oracle.rope(f64(x_in), pos, theta)
     err = np.abs(f64(y) - ref)
@@ -49,8 +64,7 @@ def test_hybrid_windowed_layer_sampled(hs):
     d = hs.layers[0]
     swa = hs.swa
     calls = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(0)))
-    g = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([np.arange(0, 130), [T - 2, T - 1], g.choice(np.arange(130, T - 2), 30)]))
+    rows = chunk_rows(T, seed=7)
 
     note("hybrid windowed: rope (chunk -> staging)")
     calls["rope0"]()
@@ -87,11 +101,10 @@ def test_hybrid_windowed_layer_sampled(hs):
     note("hybrid windowed: swa decode")
     calls["swa_decode3"]()
     torch.cuda.synchronize()
-    seqs = sorted({int(P.argmin()), int(P.argmax()), 5, 77})
-    ref = oracle.ring_decode(f64(hs.q_rot_d[seqs]), P[seqs], f64(d["kring"][seqs]), f64(d["vring"][seqs]),
+    ref = oracle.ring_decode(f64(hs.q_rot_d), P, f64(d["kring"][:S]), f64(d["vring"][:S]),
                              sinks=f64(hs.sinks), **shape_kw(swa))
-    ma, mr = assert_close(f64(hs.out_d[seqs]), ref, what="hybrid swa_decode")
-    print(f"hybrid swa_decode sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    ma, mr = assert_close(f64(hs.out_d), ref, what="hybrid swa_decode")
+    print(f"hybrid swa_decode all {S} sequences: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 def test_hybrid_full_layer_sampled(hs):
@@ -99,7 +112,7 @@ def test_hybrid_full_layer_sampled(hs):
     d = hs.layers[1]
     full = hs.full
     calls = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(1)))
-    rows = np.array([0, 1, 2, 1000, 4095, 6000, 8190, 8191])
+    rows = chunk_rows(T, seed=8)
 
     note("hybrid full: rope (chunk -> pool)")
     calls["rope0"]()
@@ -128,7 +141,7 @@ def test_hybrid_full_layer_sampled(hs):
     note("hybrid full: split-K full decode")
     calls["full_decode3"]()
     torch.cuda.synchronize()
-    seqs = sorted({int(L.argmin()), int(L.argmax()), 9})
+    seqs = full_decode_seqs(L)
     got, refs = [], []
     qd = f64(hs.q_rot_d)
     for s in seqs:
@@ -143,8 +156,9 @@ def test_hybrid_full_layer_sampled(hs):
 def test_hybrid_fused_qrope_calls(hs):
     """The same two layers through the driver's fused q-RoPE calls (K/V-only
     RoPE, then the *_qrope attention calls on the raw q): both prefills
-    byte-identical to the unfused calls on the same state, both decodes
-    against the oracle fed the raw q rotated in fp64."""
+    byte-identical to the unfused calls on the same state and their sampled
+    rows held to the oracle fed the bytes the unfused calls consumed, both
+    decodes against the oracle fed the raw q rotated in fp64."""
     T, S, P0 = hs.T, hs.S, hs.P0
     d0, d1 = hs.layers[0], hs.layers[1]
     P = hs.L.numpy() - 1
@@ -167,17 +181,25 @@ def test_hybrid_fused_qrope_calls(hs):
     assert torch.equal(d0["kring"][S], kr_u) and torch.equal(d0["vring"][S], vr_u)
     assert torch.equal(hs.out, out_u), "fused windowed prefill differs from the unfused call"
     del out_u, kst_u
+    # gate: sampled fused rows against the oracle fed the unfused call's
+    # q_rot (the K/V-only RoPE leaves it in place), staging rows and the ring
+    # as it was before the commit
+    rows = chunk_rows(T, seed=11)
+    k, v, kpos0 = linear_kv_from_ring(f64(kr0), f64(vr0), P0, f64(hs.kst), f64(hs.vst))
+    ref = oracle.attn_linear(f64(hs.q_rot[rows]), np.arange(P0, P0 + T)[rows], k, v, kpos0, window=128,
+                             sinks=f64(hs.sinks), **shape_kw(hs.swa))
+    ma, mr = assert_close(f64(hs.out[rows]), ref, what="hybrid swa_prefill_qrope")
+    print(f"hybrid swa_prefill_qrope {len(rows)} rows: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
     note("hybrid fused windowed: decode")
     fused["rope2"]()
     fused["swa_decode3"]()
     torch.cuda.synchronize()
-    seqs = sorted({int(P.argmin()), int(P.argmax()), 5, 77})
-    qr = oracle.rope(f64(d0["qd"][seqs]), P[seqs], hs.swa.rope_theta)
-    ref = oracle.ring_decode(qr, P[seqs], f64(d0["kring"][seqs]), f64(d0["vring"][seqs]),
+    qr = oracle.rope(f64(d0["qd"]), P, hs.swa.rope_theta)
+    ref = oracle.ring_decode(qr, P, f64(d0["kring"][:S]), f64(d0["vring"][:S]),
                              sinks=f64(hs.sinks), **shape_kw(hs.swa))
-    ma, mr = assert_close(f64(hs.out_d[seqs]), ref, what="hybrid swa_decode_qrope")
-    print(f"hybrid swa_decode_qrope sampled {seqs}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    ma, mr = assert_close(f64(hs.out_d), ref, what="hybrid swa_decode_qrope")
+    print(f"hybrid swa_decode_qrope all {S} sequences: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
     plain = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(1, qrope=False)))
     fused = dict((n + str(i), f) for i, (n, f) in enumerate(hs.calls(1, qrope=True)))
@@ -191,13 +213,22 @@ def test_hybrid_fused_qrope_calls(hs):
     torch.cuda.synchronize()
     assert torch.equal(hs.out, out_u), "fused chunked prefill differs from the unfused call"
     del out_u
+    # gate: sampled fused rows against the oracle fed the unfused call's q_rot
+    # and the pool rows
+    rows = chunk_rows(T, seed=12, n_random=30)
+    k, v = f64(hs.kpool[:P0 + T]), f64(hs.vpool[:P0 + T])
+    ref = oracle.attn_linear(f64(hs.q_rot[rows]), np.arange(P0, P0 + T)[rows], k, v, 0, window=0,
+                             **shape_kw(hs.full))
+    del k, v
+    ma, mr = assert_close(f64(hs.out[rows]), ref, what="hybrid full_prefill_qrope")
+    print(f"hybrid full_prefill_qrope {len(rows)} rows: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
     note("hybrid fused full: split-K decode")
     fused["rope2"]()
     fused["full_decode3"]()
     torch.cuda.synchronize()
     L, base = hs.L.numpy(), hs.base_dec.numpy()
-    seqs = sorted({int(L.argmin()), int(L.argmax()), 9})
+    seqs = full_decode_seqs(L, seed=10)
     qr = oracle.rope(f64(d1["qd"][seqs]), L[seqs] - 1, hs.full.rope_theta)
     got, refs = [], []
     for i, s in enumerate(seqs):

@@ -309,25 +309,16 @@ def test_swa_prefill_ragged(hq, hkv, lam):
 
 
 @pytest.mark.parametrize("model", ["flash", "pro"])
-def test_swa_prefill_full_size_sampled(model):
-    """4 x 8192 from position 0: every head of sampled rows (the first 130,
-    the last 2 and 124 random per sequence), plus the ring commit."""
-    note(f"swa_prefill 4x8192 sampled {model}")
+def test_swa_prefill_full_size(model):
+    """4 x 8192 from position 0: every row and head of every sequence against
+    the oracle, plus the ring commit."""
+    note(f"swa_prefill 4x8192 all rows {model}")
     batch = wl.swa_prefill_batch(seed=2, **wl.model_kw(wl.MODELS[model], "swa"))
     q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
     check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
-    cu = batch["cu_seqlens"].tolist()
-    g = np.random.default_rng(2)
-    rows = []
-    for s in range(4):
-        r = list(range(cu[s], cu[s] + 130)) + [cu[s + 1] - 2, cu[s + 1] - 1]
-        r += list(g.choice(np.arange(cu[s] + 130, cu[s + 1] - 2), 124, replace=False))
-        rows.append(np.array(sorted(r)))
-    outs = oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb, rows)
-    got = np.concatenate([f64(out[torch.from_numpy(sel)]) for sel, _ in outs])
-    ref = np.concatenate([o for _, o in outs])
-    ma, mr = assert_close(got, ref, what=f"swa_prefill 4x8192 {model}")
-    print(f"swa_prefill 4x8192 sampled {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb)])
+    ma, mr = assert_close(f64(out), ref, what=f"swa_prefill 4x8192 {model}")
+    print(f"swa_prefill 4x8192 all {out.shape[0]} rows {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 def test_logit_shift_layer_fp32_chain():
@@ -369,6 +360,52 @@ def test_decode_matches_prefill_row():
                        vring, dev(batch["sinks"]), o)
     torch.cuda.synchronize()
     assert_close(f64(o)[0], f64(out)[299], what="decode vs prefill row")
+
+
+def permute_prefill_batch(batch, perm, per_seq_keys):
+    """The same sequences in the order `perm`: chunk rows moved with their
+    sequence, cu_seqlens and positions rebuilt, and the per-sequence tensors
+    named in per_seq_keys (rings, starts, pool bases) permuted."""
+    cu = batch["cu_seqlens"].tolist()
+    rows = torch.cat([torch.arange(cu[s], cu[s + 1]) for s in perm]) if cu[-1] else torch.zeros(0, dtype=torch.long)
+    lens = torch.tensor([cu[s + 1] - cu[s] for s in perm], dtype=torch.int64)
+    pb = dict(batch)
+    for k in ("q", "k", "v", "pos"):
+        pb[k] = batch[k][rows]
+    for k in per_seq_keys:
+        pb[k] = batch[k][list(perm)]
+    pb["cu_seqlens"] = torch.zeros(len(perm) + 1, dtype=torch.int64)
+    pb["cu_seqlens"][1:] = torch.cumsum(lens, 0)
+    pb["seq"] = torch.repeat_interleave(torch.arange(len(perm), dtype=torch.int32), lens)
+    return pb, rows
+
+
+def test_swa_prefill_batch_order_bitwise():
+    """A prefill row depends only on its own sequence (colibri 'Correctness';
+    P14): the same sequences in another order give byte-identical output
+    rows and ring commits."""
+    note("swa_prefill batch order")
+    batch = wl.swa_prefill_batch(seed=46, n_seqs=5, seqlens=(300, 17, 0, 700, 129),
+                                 start_pos=(0, 5000, 64, 130, 524000))
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    perm = [3, 0, 4, 2, 1]
+    pb, rows = permute_prefill_batch(batch, perm, ("kring", "vring", "start_pos"))
+    _, _, _, _, _, kring_p, vring_p, out_p = run_swa_prefill(pb)
+    assert torch.equal(out_p.cpu(), out.cpu()[rows]), "output rows depend on batch order"
+    assert torch.equal(kring_p.cpu(), kring.cpu()[perm]) and torch.equal(vring_p.cpu(), vring.cpu()[perm])
+
+
+def test_full_prefill_batch_order_bitwise():
+    """The chunked full prefill under a permutation of its sequences (pool rows
+    stay where they are; the sequences' bases move with them): byte-identical
+    output rows (colibri 'Correctness'; P14)."""
+    note("full_prefill batch order")
+    batch = wl.full_prefill_batch(seed=75, n_seqs=4, seqlens=(300, 77, 129, 1), start_pos=(3000, 100, 0, 40000))
+    _, _, _, out = run_full_prefill(batch)
+    perm = [2, 3, 0, 1]
+    pb, rows = permute_prefill_batch(batch, perm, ("start_pos", "seq_base", "ctx_len"))
+    _, _, _, out_p = run_full_prefill(pb)
+    assert torch.equal(out_p.cpu(), out.cpu()[rows]), "output rows depend on batch order"
 
 
 # ------------------------------------------------------- full decode
@@ -418,18 +455,30 @@ def test_full_decode_small(chunk, with_sink, model):
     print(f"full_decode chunk={chunk} sink={with_sink} {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
+def c4_sequences(L, n=None, seed=4):
+    """Sequences of the 64-sequence full decode held to the oracle: all of
+    them (n None), or the shortest, the longest and n - 2 others drawn from a
+    seeded generator."""
+    if n is None:
+        return list(range(len(L)))
+    lo, hi = int(L.argmin()), int(L.argmax())
+    rest = [s for s in range(len(L)) if s not in (lo, hi)]
+    pick = np.random.default_rng(seed).choice(rest, n - 2, replace=False)
+    return sorted({lo, hi, *map(int, pick)})
+
+
 @pytest.mark.parametrize("model", ["flash", "pro"])
-def test_full_decode_full_size_sampled(model):
-    """64 sequences with contexts U{32768..131072}: the shortest, the longest
-    and two random sequences checked against the oracle, all heads."""
-    note(f"full_decode 64 seqs sampled {model}")
+def test_full_decode_full_size(model):
+    """64 sequences with contexts U{32768..131072}: every head of all 64
+    sequences (Flash) or of 16 including the shortest and the longest (Pro,
+    whose pool is twice as large) against the oracle."""
+    note(f"full_decode 64 seqs {model}")
     batch = wl.full_decode_batch(seed=4, device=DEV, **wl.model_kw(wl.MODELS[model], "full"))
     q_rot, kpool, vpool, out = run_full_decode(batch)
-    L = batch["ctx_len"].numpy()
-    seqs = sorted({int(L.argmin()), int(L.argmax()), 17, 42})
+    seqs = c4_sequences(batch["ctx_len"].numpy(), None if model == "flash" else 16)
     ref = oracle_full_decode(batch, q_rot, kpool, vpool, seqs)
     ma, mr = assert_close(f64(out[seqs]), ref, what="full_decode 64 seqs")
-    print(f"full_decode 64 seqs {model} (sampled {seqs}): max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"full_decode 64 seqs {model} ({len(seqs)} checked): max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 # ------------------------------------------------------ full prefill
@@ -482,15 +531,27 @@ def test_full_prefill_ragged(model):
     print(f"full_prefill ragged {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
+def sampled_chunk_rows(T, seed, n_random=124):
+    """The first 130 rows of a chunk, its last 2 and n_random others drawn
+    from a seeded generator (sorted, distinct)."""
+    g = np.random.default_rng(seed)
+    r = list(range(130)) + [T - 2, T - 1]
+    r += list(g.choice(np.arange(130, T - 2), n_random, replace=False))
+    return np.array(sorted(set(r)))
+
+
 @pytest.mark.parametrize("model", ["flash", "pro"])
 def test_full_prefill_chunk_8192_after_131072_sampled(model):
+    """8192-token chunk after 131072 prior rows: every head of 256 rows (the
+    first 130, the last 2 and 124 random ones, which reach well over a
+    hundred of the 64-row query blocks) against the oracle."""
     note(f"full_prefill 8192 @ 131072 sampled {model}")
     batch = wl.full_prefill_batch(seed=5, device=DEV, **wl.model_kw(wl.MODELS[model], "full"))
     q_rot, kpool, vpool, out = run_full_prefill(batch)
-    rows = [np.array([0, 1, 2, 1000, 4095, 6000, 8190, 8191])]
+    rows = [sampled_chunk_rows(8192, seed=5)]
     idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, rows)
     ma, mr = assert_close(f64(out[torch.from_numpy(idx)]), ref, what="full_prefill 8192")
-    print(f"full_prefill 8192@131072 sampled {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"full_prefill 8192@131072 {len(idx)} rows {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 def test_full_prefill_values_beyond_fp16_range():
@@ -679,9 +740,9 @@ def run_swa_prefill_qrope(batch):
 def test_swa_prefill_qrope_bitwise_equals_rope_then_prefill(model):
     """The fused call rotates q with the RoPE call's own arithmetic, so its
     output, staging rows and ring commit are byte-identical to RoPE then
-    hsw_swa_prefill (which the other prefill tests hold to the oracle); the
-    error of the chain from the raw inputs (rotation in fp64, colibri 'What
-    the engine implements') is reported."""
+    hsw_swa_prefill; every output row is held to the oracle fed the bytes the
+    unfused call consumed, and the error of the chain from the raw inputs
+    (rotation in fp64, colibri 'What the engine implements') is reported."""
     note(f"swa_prefill_qrope bitwise {model}")
     batch = wl.swa_prefill_batch(seed=81, n_seqs=4, seqlens=(300, 17, 1000, 129),
                                  start_pos=(0, 5000, 130, 524000), **wl.model_kw(wl.MODELS[model], "swa"))
@@ -690,6 +751,11 @@ def test_swa_prefill_qrope_bitwise_equals_rope_then_prefill(model):
     assert torch.equal(kst2.cpu(), kst.cpu()) and torch.equal(vst2.cpu(), vst.cpu())
     assert torch.equal(kring2.cpu(), kring.cpu()) and torch.equal(vring2.cpu(), vring.cpu())
     assert torch.equal(out2.cpu(), out.cpu()), "fused prefill differs from RoPE + prefill"
+    # gate: the fused output against the oracle fed the q_rot, staging and
+    # ring bytes of the unfused call (exactly what the fused call computes
+    # from, by the bitwise equality above)
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb)])
+    gma, gmr = assert_close(f64(out2), ref, what=f"swa_prefill_qrope {model}")
     # chain from the raw inputs: q and k rotated in fp64
     shape = batch["shape"]
     P = batch["pos"].numpy()
@@ -705,7 +771,8 @@ def test_swa_prefill_qrope_bitwise_equals_rope_then_prefill(model):
     # reported, not gated: it adds the bf16 storage of the rotated q and k,
     # which the bitwise match above already ties to the gated unfused path
     ma, mr = errors(f64(out2), np.concatenate(refs))
-    print(f"swa_prefill_qrope {model}: bitwise equal to RoPE + prefill; chain max_abs={ma:.2e} mean_rel={mr:.2e}")
+    print(f"swa_prefill_qrope {model}: bitwise equal to RoPE + prefill; bf16-in max_abs={gma:.2e} "
+          f"mean_rel={gmr:.2e}; chain max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 @pytest.mark.parametrize("model", ["flash", "pro"])
@@ -768,8 +835,9 @@ def test_full_prefill_qrope_bitwise_equals_rope_then_prefill(case, model):
     """The fused chunked prefill rotates q with the RoPE call's arithmetic and
     stores it as bf16 in the same registers the unfused kernel loads q_rot
     into, so its output is byte-identical to RoPE then hsw_full_prefill_chunk
-    (held to the oracle by the other full prefill tests), over ragged chunks
-    and at the full size, where every output row is compared."""
+    over ragged chunks and at the full size, where every output row is
+    compared; the fused rows are also held to the oracle fed the unfused
+    call's q_rot and pool rows."""
     note(f"full_prefill_qrope bitwise {case} {model}")
     kw = wl.model_kw(wl.MODELS[model], "full")
     if case == "ragged":
@@ -782,7 +850,19 @@ def test_full_prefill_qrope_bitwise_equals_rope_then_prefill(case, model):
     out2 = run_full_prefill_qrope(batch, kpool0, vpool0)
     assert torch.equal(kpool0, kpool) and torch.equal(vpool0, vpool)
     assert torch.equal(out2, out), "fused chunked prefill differs from RoPE + prefill"
-    print(f"full_prefill_qrope {case} {model}: bitwise equal to RoPE + prefill over {out.shape[0]} rows")
+    # gate: the fused output against the oracle fed the unfused call's q_rot
+    # and pool rows (all rows of the ragged chunks; 256 rows of the full one,
+    # drawn apart from the unfused test's sample)
+    cu = batch["cu_seqlens"].tolist()
+    if case == "ragged":
+        rows = [np.arange(cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+    else:
+        rows = [sampled_chunk_rows(8192, seed=6)]
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, rows)
+    ma, mr = assert_close(f64(out2[torch.from_numpy(idx).to(out2.device)]), ref,
+                          what=f"full_prefill_qrope {case} {model}")
+    print(f"full_prefill_qrope {case} {model}: bitwise equal to RoPE + prefill over {out.shape[0]} rows; "
+          f"{len(idx)} rows against the oracle: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 @pytest.mark.parametrize("model", ["flash", "pro"])
@@ -800,8 +880,7 @@ def test_full_decode_qrope_against_raw_chain(case, model):
         seqs, chunk = list(range(len(lengths))), 128
     else:
         batch = wl.full_decode_batch(seed=4, device=DEV, **kw)
-        L = batch["ctx_len"].numpy()
-        seqs, chunk = sorted({int(L.argmin()), int(L.argmax()), 17, 42}), 2048
+        seqs, chunk = c4_sequences(batch["ctx_len"].numpy(), 16, seed=5), 2048
     shape = batch["shape"]
     S = batch["ctx_len"].shape[0]
     sinks = dev(batch.get("sinks"))
