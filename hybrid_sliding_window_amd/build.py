@@ -1,11 +1,14 @@
 """Build libhsw.so (the C-ABI library of hand-written gfx950 HIP kernels) in
-place, next to this file.
+place, next to this file, and libhsw_checked.so, the same sources built with
+HSW_CHECK_DEVICE=1 (device-resident arguments checked on the device before
+each call's kernels run).
 
     python -m hybrid_sliding_window_amd.build
 
 Each .hip source is compiled separately (in parallel) for --offload-arch=gfx950
-and linked into one shared library.  Packed-fp32 instruction selection is
-disabled for the device code (some of those forms are not trusted here).
+and linked into one shared library per build.  Packed-fp32 instruction
+selection is disabled for the device code (some of those forms are not
+trusted here).
 """
 from __future__ import annotations
 
@@ -21,7 +24,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libhsw.so")
+CHECKED_LIB = os.path.join(HERE, "libhsw_checked.so")
 BUILD_DIR = os.path.join(HERE, "_build")
+CHECKED_BUILD_DIR = os.path.join(HERE, "_build_checked")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -44,9 +49,11 @@ RELAXED_NAN = {"swa_prefill.hip", "full_prefill.hip"}
 RELAXED_NAN_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, build_dir: str, checked: bool) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     extra = RELAXED_NAN_FLAGS if os.path.basename(src) in RELAXED_NAN else []
+    if checked:
+        extra = extra + ["-DHSW_CHECK_DEVICE=1"]
     cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -54,19 +61,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, checked: bool = True) -> str:
+    """Compile and link libhsw.so, and (checked=True) libhsw_checked.so."""
+    builds = [(BUILD_DIR, LIB, False)] + ([(CHECKED_BUILD_DIR, CHECKED_LIB, True)] if checked else [])
+    srcs = sources()
+    jobs = []
+    for d, _, chk in builds:
+        os.makedirs(d, exist_ok=True)
+        jobs += [(src, d, chk) for src in srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(srcs)
+    for i, (_, lib, _) in enumerate(builds):
+        _link(objs[i * n:(i + 1) * n], lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

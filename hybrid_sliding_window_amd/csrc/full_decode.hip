@@ -54,6 +54,7 @@ struct StepRegs {
 
 template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnArgs a) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     __shared__ __attribute__((aligned(16))) uint16_t vt[4 * DV * VT_STRIDE];
     __shared__ float red_m[4][16], red_l[4][16];
     __shared__ float qcs[QROPE ? 4 : 1][64];  // per wave: cos, sin of the 32 angles
@@ -251,6 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
 
 // One wave per (sequence, q head); lane owns value dims 2*lane, 2*lane+1.
 __global__ __launch_bounds__(kThreads) void full_decode_combine_kernel(AttnArgs a) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (wid >= (int64_t)a.n_seqs * a.hq) return;

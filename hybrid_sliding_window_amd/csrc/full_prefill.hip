@@ -22,9 +22,14 @@
 //   softmax          online in log2 units; the reference max is raised only
 //                    when a chunk's max exceeds it by more than 2^8 (P <= 256),
 //                    so the O rescale is rare
-//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P split into bf16 hi + lo
-//                    (about 16 significant bits, V exact in bf16); the V^T
-//                    operand is read from row-major V by ds_read_b64_tr_b16.
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_f16: P rounded to fp16 (11
+//                    significant bits; P <= 256 keeps it in range) times V
+//                    converted to fp16 in LDS, exact for every bf16 value of
+//                    magnitude below 65536.  A 32-column block of a chunk
+//                    holding a larger or non-finite value stays bf16 and takes
+//                    the fp16-rounded P split exactly into bf16 hi + lo
+//                    (v_mfma_f32_16x16x32_bf16 twice).  The V^T operand is
+//                    read from row-major V by ds_read_b64_tr_b16.
 // LDS holds K and V in MFMA fragment order (the load side places each
 // 16-byte piece where a lane will read it), so every LDS read is a contiguous
 // run in lane order, free of bank conflicts.  Block ids are remapped so
@@ -118,6 +123,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 
 template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, int nqb) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     constexpr int BQ = 128 / G;
     // Three stages, each its own LDS object so the compiler can tell that a
     // read of one stage does not depend on the loads in flight to another.
@@ -146,7 +152,11 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     const int64_t tok0 = a.cu_seqlens[s];
     const int len = (int)(a.cu_seqlens[s + 1] - tok0);
     if (qb * BQ >= len) return;
-    const int start = (int)a.start_pos[s];
+    // Positions index pool rows (base + position < pool_rows < 2^31, checked
+    // on the host), so they fit in an int; an out-of-contract start is
+    // clamped into [0, pool_rows] and its keys to the pool below.
+    const int64_t start64 = a.start_pos[s];
+    const int start = (int)(start64 < 0 ? 0 : start64 > a.pool_rows ? a.pool_rows : start64);
     const int p0 = start + qb * BQ;                         // first query position
     const int plast = start + min(len, qb * BQ + BQ) - 1;   // last query position
     const int64_t base = a.seq_base[s];

@@ -26,6 +26,7 @@ constexpr int kSlices = kMaxDim / kWave;
 
 template <typename T, typename TO>
 __global__ __launch_bounds__(kThreads) void generic_attn_kernel(AttnArgs a) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     const int lane = threadIdx.x % kWave;
     const int64_t wid = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     if (wid >= a.n_rows * a.hq) return;
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void generic_attn_kernel(AttnArgs a) {
 // (pos mod W).  One block per (sequence, ring row).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void ring_commit_kernel(AttnArgs a) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     const int s = blockIdx.y;
     const int i = blockIdx.x;
     const int64_t tok0 = a.cu_seqlens[s];

@@ -10,8 +10,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/hsw.h"
+#include "dev_check.h"
 #include "hsw_launch.h"
+
+#ifndef HSW_CHECK_DEVICE
+#define HSW_CHECK_DEVICE 0
+#endif
 
 namespace {
 thread_local char g_err[512] = "";
@@ -33,6 +40,81 @@ hsw_status fail(hsw_status st, const char *fmt, ...) {
 
 namespace {
 using hsw::fail;
+namespace dc = hsw::devcheck;
+
+// Pool rows are addressed by int positions in the kernels; no pool that fits
+// in one GPU's memory comes near this many rows.
+constexpr int64_t kMaxPoolRows = 0x7fffffffLL;
+
+// ------------------------------------------------------------ device checks
+#if HSW_CHECK_DEVICE
+// Per device: [0] the code of a contract violation found (0: none), [1] the
+// index of the element that broke it.  Module memory of the checked build:
+// nothing is allocated.  Host code takes its address once per device with
+// hipGetSymbolAddress and uses only that address.
+__device__ __align__(16) unsigned long long g_dev_check[2];
+
+__global__ __launch_bounds__(256) void check_kernel(dc::Inputs in, unsigned long long *flag) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < in.n; i += (int64_t)gridDim.x * 256) {
+        const int32_t c = dc::check_element(in, i);
+        if (c != 0 && atomicCAS(&flag[0], 0ull, (unsigned long long)c) == 0ull) flag[1] = (unsigned long long)i;
+    }
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_flag_mu;
+unsigned long long *g_flag[kMaxDevices];
+
+// The current device's flag.
+hsw_status device_flag(unsigned long long **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(HSW_E_LAUNCH, "device %d is beyond the %d the checks keep a flag for", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_flag_mu);
+    if (!g_flag[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_dev_check));
+        if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+        g_flag[dev] = static_cast<unsigned long long *>(p);
+    }
+    *out = g_flag[dev];
+    return HSW_OK;
+}
+#endif
+
+// Checked builds: launch the check of a call's device-resident arguments on
+// `s`, ahead of the call's kernels, and hand back the flag those kernels
+// test.  Release builds: no launch, flag NULL.
+hsw_status device_checks(const dc::Inputs &in, hipStream_t s, const unsigned long long **flag) {
+    *flag = nullptr;
+#if HSW_CHECK_DEVICE
+    unsigned long long *f = nullptr;
+    hsw_status st = device_flag(&f);
+    if (st) return st;
+    if (in.n > 0) {
+        int64_t blocks = (in.n + 255) / 256;
+        if (blocks > 1024) blocks = 1024;
+        hipLaunchKernelGGL(check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, in, f);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(HSW_E_LAUNCH, "device check: %s", hipGetErrorString(e));
+    }
+    *flag = f;
+#else
+    (void)in;
+    (void)s;
+#endif
+    return HSW_OK;
+}
+
+dc::Inputs check_inputs(int32_t call, int64_t n) {
+    dc::Inputs in;
+    memset(&in, 0, sizeof in);
+    in.call = call;
+    in.n = n;
+    return in;
+}
 
 bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
@@ -109,6 +191,7 @@ hsw_status full_decode_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t ma
     if (st) return st;
     if (n_seqs < 0 || max_ctx < 0 || pool_rows < 0)
         return fail(HSW_E_SHAPE, "n_seqs, max_ctx and pool_rows must be >= 0");
+    if (pool_rows > kMaxPoolRows) return fail(HSW_E_SHAPE, "pool_rows exceeds 2^31 - 1");
     if (chunk <= 0 || chunk % 128 != 0) return fail(HSW_E_SHAPE, "chunk (%d) must be a positive multiple of 128", chunk);
     if (!q) return fail(HSW_E_NULL, qrope ? "q is NULL" : "q_rot is NULL");
     REQUIRE_PTR(ctx_len); REQUIRE_PTR(seq_base); REQUIRE_PTR(k_pool);
@@ -134,6 +217,9 @@ hsw_status full_decode_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t ma
     a.q = q; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.ctx_len = ctx_len;
     a.seq_base = seq_base; a.out = out; a.ws = ws; a.n_seqs = n_seqs; a.n_rows = n_seqs;
     a.max_seqlen = max_ctx; a.pool_rows = pool_rows; a.n_chunks = (int)nc;
+    dc::Inputs ci = check_inputs(dc::kFullDecode, n_seqs);
+    ci.ctx_len = ctx_len; ci.seq_base = seq_base; ci.max_ctx = max_ctx; ci.pool_rows = pool_rows;
+    if ((st = device_checks(ci, s, &a.dev_flag))) return st;
     hipError_t e = (qrope || hsw::full_decode_fast_ok(a, sh->dtype, sh->out_dtype))
                        ? hsw::launch_full_decode(a, s)
                        : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
@@ -148,6 +234,7 @@ hsw_status full_prefill_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t m
     if (st) return st;
     if (n_seqs < 0 || max_seqlen < 0 || pool_rows < 0)
         return fail(HSW_E_SHAPE, "n_seqs, max_seqlen and pool_rows must be >= 0");
+    if (pool_rows > kMaxPoolRows) return fail(HSW_E_SHAPE, "pool_rows exceeds 2^31 - 1");
     if (!q) return fail(HSW_E_NULL, qrope ? "q is NULL" : "q_rot is NULL");
     REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(start_pos); REQUIRE_PTR(seq_base);
     REQUIRE_PTR(k_pool); REQUIRE_PTR(v_pool); REQUIRE_PTR(out);
@@ -166,6 +253,10 @@ hsw_status full_prefill_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t m
     a.q = q; a.k_main = k_pool; a.v_main = v_pool; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
     a.start_pos = start_pos; a.seq_base = seq_base; a.out = out; a.n_seqs = n_seqs;
     a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen; a.pool_rows = pool_rows;
+    dc::Inputs ci = check_inputs(dc::kFullPrefill, n_seqs);
+    ci.cu_seqlens = cu_seqlens; ci.start_pos = start_pos; ci.seq_base = seq_base;
+    ci.max_seqlen = max_seqlen; ci.pool_rows = pool_rows;
+    if ((st = device_checks(ci, s, &a.dev_flag))) return st;
     hipError_t e = (qrope || hsw::full_prefill_fast_ok(a, sh->dtype, sh->out_dtype))
                        ? hsw::launch_full_prefill(a, s)
                        : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
@@ -186,13 +277,41 @@ const char *hsw_status_str(hsw_status s) {
         case HSW_E_LAUNCH: return "HSW_E_LAUNCH: kernel launch failed";
         case HSW_E_CAPACITY: return "HSW_E_CAPACITY: a KV pool lacks room";
         case HSW_E_STALE: return "HSW_E_STALE: the snapshot was released";
+        case HSW_E_DEVICE_INPUT: return "HSW_E_DEVICE_INPUT: a device-resident argument broke the contract";
         default: return "unknown hsw_status";
     }
 }
 
 const char *hsw_last_error(void) { return g_err; }
 
-const char *hsw_version(void) { return "hsw 0.1 gfx950"; }
+const char *hsw_version(void) { return HSW_CHECK_DEVICE ? "hsw 0.2 gfx950 checked" : "hsw 0.2 gfx950"; }
+
+int32_t hsw_device_checks_enabled(void) { return HSW_CHECK_DEVICE ? 1 : 0; }
+
+hsw_status hsw_device_check_status(hsw_stream_t stream, int32_t *code, int64_t *index) {
+    if (code) *code = -1;
+    if (index) *index = -1;
+#if HSW_CHECK_DEVICE
+    unsigned long long *f = nullptr;
+    hsw_status st = device_flag(&f);
+    if (st) return st;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    unsigned long long h[2] = {0, 0};
+    e = hipMemcpy(h, f, sizeof h, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "reading the check flag: %s", hipGetErrorString(e));
+    if (code) *code = (int32_t)h[0];
+    if (index) *index = h[0] ? (int64_t)h[1] : -1;
+    if (h[0] == 0) return HSW_OK;
+    const unsigned long long zero[2] = {0, 0};
+    e = hipMemcpy(f, zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "clearing the check flag: %s", hipGetErrorString(e));
+    return fail(HSW_E_DEVICE_INPUT, "device check code %d at element %lld", (int)h[0], (long long)h[1]);
+#else
+    (void)stream;
+    return HSW_OK;
+#endif
+}
 
 hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens, const void *q,
                                      const void *k, const void *v, const int64_t *pos,
@@ -229,6 +348,9 @@ hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens,
     for (int i = 0; i < sh->rope_dim / 2; ++i) a.inv_freq[i] = inv_freq(sh, i);
     a.hq = sh->n_q_heads; a.hkv = sh->n_kv_heads; a.dqk = sh->d_qk; a.dv = sh->d_v;
     a.rope_dim = sh->rope_dim; a.window = sh->window; a.dst_kind = dst_kind;
+    dc::Inputs ci = check_inputs(dc::kRope, n_tokens);
+    ci.dst_kind = dst_kind; ci.pos = pos; ci.seq = seq; ci.seq_base = seq_base; ci.dst_capacity = dst_capacity;
+    if ((st = device_checks(ci, (hipStream_t)stream, &a.dev_flag))) return st;
     return launched(hsw::launch_rope(a, sh->dtype, (hipStream_t)stream), "rope_partial_kv_write");
 }
 
@@ -253,6 +375,9 @@ hsw_status hsw_swa_prefill(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max
     a.sinks = sinks; a.cu_seqlens = cu_seqlens; a.start_pos = start_pos; a.out = out;
     a.n_seqs = n_seqs; a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen;
     hipStream_t s = (hipStream_t)stream;
+    dc::Inputs ci = check_inputs(dc::kSwaPrefill, n_seqs);
+    ci.cu_seqlens = cu_seqlens; ci.start_pos = start_pos; ci.max_seqlen = max_seqlen;
+    if ((st = device_checks(ci, s, &a.dev_flag))) return st;
     hipError_t e = hsw::swa_prefill_fast_ok(a, sh->dtype, sh->out_dtype)
                        ? hsw::launch_swa_prefill(a, s)
                        : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
@@ -278,6 +403,9 @@ hsw_status hsw_swa_decode(const hsw_attn_shape *sh, int32_t n_seqs, const int64_
     a.q = q_rot; a.k_main = k_ring; a.v_main = v_ring; a.sinks = sinks; a.pos = pos; a.out = out;
     a.n_seqs = n_seqs; a.n_rows = n_seqs;
     hipStream_t s = (hipStream_t)stream;
+    dc::Inputs ci = check_inputs(dc::kSwaDecode, n_seqs);
+    ci.pos = pos;
+    if ((st = device_checks(ci, s, &a.dev_flag))) return st;
     hipError_t e = hsw::swa_decode_fast_ok(a, sh->dtype, sh->out_dtype)
                        ? hsw::launch_swa_decode(a, s)
                        : hsw::launch_generic_attn(a, sh->dtype, sh->out_dtype, s);
@@ -309,6 +437,9 @@ hsw_status hsw_swa_prefill_qrope(const hsw_attn_shape *sh, int32_t n_seqs, int64
     a.sinks = sinks; a.cu_seqlens = cu_seqlens; a.start_pos = start_pos; a.out = out;
     a.n_seqs = n_seqs; a.max_seqlen = max_seqlen; a.n_rows = (int64_t)n_seqs * max_seqlen;
     hipStream_t s = (hipStream_t)stream;
+    dc::Inputs ci = check_inputs(dc::kSwaPrefill, n_seqs);
+    ci.cu_seqlens = cu_seqlens; ci.start_pos = start_pos; ci.max_seqlen = max_seqlen;
+    if ((st = device_checks(ci, s, &a.dev_flag))) return st;
     if ((st = launched(hsw::launch_swa_prefill(a, s), "swa_prefill_qrope"))) return st;
     return launched(hsw::launch_ring_commit(a, sh->dtype, s), "swa_prefill_qrope ring commit");
 }
@@ -332,6 +463,9 @@ hsw_status hsw_swa_decode_qrope(const hsw_attn_shape *sh, int32_t n_seqs, const 
     if (n_seqs == 0) return HSW_OK;
     a.q = q; a.k_main = k_ring; a.v_main = v_ring; a.sinks = sinks; a.pos = pos; a.out = out;
     a.n_seqs = n_seqs; a.n_rows = n_seqs;
+    dc::Inputs ci = check_inputs(dc::kSwaDecode, n_seqs);
+    ci.pos = pos;
+    if ((st = device_checks(ci, (hipStream_t)stream, &a.dev_flag))) return st;
     return launched(hsw::launch_swa_decode(a, (hipStream_t)stream), "swa_decode_qrope");
 }
 
@@ -465,6 +599,9 @@ hsw_status hsw_vit_attention(const hsw_attn_shape *sh, int32_t n_images, int64_t
         return fail(HSW_E_SHAPE, "grid too large");
     a.q = q; a.k = k; a.v = v; a.out = out; a.cu_seqlens = cu_seqlens; a.order = order; a.sinks = sinks;
     a.n_images = n_images;
+    dc::Inputs ci = check_inputs(dc::kVit, n_images);
+    ci.cu_seqlens = cu_seqlens; ci.order = order; ci.max_seqlen = max_len;
+    if ((st = device_checks(ci, (hipStream_t)stream, &a.dev_flag))) return st;
     return launched(hsw::launch_vit_attn(a, max_len, (hipStream_t)stream), "vit_attention");
 }
 

@@ -48,17 +48,20 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) {
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-// Streaming (non-temporal) forms, for bytes a kernel reads or writes exactly
-// once: the access is marked so it does not displace reused lines in L2 and
-// the Infinity Cache.
-__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-__device__ __forceinline__ void st16_nt(void *p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-}
-__device__ __forceinline__ void st8_nt(void *p, u32x2 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+// Builds with HSW_CHECK_DEVICE=1 launch a check of the call's device-resident
+// arguments before its kernels; each kernel then returns at once if the check
+// recorded a violation (the flag is written by an earlier kernel on the same
+// stream).  Release builds compile this to nothing.
+#ifndef HSW_CHECK_DEVICE
+#define HSW_CHECK_DEVICE 0
+#endif
+__device__ __forceinline__ bool checks_failed(const unsigned long long *flag) {
+#if HSW_CHECK_DEVICE
+    return flag != nullptr && *flag != 0ull;
+#else
+    (void)flag;
+    return false;
+#endif
 }
 
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {

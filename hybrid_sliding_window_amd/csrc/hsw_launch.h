@@ -14,6 +14,7 @@ struct RopeArgs {
     const int64_t *seq_base;
     void *k_dst, *v_dst, *q_rot;
     int64_t *dst_index_out;
+    const unsigned long long *dev_flag;  // checked builds: nonzero once an argument broke the contract
     int64_t n_tokens, dst_capacity;
     int hq, hkv, dqk, dv, rope_dim, window, dst_kind;
     double inv_freq[128];      // theta^(-2i/rope_dim), i < rope_dim/2
@@ -36,6 +37,7 @@ struct AttnArgs {
     const int64_t *seq_base;   // full kinds
     void *out;
     void *ws;                  // full decode partials
+    const unsigned long long *dev_flag;  // checked builds: nonzero once an argument broke the contract
     int64_t n_rows;            // query rows (tokens or sequences)
     int64_t max_seqlen;        // prefill: bound on chunk length; full decode: max_ctx
     int64_t pool_rows;         // full kinds: rows in the pool
@@ -68,6 +70,7 @@ struct VitArgs {
     const int32_t *order;       // picture-local token at each position of the order, or null
     const float *sinks;         // learned sink logits [Hq], or null
     void *out;
+    const unsigned long long *dev_flag;  // checked builds: nonzero once an argument broke the contract
     int n_images, hq, hkv, window, sink_key;
     float scale;
 };

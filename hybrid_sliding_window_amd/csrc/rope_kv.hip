@@ -56,6 +56,7 @@ template <> struct Chunk8<float> {  // 8 fp32 = 32 bytes
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rope_kv_kernel(RopeArgs a) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     __shared__ float cs[kMaxHalf], sn[kMaxHalf];
     __shared__ int64_t dst_row;  // element row of head 0: ring (seq*Hkv)*window + slot; pool/staging row*Hkv
     const int64_t t = blockIdx.x;

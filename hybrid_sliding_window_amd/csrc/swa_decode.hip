@@ -101,6 +101,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     // V of the current and the next item, each wave's 32 slots in its own
     // 8 KiB; after a wave's PV it holds that wave's O partial [G][PS] fp32.
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[VBUF], vb1[VBUF];
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int slot = 32 * w + 16 * h + 4 * quad + j;
-                const int back = ((int)P - slot) & (W - 1);
+                const int back = ((int)(P & (W - 1)) - slot) & (W - 1);  // (P - slot) mod W, any int64 P
                 const float v = back <= pc ? sacc[h][j] * scale2 : -INFINITY;
                 sv[4 * h + j] = v;
                 mx = fmaxf(mx, v);

@@ -22,9 +22,14 @@
 //   softmax          online in log2 units over logits only (the sink joins the
 //                    denominator at the end); the reference max is raised only
 //                    when a chunk's max exceeds it by more than 2^8 (P <= 256)
-//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P split into bf16 hi + lo
-//                    (about 16 significant bits, V exact in bf16); the V^T
-//                    operand is read from row-major V by ds_read_b64_tr_b16.
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_f16: P rounded to fp16 (11
+//                    significant bits; P <= 256 keeps it in range) times V
+//                    converted to fp16 in LDS, exact for every bf16 value of
+//                    magnitude below 65536.  A 32-column block of a chunk
+//                    holding a larger or non-finite value stays bf16 and takes
+//                    the fp16-rounded P split exactly into bf16 hi + lo
+//                    (v_mfma_f32_16x16x32_bf16 twice).  The V^T operand is
+//                    read from row-major V by ds_read_b64_tr_b16.
 // LDS holds K and V in MFMA fragment order (the load side places each
 // 16-byte piece where a lane will read it), so every LDS read is a contiguous
 // run in lane order, free of bank conflicts.  Block ids are remapped so consecutive query
@@ -131,6 +136,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 
 template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, int nqb) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     constexpr int BQ = 128 / G;
     // Three stages, each its own LDS object so the compiler can tell that a
     // read of one stage does not depend on the loads in flight to another.
@@ -159,10 +165,16 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     const int64_t tok0 = a.cu_seqlens[s];
     const int len = (int)(a.cu_seqlens[s + 1] - tok0);
     if (qb * BQ >= len) return;
-    const int start = (int)a.start_pos[s];
-    const int p0 = start + qb * BQ;                 // first query position
-    const int plast = start + min(len, qb * BQ + BQ) - 1;
-    const int kstart = max(0, p0 - (W - 1));        // band: kstart .. plast
+    // Positions are taken relative to the chunk start (its first token is 0),
+    // so every position the block handles fits in an int whatever the int64
+    // start: relative key kp < 0 is absolute start + kp, which exists iff
+    // >= 0, and lives in ring slot (start + kp) mod W.
+    const int64_t start = a.start_pos[s];
+    const int kmin = start < W - 1 ? -(int)start : -(W - 1);  // lowest relative key that exists
+    const int smod = (int)(start & (W - 1));                   // ring slot of relative position 0
+    const int p0 = qb * BQ;                         // first query position
+    const int plast = min(len, qb * BQ + BQ) - 1;
+    const int kstart = max(kmin, p0 - (W - 1));     // band: kstart .. plast
     const int nch = max((plast - kstart + KC) / KC, 1);  // >= 1 (stated so the compiler knows the loop runs)
 
     // this lane's rotary frequency (fused q-RoPE), loaded before any
@@ -224,27 +236,27 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     const uint32_t koff_l = (uint32_t)(col * krow + 16 * quad);
     const uint32_t voff_l = (uint32_t)(vrow_l * vrow + vbyte_l);
 
-    // Key at band position kp: ring slot (kp mod W) before the chunk start,
-    // staging row (kp - start) from it; positions past plast are clamped to
-    // plast (finite data, masked).
+    // Key at relative band position kp: ring slot (start + kp) mod W before
+    // the chunk start, staging row kp from it; positions past plast are
+    // clamped to plast (finite data, masked).
     auto key_src = [&](int kp, const char *st_base, const char *ring_base, int64_t row_bytes,
                        int ring_row_bytes) -> const char * {
-        return kp >= start ? st_base + (int64_t)(kp - start) * row_bytes
-                           : ring_base + (int64_t)(kp % W) * ring_row_bytes;
+        return kp >= 0 ? st_base + (int64_t)kp * row_bytes
+                       : ring_base + (int64_t)((smod + kp) & (W - 1)) * ring_row_bytes;
     };
     auto issue = [&](int c, uint16_t *ksd, uint16_t *vsd) {
         const int k0 = kstart + c * KC;
-        if (k0 >= start && k0 + KC - 1 <= plast) {
+        if (k0 >= 0 && k0 + KC - 1 <= plast) {
 #pragma unroll
             for (int i = 0; i < K_LOADS; ++i) {
                 const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
-                load_lds16_s(kst + (int64_t)(k0 + 16 * h - start) * krow + 64 * st, koff_l,
+                load_lds16_s(kst + (int64_t)(k0 + 16 * h) * krow + 64 * st, koff_l,
                              (const char *)ksd + j * 1024);
             }
 #pragma unroll
             for (int i = 0; i < V_LOADS; ++i) {
                 const int j = 4 * i + w, hh = j / 4;
-                load_lds16_s(vst + (int64_t)(k0 + 16 * hh - start) * vrow + 64 * (j % 4), voff_l,
+                load_lds16_s(vst + (int64_t)(k0 + 16 * hh) * vrow + 64 * (j % 4), voff_l,
                              (const char *)vsd + j * 1024);
             }
         } else {
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
 #pragma unroll
         for (int e = lane; e < NP * 32; e += 64) {
             float cv, sv;
-            rope_cos_sin((int64_t)(pw + e / 32), invf, cv, sv);
+            rope_cos_sin(start + pw + e / 32, invf, cv, sv);
             tc[e] = cv;
             ts[e] = sv;
         }

@@ -23,8 +23,12 @@
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16 (K from LDS in fragment order)
 //   softmax          online in log2 units, the reference max raised only when
 //                    a chunk's max exceeds it by more than 2^8
-//   O^T += V^T P^T   v_mfma_f32_16x16x32_bf16 twice, P as bf16 hi + lo, V^T
-//                    read from row-major V fragments by ds_read_b64_tr_b16.
+//   O^T += V^T P^T   v_mfma_f32_16x16x32_f16: fp16 P times V converted to
+//                    fp16 as it is staged; a chunk holding a value of
+//                    magnitude 65536 or more (or a non-finite one) is staged
+//                    in bf16 instead and takes P as bf16 hi + lo (two bf16
+//                    MFMAs), chosen block-wide.  V^T is read from row-major V
+//                    fragments by ds_read_b64_tr_b16.
 // The sink key is a fifth 16-key tile (its first row; the rest zero and
 // masked) and a third PV step, only in windows after the first.  Queries and
 // keys are fetched through the order array, so a block in column order reads
@@ -111,6 +115,7 @@ __global__ __launch_bounds__(256) void vit_rope_kernel(VitRopeArgs a) {
 // computed).
 template <int G, bool WIN>
 __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_kernel(VitArgs a, int nqb) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     constexpr int NW = G == 1 ? 2 : 4;        // waves: 64 tokens per block at G = 1
     constexpr int NT = NW * 64;
     constexpr int BQ = 32 * NW / G;           // tokens per block; divides 64

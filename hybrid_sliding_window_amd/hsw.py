@@ -5,6 +5,11 @@ memory, passes their data pointers and the current HIP stream to the C entry
 point of the same name, and raises HswError on a non-zero status.  All
 arithmetic happens in the library's kernels; there is no CPU fallback, and
 importing this module fails loudly if the library has not been built.
+
+The library is libhsw.so, or libhsw_checked.so (device-resident arguments
+checked on the device) when the environment sets HSW_CHECK_DEVICE=1;
+load_library() binds a second copy of these functions to another build in
+the same process.
 """
 from __future__ import annotations
 
@@ -14,12 +19,20 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhsw.so")
+RELEASE_LIB_PATH = os.path.join(HERE, "libhsw.so")
+CHECKED_LIB_PATH = os.path.join(HERE, "libhsw_checked.so")
+# load_library() sets _LIB_OVERRIDE on a fresh copy of this module before
+# running it
+LIB_PATH = (globals().get("_LIB_OVERRIDE")
+            or (CHECKED_LIB_PATH if os.environ.get("HSW_CHECK_DEVICE") == "1" else RELEASE_LIB_PATH))
 
 HSW_BF16, HSW_F32 = 0, 1
 HSW_DST_RING, HSW_DST_POOL, HSW_DST_STAGING = 0, 1, 2
 STATUS = {0: "HSW_OK", 1: "HSW_E_NULL", 2: "HSW_E_SHAPE", 3: "HSW_E_ALIGN", 4: "HSW_E_DTYPE",
-          5: "HSW_E_WORKSPACE", 6: "HSW_E_LAUNCH", 7: "HSW_E_CAPACITY", 8: "HSW_E_STALE"}
+          5: "HSW_E_WORKSPACE", 6: "HSW_E_LAUNCH", 7: "HSW_E_CAPACITY", 8: "HSW_E_STALE",
+          9: "HSW_E_DEVICE_INPUT"}
+HSW_DEV = {0: "OK", 1: "POSITION", 2: "CU_SEQLENS", 3: "POOL_RANGE", 4: "RING_SEQ", 5: "CTX_LEN", 6: "ORDER",
+           7: "DST_RANGE"}
 
 
 class HswError(RuntimeError):
@@ -62,6 +75,9 @@ def _load() -> ctypes.CDLL:
     lib.hsw_status_str.argtypes = [I32]
     lib.hsw_last_error.restype = ctypes.c_char_p
     lib.hsw_version.restype = ctypes.c_char_p
+    lib.hsw_device_checks_enabled.restype = I32
+    lib.hsw_device_check_status.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I64)]
+    lib.hsw_device_check_status.restype = I32
     lib.hsw_rope_partial_kv_write.argtypes = [SH, I64, P, P, P, P, P, I32, P, P, I64, P, P, P, P]
     lib.hsw_swa_prefill.argtypes = [SH, I32, I64, P, P, P, P, P, P, P, P, P, P]
     lib.hsw_swa_decode.argtypes = [SH, I32, P, P, P, P, P, P, P]
@@ -110,7 +126,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
-EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_rope_partial_kv_write",
+EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_device_checks_enabled",
+            "hsw_device_check_status", "hsw_rope_partial_kv_write",
             "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope", "hsw_swa_decode_qrope",
             "hsw_full_decode_workspace_bytes",
             "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_full_decode_splitk_qrope",
@@ -230,6 +247,29 @@ def hsw_kv_bytes(kind, n_seqs, ctx, window, n_kv_heads, d_qk, d_v_stored, elem_b
 
 def hsw_version() -> str:
     return lib.hsw_version().decode()
+
+
+def hsw_device_checks_enabled() -> bool:
+    return bool(lib.hsw_device_checks_enabled())
+
+
+def hsw_device_check_status(stream=None):
+    """(status, code, index) of the current device's check flag (the flag is
+    cleared when a violation is reported); code -1 in a release build."""
+    code, index = ctypes.c_int32(), ctypes.c_int64()
+    rc = int(lib.hsw_device_check_status(_stream(stream), ctypes.byref(code), ctypes.byref(index)))
+    return rc, code.value, index.value
+
+
+def load_library(path):
+    """A second copy of this binding, on the library at `path` (e.g.
+    CHECKED_LIB_PATH), as a module object with the same functions."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(f"{__name__}_{os.path.basename(path)}", __file__)
+    mod = importlib.util.module_from_spec(spec)
+    mod._LIB_OVERRIDE = path
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def hsw_kvm_snapshot_bytes(cfg: KvmConfig) -> int:

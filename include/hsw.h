@@ -33,9 +33,16 @@
  *    HSW_OK without a launch.  A launch failure reported by the runtime gives
  *    HSW_E_LAUNCH.  Device-resident values (positions, lengths, bases) are not
  *    read on the host; kernels skip, without writing, any K/V row whose
- *    destination or source falls outside the capacities passed in.
- *  - Positions are 0-based.  A window of W positions at position p holds
- *    p-W+1 .. p (the token itself and the W-1 before it).
+ *    destination or source falls outside the capacities passed in.  The
+ *    contract on them (stated per call, collected under "Device-resident
+ *    argument checks" below) is checked on the device only by builds with
+ *    HSW_CHECK_DEVICE=1 (libhsw_checked.so).
+ *  - Positions are 0-based int64.  A window of W positions at position p
+ *    holds p-W+1 .. p (the token itself and the W-1 before it).  Windowed
+ *    calls take any position below 2^53 (the RoPE angle is formed in double;
+ *    ring slots need only its low bits).  Full-attention positions index pool
+ *    rows (base + position < pool_rows), and pool_rows must be below 2^31
+ *    (HSW_E_SHAPE otherwise): no pool that fits in one GPU comes near it.
  *  - Query head h reads KV head h / (n_q_heads / n_kv_heads).
  *  - No C++ exception crosses this boundary.
  */
@@ -61,7 +68,8 @@ enum {
     HSW_E_WORKSPACE = 5, /* workspace smaller than required */
     HSW_E_LAUNCH = 6,    /* the HIP runtime rejected a launch */
     HSW_E_CAPACITY = 7,  /* a KV pool (ring slots, pool rows, snapshots) lacks room */
-    HSW_E_STALE = 8      /* a snapshot was released (its rows were rewritten) */
+    HSW_E_STALE = 8,     /* a snapshot was released (its rows were rewritten) */
+    HSW_E_DEVICE_INPUT = 9 /* checked builds: a device-resident argument broke the contract */
 };
 
 enum { HSW_BF16 = 0, HSW_F32 = 1 };
@@ -104,6 +112,57 @@ typedef struct hsw_attn_shape {
 const char *hsw_status_str(hsw_status s);
 const char *hsw_last_error(void);
 const char *hsw_version(void);
+
+/* ------------------------------------------------------------------
+ * Device-resident argument checks.
+ *
+ * The calls never read device-resident arguments on the host (that would
+ * need a synchronisation), so release builds trust them.  A build with
+ * HSW_CHECK_DEVICE=1 (libhsw_checked.so, same ABI) launches a check kernel
+ * ahead of each call's kernels on the call's stream; it tests every element
+ * against the contract below and records the first violation it sees in a
+ * flag held in the library's module memory, one per device (nothing is
+ * allocated).  Every kernel of that and every later call on the device then
+ * returns without reading or writing anything, until the flag is cleared.
+ * The contract per call (codes HSW_DEV_*):
+ *   RoPE:        pos[t] >= 0 (POSITION); ring: 0 <= seq[t] < dst_capacity
+ *                (RING_SEQ); pool: seq[t] >= 0 and 0 <= seq_base[seq[t]] +
+ *                pos[t] < dst_capacity, staging: t < dst_capacity
+ *                (DST_RANGE).  seq[t] must also index seq_base, which no
+ *                build can check (its length is not passed).
+ *   prefills:    cu_seqlens[0] >= 0, non-decreasing, every length <=
+ *                max_seqlen (CU_SEQLENS), and cu_seqlens[n_seqs] at most the
+ *                rows of q / staging / out (not checkable); start_pos >= 0
+ *                (POSITION); full: 0 <= seq_base and seq_base + start_pos +
+ *                length <= pool_rows (POOL_RANGE).
+ *   SWA decode:  pos >= 0 (POSITION).
+ *   full decode: 1 <= ctx_len <= max_ctx (CTX_LEN); 0 <= seq_base and
+ *                seq_base + ctx_len <= pool_rows (POOL_RANGE).
+ *   ViT:         cu_seqlens as for the prefills with max_len; every order
+ *                entry inside its picture (ORDER).
+ * Calls on several streams of one device share the flag.
+ */
+enum {
+    HSW_DEV_OK = 0,
+    HSW_DEV_POSITION = 1,
+    HSW_DEV_CU_SEQLENS = 2,
+    HSW_DEV_POOL_RANGE = 3,
+    HSW_DEV_RING_SEQ = 4,
+    HSW_DEV_CTX_LEN = 5,
+    HSW_DEV_ORDER = 6,
+    HSW_DEV_DST_RANGE = 7
+};
+
+/* 1 in a build with HSW_CHECK_DEVICE=1, else 0. */
+int32_t hsw_device_checks_enabled(void);
+
+/* Synchronise `stream`, then read the current device's check flag: HSW_OK
+ * with *code = HSW_DEV_OK and *index = -1 when no violation was recorded;
+ * HSW_E_DEVICE_INPUT with *code the HSW_DEV_* code and *index the element
+ * (token, sequence or picture) that broke it, after which the flag is
+ * cleared.  In a release build nothing is checked: HSW_OK with *code = -1
+ * and *index = -1, no synchronisation.  code and index may be NULL. */
+hsw_status hsw_device_check_status(hsw_stream_t stream, int32_t *code, int64_t *index);
 
 /*
  * Partial rotate-half RoPE on q and k, plus the K/V write.

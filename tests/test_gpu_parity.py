@@ -347,6 +347,32 @@ def test_logit_shift_layer_fp32_chain():
     print(f"fp32 logit-shift chain: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
+def test_windowed_calls_at_positions_beyond_2_31():
+    """Windowed positions are int64 (the ring needs only p mod 128): a chunk
+    that crosses 2^31, one past 2^33, their fused q-RoPE form and decodes at
+    such positions, all against the oracle (the fused chain from the raw q
+    rotated in fp64)."""
+    note("windowed calls past 2^31")
+    starts = (2 ** 31 - 50, 2 ** 33 + 3, 2 ** 31 + 1)
+    batch = wl.swa_prefill_batch(seed=48, n_seqs=3, seqlens=(300, 140, 1), start_pos=starts)
+    q_rot, kst, vst, kb, vb, kring, vring, out = run_swa_prefill(batch)
+    check_ring_commit(batch, kst, vst, kb, vb, kring, vring)
+    ref = np.concatenate([o for _, o in oracle_swa_prefill_rows(batch, q_rot, kst, vst, kb, vb)])
+    ma, mr = assert_close(f64(out), ref, what="swa_prefill past 2^31")
+    check_rope_values(batch["q"], q_rot, batch["pos"].numpy(), wl.THETA_SWA, what="q_rot past 2^31")
+    kst2, vst2, kring2, vring2, out2 = run_swa_prefill_qrope(batch)
+    assert torch.equal(out2, out) and torch.equal(kring2, kring)
+    positions = [2 ** 31 - 1, 2 ** 31, 2 ** 31 + 127, 2 ** 32 + 5, 2 ** 40 + 3, 2 ** 52 + 9]
+    dec = wl.swa_decode_batch(seed=49, n_seqs=len(positions), positions=positions)
+    q_rot_d, kring_d, vring_d, out_d, idx = run_swa_decode(dec)
+    P = dec["pos"].numpy()
+    assert np.array_equal(idx.cpu().numpy(), P % 128)
+    ref_d = oracle.ring_decode(f64(q_rot_d), P, f64(kring_d), f64(vring_d), sinks=f64(dec["sinks"]),
+                               **shape_kw(dec["shape"]))
+    dma, dmr = assert_close(f64(out_d), ref_d, what="swa_decode past 2^31")
+    print(f"past 2^31: prefill max_abs={ma:.2e} mean_rel={mr:.2e}; decode max_abs={dma:.2e} mean_rel={dmr:.2e}")
+
+
 def test_decode_matches_prefill_row():
     """Decode at position P equals prefill row P (colibri 'Correctness':
     prefill in blocks and one token at a time agree)."""
@@ -690,12 +716,12 @@ def test_zero_sizes_launch_nothing():
 def test_rope_cos_sin_fp32_against_fp64():
     """The angle code itself: an fp32 RoPE call on unit vectors (x_lo = 1,
     x_hi = 0) returns exactly the fp32 cos and sin it formed, for every
-    frequency at positions up to 2^24 + 5; each within 3e-7 of the fp64
-    rotation (angle formed and reduced in double, gaudi-cookbook 'The RoPE fix
-    for large positions')."""
+    frequency at positions up to 2^52 + 5 (windowed positions are int64);
+    each within 3e-7 of the fp64 rotation (angle formed and reduced in
+    double, gaudi-cookbook 'The RoPE fix for large positions')."""
     note("rope cos/sin fp32 vs fp64")
     positions = [0, 1, 2, 3, 100, 127, 128, 4095, 65536, 131071, 196608, 200000, 205000, 262143,
-                 524287, 524288, 1_000_003, 2 ** 24 + 5]
+                 524287, 524288, 1_000_003, 2 ** 24 + 5, 2 ** 31 + 7, 2 ** 33 + 3, 2 ** 40 + 9, 2 ** 52 + 5]
     T = len(positions)
     for theta in (wl.THETA_SWA, wl.THETA_FULL):
         shape = wl.Shape(1, 1, 0, theta, dtype=torch.float32)
