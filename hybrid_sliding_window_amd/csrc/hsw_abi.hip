@@ -46,6 +46,38 @@ namespace dc = hsw::devcheck;
 // in one GPU's memory comes near this many rows.
 constexpr int64_t kMaxPoolRows = 0x7fffffffLL;
 
+// Module memory is per device: each GPU holds its own copy of a __device__
+// variable at its own address.  Host code takes that address once per device
+// (with the device current) and uses only it.
+constexpr int kMaxDevices = 64;
+std::mutex g_symbol_mu;
+
+hsw_status symbol_address(const void *symbol, void *(&cache)[kMaxDevices], void **out, const char *what) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(HSW_E_LAUNCH, "device %d is beyond the %d this library keeps %s for", dev, kMaxDevices, what);
+    std::lock_guard<std::mutex> lock(g_symbol_mu);
+    if (!cache[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, symbol);
+        if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipGetSymbolAddress(%s): %s", what, hipGetErrorString(e));
+        cache[dev] = p;
+    }
+    *out = cache[dev];
+    return HSW_OK;
+}
+
+// ------------------------------------------------ the no-allocation call
+// Scratch of hsw_full_decode_splitk_noalloc: its split-K partials, in module
+// memory (nothing is allocated; each GPU the library runs on holds this
+// array until the process ends).  Every call on a device shares the one
+// array: calls that overlap on one GPU race.  The partial pass writes every
+// slot the combine pass reads, so nothing has to start at zero.
+static __device__ __align__(256) unsigned char scratch[HSW_NOALLOC_SCRATCH_BYTES];
+void *g_scratch_ptr[kMaxDevices];
+
 // ------------------------------------------------------------ device checks
 #if HSW_CHECK_DEVICE
 // Per device: [0] the code of a contract violation found (0: none), [1] the
@@ -61,26 +93,14 @@ __global__ __launch_bounds__(256) void check_kernel(dc::Inputs in, unsigned long
     }
 }
 
-constexpr int kMaxDevices = 64;
-std::mutex g_flag_mu;
-unsigned long long *g_flag[kMaxDevices];
+void *g_flag_ptr[kMaxDevices];
 
 // The current device's flag.
 hsw_status device_flag(unsigned long long **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev < 0 || dev >= kMaxDevices)
-        return fail(HSW_E_LAUNCH, "device %d is beyond the %d the checks keep a flag for", dev, kMaxDevices);
-    std::lock_guard<std::mutex> lock(g_flag_mu);
-    if (!g_flag[dev]) {
-        void *p = nullptr;
-        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_dev_check));
-        if (e != hipSuccess) return fail(HSW_E_LAUNCH, "hipGetSymbolAddress: %s", hipGetErrorString(e));
-        g_flag[dev] = static_cast<unsigned long long *>(p);
-    }
-    *out = g_flag[dev];
-    return HSW_OK;
+    void *p = nullptr;
+    hsw_status st = symbol_address(HIP_SYMBOL(g_dev_check), g_flag_ptr, &p, "the check flag");
+    *out = static_cast<unsigned long long *>(p);
+    return st;
 }
 #endif
 
@@ -183,10 +203,11 @@ hsw::AttnArgs base_args(const hsw_attn_shape *sh) {
 }  // namespace
 
 namespace {
+// noalloc: ws / ws_bytes are ignored; the partials go to `scratch`.
 hsw_status full_decode_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx, const int64_t *ctx_len,
                             const int64_t *seq_base, const void *q, const void *k_pool, const void *v_pool,
                             int64_t pool_rows, const float *sinks, int32_t chunk, void *ws, size_t ws_bytes,
-                            void *out, hipStream_t s, bool qrope, const char *what) {
+                            void *out, hipStream_t s, bool qrope, const char *what, bool noalloc = false) {
     hsw_status st = check_shape(sh, 0);
     if (st) return st;
     if (n_seqs < 0 || max_ctx < 0 || pool_rows < 0)
@@ -208,6 +229,15 @@ hsw_status full_decode_impl(const hsw_attn_shape *sh, int32_t n_seqs, int64_t ma
                                  "and 1, 2, 4, 8 or 16 query heads per KV head");
     if (n_seqs == 0) return HSW_OK;
     size_t need = hsw_full_decode_workspace_bytes(sh, n_seqs, max_ctx, chunk);
+    if (noalloc) {
+        if (need > (size_t)HSW_NOALLOC_SCRATCH_BYTES)
+            return fail(HSW_E_WORKSPACE, "the partials need %zu bytes; the no-allocation call holds %zu "
+                                         "(use a larger chunk or fewer sequences per call)",
+                        need, (size_t)HSW_NOALLOC_SCRATCH_BYTES);
+        if (max_ctx == 0) return HSW_OK;
+        if ((st = symbol_address(HIP_SYMBOL(scratch), g_scratch_ptr, &ws, "the scratch array"))) return st;
+        ws_bytes = HSW_NOALLOC_SCRATCH_BYTES;
+    }
     if (!ws || ws_bytes < need)
         return fail(HSW_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
     if (max_ctx == 0) return HSW_OK;
@@ -493,6 +523,14 @@ hsw_status hsw_full_decode_splitk_qrope(const hsw_attn_shape *sh, int32_t n_seqs
                                         hsw_stream_t stream) {
     return full_decode_impl(sh, n_seqs, max_ctx, ctx_len, seq_base, q, k_pool, v_pool, pool_rows, sinks, chunk,
                             ws, ws_bytes, out, (hipStream_t)stream, true, "full_decode_splitk_qrope");
+}
+
+hsw_status hsw_full_decode_splitk_noalloc(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                          const int64_t *ctx_len, const int64_t *seq_base, const void *q_rot,
+                                          const void *k_pool, const void *v_pool, int64_t pool_rows,
+                                          const float *sinks, int32_t chunk, void *out, hsw_stream_t stream) {
+    return full_decode_impl(sh, n_seqs, max_ctx, ctx_len, seq_base, q_rot, k_pool, v_pool, pool_rows, sinks, chunk,
+                            nullptr, 0, out, (hipStream_t)stream, false, "full_decode_splitk_noalloc", true);
 }
 
 hsw_status hsw_full_prefill_chunk(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_seqlen,

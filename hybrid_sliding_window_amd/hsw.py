@@ -89,6 +89,7 @@ def _load() -> ctypes.CDLL:
     lib.hsw_full_prefill_chunk.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
     lib.hsw_full_prefill_chunk_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, P, I64, P, P, P]
     lib.hsw_full_decode_splitk_qrope.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, SZ, P, P]
+    lib.hsw_full_decode_splitk_noalloc.argtypes = [SH, I32, I64, P, P, P, P, P, I64, P, I32, P, P]
     lib.hsw_kv_bytes.argtypes = [I32, I64, I64, I32, I32, I32, I32, I32, I32]
     lib.hsw_vit_layout.argtypes = [I32, I32, P, P, P]
     lib.hsw_vit_rope_2d.argtypes = [SH, I64, P, P, P, P, P, P, P]
@@ -117,7 +118,8 @@ def _load() -> ctypes.CDLL:
               "hsw_kvm_drop_snapshot"):
         getattr(lib, f).restype = I32
     for f in ("hsw_rope_partial_kv_write", "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope",
-              "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_prefill_chunk",
+              "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_decode_splitk_noalloc",
+              "hsw_full_prefill_chunk",
               "hsw_full_decode_splitk_qrope", "hsw_full_prefill_chunk_qrope", "hsw_vit_layout",
               "hsw_vit_rope_2d", "hsw_vit_attention"):
         getattr(lib, f).restype = I32
@@ -130,7 +132,8 @@ EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_device_check
             "hsw_device_check_status", "hsw_rope_partial_kv_write",
             "hsw_swa_prefill", "hsw_swa_decode", "hsw_swa_prefill_qrope", "hsw_swa_decode_qrope",
             "hsw_full_decode_workspace_bytes",
-            "hsw_full_decode_splitk", "hsw_full_prefill_chunk", "hsw_full_decode_splitk_qrope",
+            "hsw_full_decode_splitk", "hsw_full_decode_splitk_noalloc", "hsw_full_prefill_chunk",
+            "hsw_full_decode_splitk_qrope",
             "hsw_full_prefill_chunk_qrope", "hsw_kv_bytes",
             "hsw_kvm_snapshot_bytes", "hsw_kvm_create", "hsw_kvm_destroy", "hsw_kvm_admit", "hsw_kvm_release",
             "hsw_kvm_append", "hsw_kvm_truncate", "hsw_kvm_info", "hsw_kvm_free_space", "hsw_kvm_snapshot",
@@ -211,6 +214,18 @@ def hsw_full_decode_splitk(shape, n_seqs, max_ctx, ctx_len, seq_base, q_rot, k_p
                                       int(pool_rows), _ptr(sinks), int(chunk), _ptr(ws),
                                       int(ws_bytes), _ptr(out), _stream(stream)),
            "hsw_full_decode_splitk")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # HSW_NOALLOC_SCRATCH_BYTES
+
+
+def hsw_full_decode_splitk_noalloc(shape, n_seqs, max_ctx, ctx_len, seq_base, q_rot, k_pool, v_pool,
+                                   pool_rows, sinks, chunk, out, stream=None):
+    _check(lib.hsw_full_decode_splitk_noalloc(_sh(shape), int(n_seqs), int(max_ctx), _ptr(ctx_len),
+                                              _ptr(seq_base), _ptr(q_rot), _ptr(k_pool), _ptr(v_pool),
+                                              int(pool_rows), _ptr(sinks), int(chunk), _ptr(out),
+                                              _stream(stream)),
+           "hsw_full_decode_splitk_noalloc")
 
 
 def hsw_full_prefill_chunk(shape, n_seqs, max_seqlen, cu_seqlens, start_pos, seq_base, q_rot,

@@ -293,6 +293,26 @@ hsw_status hsw_full_decode_splitk(const hsw_attn_shape *sh, int32_t n_seqs, int6
                                   void *ws, size_t ws_bytes, void *out, hsw_stream_t stream);
 
 /*
+ * hsw_full_decode_splitk without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split-K partials go to a scratch
+ * array in the library's module memory, HSW_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per device, held until the process ends; the call allocates and frees
+ * nothing.  Every other argument, the result and the error behaviour are
+ * those of hsw_full_decode_splitk (bit for bit the same output).  A call
+ * whose partials, hsw_full_decode_workspace_bytes(sh, n_seqs, max_ctx,
+ * chunk), exceed the scratch returns HSW_E_WORKSPACE and launches nothing
+ * (64 sequences x 64 heads at 131072 keys fit with chunk 8192).  All calls
+ * on one device share the scratch: calls that overlap on one GPU (several
+ * streams, several host threads) race and must be serialised by the caller.
+ */
+#define HSW_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hsw_status hsw_full_decode_splitk_noalloc(const hsw_attn_shape *sh, int32_t n_seqs, int64_t max_ctx,
+                                          const int64_t *ctx_len, const int64_t *seq_base, const void *q_rot,
+                                          const void *k_pool, const void *v_pool, int64_t pool_rows,
+                                          const float *sinks, int32_t chunk, void *out, hsw_stream_t stream);
+
+/*
  * Full-attention chunked prefill over prior rows plus the chunk (causal).
  * Follows gaudi-cookbook "Tiled global-attention prefill" (query tiles, no
  * materialised mask, no cross-tile merge since softmax is per row) and
