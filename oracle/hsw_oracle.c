@@ -103,33 +103,65 @@ int64_t hswo_dst_index(int kind, int64_t t, int64_t pos, int64_t seq_base,
     return t;
 }
 
-/* One (query row, head) over an explicit list of keys given by row pointers.
- * Logits l_j = tau * <q, k_j>; with a sink s (when has_sink):
- *   m = max(s, max_j l_j),  Z = exp(s-m) + sum_j exp(l_j-m),
- *   o = sum_j exp(l_j-m) * (lambda * v_j) / Z,  lse = m + log Z.
+/* One query row over an explicit list of keys given by row pointers, for
+ * the `group` query heads that share one KV head (q and o hold their rows
+ * one after the other).  For each head h, logits l_j = tau * <q_h, k_j>; with
+ * a sink s_h (when sinks is not NULL):
+ *   m = max(s_h, max_j l_j),  Z = exp(s_h-m) + sum_j exp(l_j-m),
+ *   o_h = sum_j exp(l_j-m) * (lambda * v_j) / Z,  lse = m + log Z.
  * Without a sink the s terms are dropped.  colibri "What the engine
- * implements" (sink in the denominator only; value scale before attention). */
-static void attend_row(int dqk, int dv, double tau, double lambda,
-                       int has_sink, double sink, const double *q,
-                       int64_t nkeys, const double *const *krows,
-                       const double *const *vrows, double *logit,
-                       double *o, double *lse) {
-    double m = has_sink ? sink : -INFINITY;
+ * implements" (sink in the denominator only; value scale before attention).
+ * Every head runs the same operations in the same order as it would alone:
+ * the key loop is outside the head loop only so that each K and V row is
+ * read once for the whole group.  logit holds group * nkeys values. */
+static void attend_group(int group, int dqk, int dv, double tau, double lambda,
+                         const double *sinks, const double *q, int64_t nkeys,
+                         const double *const *krows, const double *const *vrows,
+                         double *logit, double *m, double *z, double *o,
+                         double *lse, double *qt, double *acc) {
+    /* qt[e][h] = q_h[e]: the heads' dot products then advance together over
+     * e (acc[h] still sums its products in the order e = 0, 1, ...) */
+    for (int h = 0; h < group; ++h)
+        for (int e = 0; e < dqk; ++e) qt[e * group + h] = q[h * (int64_t)dqk + e];
+    for (int h = 0; h < group; ++h) m[h] = sinks ? sinks[h] : -INFINITY;
     for (int64_t j = 0; j < nkeys; ++j) {
-        double acc = 0.0;
-        for (int e = 0; e < dqk; ++e) acc += q[e] * krows[j][e];
-        logit[j] = tau * acc;
-        if (logit[j] > m) m = logit[j];
+        for (int h = 0; h < group; ++h) acc[h] = 0.0;
+        for (int e = 0; e < dqk; ++e) {
+            const double ke = krows[j][e];
+            for (int h = 0; h < group; ++h) acc[h] += qt[e * group + h] * ke;
+        }
+        for (int h = 0; h < group; ++h) {
+            double lj = tau * acc[h];
+            logit[h * nkeys + j] = lj;
+            if (lj > m[h]) m[h] = lj;
+        }
     }
-    double z = has_sink ? exp(sink - m) : 0.0;
-    for (int e = 0; e < dv; ++e) o[e] = 0.0;
+    for (int h = 0; h < group; ++h) {
+        z[h] = sinks ? exp(sinks[h] - m[h]) : 0.0;
+        for (int e = 0; e < dv; ++e) o[h * (int64_t)dv + e] = 0.0;
+    }
     for (int64_t j = 0; j < nkeys; ++j) {
-        double p = exp(logit[j] - m);
-        z += p;
-        for (int e = 0; e < dv; ++e) o[e] += p * (lambda * vrows[j][e]);
+        for (int h = 0; h < group; ++h) {
+            double p = exp(logit[h * nkeys + j] - m[h]);
+            z[h] += p;
+            double *oh = o + h * (int64_t)dv;
+            for (int e = 0; e < dv; ++e) oh[e] += p * (lambda * vrows[j][e]);
+        }
     }
-    for (int e = 0; e < dv; ++e) o[e] /= z;
-    if (lse) *lse = (nkeys > 0 || has_sink) ? m + log(z) : -INFINITY;
+    for (int h = 0; h < group; ++h) {
+        for (int e = 0; e < dv; ++e) o[h * (int64_t)dv + e] /= z[h];
+        if (lse) lse[h] = (nkeys > 0 || sinks) ? m[h] + log(z[h]) : -INFINITY;
+    }
+}
+
+/* First key position of the query at position p: a window of W positions
+ * holds p-W+1 .. p (the token and the W-1 before it), clipped at 0; W = 0 is
+ * full causal attention, 0 .. p.  colibri "System One mode and prompt
+ * reuse" (128 slots, the token written before it attends); gaudi-cookbook
+ * "What was built" (exactly the last 128 positions). */
+static int64_t first_key(int64_t p, int64_t window) {
+    int64_t lo = window > 0 ? p - window + 1 : 0;
+    return lo < 0 ? 0 : lo;
 }
 
 /* Attention over K/V laid out linearly by absolute position.
@@ -149,45 +181,47 @@ int hswo_attn_linear(int hq, int hkv, int dqk, int dv, int64_t window,
                      int64_t kpos0, double *o, double *lse) {
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || window < 0) return HSWO_E_ARG;
     int group = hq / hkv;
+    int64_t cap = 1;                           /* most keys any query sees */
     for (int64_t i = 0; i < nq; ++i) {
-        int64_t lo = window > 0 ? qpos[i] - window + 1 : 0;
-        if (lo < 0) lo = 0;
+        int64_t lo = first_key(qpos[i], window);
         if (qpos[i] < 0 || lo < kpos0 || qpos[i] > kpos0 + nk - 1) return HSWO_E_RANGE;
+        if (qpos[i] - lo + 1 > cap) cap = qpos[i] - lo + 1;
     }
     int err = HSWO_OK;
     #pragma omp parallel
     {
-        int64_t cap = window > 0 ? window : nk;
-        if (cap > nk) cap = nk;
-        if (cap < 1) cap = 1;
-        double *logit = (double *)malloc(sizeof(double) * cap);
+        double *logit = (double *)malloc(sizeof(double) * cap * group);
+        double *mz = (double *)malloc(sizeof(double) * 3 * group);
+        double *qt = (double *)malloc(sizeof(double) * group * dqk);
         const double **kr = (const double **)malloc(sizeof(double *) * cap);
         const double **vr = (const double **)malloc(sizeof(double *) * cap);
-        if (!logit || !kr || !vr) {
+        if (!logit || !mz || !qt || !kr || !vr) {
             #pragma omp atomic write
             err = HSWO_E_ARG;
         } else {
-            #pragma omp for schedule(dynamic, 4)
-            for (int64_t ih = 0; ih < nq * hq; ++ih) {
-                int64_t i = ih / hq;
-                int h = (int)(ih % hq);
-                int g = h / group;
+            /* one (query row, KV head) at a time: its `group` query heads
+             * h = g * group .. share the key rows */
+            #pragma omp for schedule(dynamic, 1)
+            for (int64_t ig = 0; ig < nq * hkv; ++ig) {
+                int64_t i = ig / hkv;
+                int g = (int)(ig % hkv);
                 int64_t p = qpos[i];
-                int64_t lo = window > 0 ? p - window + 1 : 0;
-                if (lo < 0) lo = 0;
+                int64_t lo = first_key(p, window);
                 int64_t n = p - lo + 1;
                 for (int64_t j = 0; j < n; ++j) {
                     int64_t row = lo + j - kpos0;
                     kr[j] = k + (row * hkv + g) * (int64_t)dqk;
                     vr[j] = v + (row * hkv + g) * (int64_t)dv;
                 }
-                attend_row(dqk, dv, tau, lambda, sinks != NULL,
-                           sinks ? sinks[h] : 0.0, q + ih * (int64_t)dqk, n,
-                           kr, vr, logit, o + ih * (int64_t)dv,
-                           lse ? lse + ih : NULL);
+                int64_t ih0 = i * hq + (int64_t)g * group;   /* first (row, head) of the group */
+                attend_group(group, dqk, dv, tau, lambda, sinks ? sinks + g * group : NULL,
+                             q + ih0 * (int64_t)dqk, n, kr, vr, logit, mz, mz + group,
+                             o + ih0 * (int64_t)dv, lse ? lse + ih0 : NULL, qt, mz + 2 * group);
             }
         }
         free(logit);
+        free(mz);
+        free(qt);
         free(kr);
         free(vr);
     }
@@ -211,18 +245,20 @@ int hswo_ring_decode(int hq, int hkv, int dqk, int dv, int64_t slots,
     int err = HSWO_OK;
     #pragma omp parallel
     {
-        double *logit = (double *)malloc(sizeof(double) * slots);
+        double *logit = (double *)malloc(sizeof(double) * slots * group);
+        double *mz = (double *)malloc(sizeof(double) * 3 * group);
+        double *qt = (double *)malloc(sizeof(double) * group * dqk);
         const double **kr = (const double **)malloc(sizeof(double *) * slots);
         const double **vr = (const double **)malloc(sizeof(double *) * slots);
-        if (!logit || !kr || !vr) {
+        if (!logit || !mz || !qt || !kr || !vr) {
             #pragma omp atomic write
             err = HSWO_E_ARG;
         } else {
+            /* one (sequence, KV head) at a time, with its `group` query heads */
             #pragma omp for schedule(dynamic, 4)
-            for (int64_t sh = 0; sh < ns * hq; ++sh) {
-                int64_t s = sh / hq;
-                int h = (int)(sh % hq);
-                int g = h / group;
+            for (int64_t sg = 0; sg < ns * hkv; ++sg) {
+                int64_t s = sg / hkv;
+                int g = (int)(sg % hkv);
                 int64_t P = pos[s];
                 int64_t n = 0;
                 for (int64_t t = 0; t < slots; ++t) {
@@ -234,13 +270,15 @@ int hswo_ring_decode(int hq, int hkv, int dqk, int dv, int64_t slots,
                     vr[n] = vring + ((s * hkv + g) * slots + t) * (int64_t)dv;
                     ++n;
                 }
-                attend_row(dqk, dv, tau, lambda, sinks != NULL,
-                           sinks ? sinks[h] : 0.0, q + sh * (int64_t)dqk, n,
-                           kr, vr, logit, o + sh * (int64_t)dv,
-                           lse ? lse + sh : NULL);
+                int64_t sh0 = s * hq + (int64_t)g * group;
+                attend_group(group, dqk, dv, tau, lambda, sinks ? sinks + g * group : NULL,
+                             q + sh0 * (int64_t)dqk, n, kr, vr, logit, mz, mz + group,
+                             o + sh0 * (int64_t)dv, lse ? lse + sh0 : NULL, qt, mz + 2 * group);
             }
         }
         free(logit);
+        free(mz);
+        free(qt);
         free(kr);
         free(vr);
     }
@@ -265,8 +303,7 @@ int hswo_attn_partial(int hq, int hkv, int dqk, int dv, int64_t window,
         int64_t i = ih / hq;
         int g = (int)(ih % hq) / group;
         int64_t p = qpos[i];
-        int64_t lo = window > 0 ? p - window + 1 : 0;
-        if (lo < 0) lo = 0;
+        int64_t lo = first_key(p, window);
         if (lo < a) lo = a;
         int64_t hi = p < b - 1 ? p : b - 1;
         double m = -INFINITY, l = 0.0;
@@ -420,7 +457,7 @@ int hswo_vit_attn(int n_img, const int64_t *cu, const int32_t *order, int window
                   int sink_key, int hq, int hkv, int d, int dv, double tau,
                   const double *sinks, const double *q, const double *k,
                   const double *v, double *o) {
-    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || window < 0) return HSWO_E_ARG;
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || window < 0 || d <= 0 || d > 256) return HSWO_E_ARG;
     int group = hq / hkv;
     int64_t maxlen = 1;
     for (int s = 0; s < n_img; ++s) {
@@ -465,9 +502,10 @@ int hswo_vit_attn(int n_img, const int64_t *cu, const int32_t *order, int window
                         vr[nk] = v + (r * hkv + g) * (int64_t)dv;
                         ++nk;
                     }
-                    attend_row(d, dv, tau, 1.0, sinks != NULL, sinks ? sinks[h] : 0.0,
-                               q + (t * hq + h) * (int64_t)d, nk, kr, vr, logit,
-                               o + (t * hq + h) * (int64_t)dv, NULL);
+                    double mz[3], qt[256];
+                    attend_group(1, d, dv, tau, 1.0, sinks ? sinks + h : NULL,
+                                 q + (t * hq + h) * (int64_t)d, nk, kr, vr, logit,
+                                 mz, mz + 1, o + (t * hq + h) * (int64_t)dv, NULL, qt, mz + 2);
                 }
             }
             free(logit);

@@ -18,16 +18,29 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = [
     ("sink dropped from the denominator",
-     "double z = has_sink ? exp(sink - m) : 0.0;", "double z = 0.0;"),
+     "z[h] = sinks ? exp(sinks[h] - m[h]) : 0.0;", "z[h] = 0.0;"),
     ("value scale ignored",
-     "o[e] += p * (lambda * vrows[j][e]);", "o[e] += p * (vrows[j][e]);"),
+     "oh[e] += p * (lambda * vrows[j][e]);", "oh[e] += p * (vrows[j][e]);"),
+    ("sink also added to the numerator",
+     "for (int h = 0; h < group; ++h) {\n        for (int e = 0; e < dv; ++e) o[h * (int64_t)dv + e] /= z[h];",
+     "for (int h = 0; h < group; ++h) {\n        if (sinks) for (int e = 0; e < dv; ++e) "
+     "o[h * (int64_t)dv + e] += exp(sinks[h] - m[h]);\n        for (int e = 0; e < dv; ++e) o[h * (int64_t)dv + e] /= z[h];"),
+    ("each head's logits summed over the wrong query head",
+     "for (int e = 0; e < dqk; ++e) qt[e * group + h] = q[h * (int64_t)dqk + e];",
+     "for (int e = 0; e < dqk; ++e) qt[e * group + h] = q[((h + 1) % group) * (int64_t)dqk + e];"),
     ("window one position too long",
-     "int64_t lo = window > 0 ? p - window + 1 : 0;\n                if (lo < 0) lo = 0;\n                int64_t n",
-     "int64_t lo = window > 0 ? p - window : 0;\n                if (lo < 0) lo = 0;\n                int64_t n"),
+     "int64_t lo = window > 0 ? p - window + 1 : 0;", "int64_t lo = window > 0 ? p - window : 0;"),
+    ("window one position too short",
+     "int64_t lo = window > 0 ? p - window + 1 : 0;", "int64_t lo = window > 0 ? p - window + 2 : 0;"),
     ("rotation sign flipped",
      "yr[i] = xr[i] * c - xr[i + half] * s;", "yr[i] = xr[i] * c + xr[i + half] * s;"),
-    ("GQA head mapping interleaved",
-     "int g = h / group;\n                int64_t P", "int g = h % hkv;\n                int64_t P"),
+    ("GQA: a group of query heads reads the next KV head",
+     "kr[j] = k + (row * hkv + g) * (int64_t)dqk;\n                    vr[j] = v + (row * hkv + g) * (int64_t)dv;",
+     "kr[j] = k + (row * hkv + (g + 1) % hkv) * (int64_t)dqk;\n"
+     "                    vr[j] = v + (row * hkv + (g + 1) % hkv) * (int64_t)dv;"),
+    ("GQA in the ring decode: a group reads the next KV head's ring",
+     "kr[n] = kring + ((s * hkv + g) * slots + t) * (int64_t)dqk;",
+     "kr[n] = kring + ((s * hkv + (g + 1) % hkv) * slots + t) * (int64_t)dqk;"),
     ("frequency base over the full head width",
      "inv_freq[i] = pow(theta, -2.0 * (double)i / (double)rope_dim);",
      "inv_freq[i] = pow(theta, -2.0 * (double)i / 192.0);"),
