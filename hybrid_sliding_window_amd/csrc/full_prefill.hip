@@ -11,7 +11,10 @@
 // values carry the value scale (applied to the fp32 output).
 //
 // MFMA-bound (~6.6e4 flop/B for an 8192-token chunk after 131072 rows).
-// One workgroup (4 waves) per query block: 128 rows = 128/G positions x the G
+// Sixteen query heads per KV head (both models' full layers) take the
+// 8-wave kernel at the end of this file, whose two wave halves alternate
+// between MFMA and VALU work; the smaller groups take the kernel described
+// here.  One workgroup (4 waves) per query block: 128 rows = 128/G positions x the G
 // query heads of one KV head (the heads are the 16-wide MFMA columns), two
 // column tiles per wave.  The block's keys (pool rows base + 0 .. base +
 // its last position) stream through LDS in 32-key chunks with a three-stage
@@ -68,20 +71,21 @@ constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) alon
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0).  Issued
+// lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0; said
+// so, for code where the compiler cannot tell).  Issued
 // as inline asm so the compiler does not track it: it would otherwise add
 // waits of its own before some LDS reads, for more of these loads than the
 // read needs.  Completion is awaited explicitly (s_waitcnt vmcnt) before the
 // barrier that publishes a stage; m0 is used by nothing else in this kernel.
 __device__ __forceinline__ void load_lds16(const void *src, const void *lds_wave_base) {
-    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(src) : "memory", "m0");
 }
 
 // The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane
 // offset: no per-lane address arithmetic.
 __device__ __forceinline__ void load_lds16_s(const void *sbase, uint32_t voff, const void *lds_wave_base) {
-    const uint32_t m = (uint32_t)(uintptr_t)lds_wave_base;
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
@@ -113,6 +117,15 @@ __device__ __forceinline__ float quad_sum_swap(float v) {
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     return __builtin_bit_cast(u32x2, v);
+}
+
+// A pointer every lane holds, said to be wave-uniform (SGPRs), as the
+// scalar base of a load must be.
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -564,6 +577,519 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
     }
 }
 
+// ---------------------------------------------------------------------
+// G = 16 (16 query heads per KV head, both models' full layers): one 8-wave
+// workgroup per CU over 256 query rows (16 positions x 16 heads), keys in
+// 64-key chunks.  The two halves of the workgroup (waves 0-3: rows 0-127,
+// waves 4-7: rows 128-255) share every K/V chunk in LDS and take turns on
+// each SIMD: between two workgroup barriers one half issues MFMAs (PV of the
+// previous chunk, then S^T of this one, at raised wave priority) while the
+// other runs the softmax and the fp16 conversion of V (VALU), then they
+// swap, so the two waves of a SIMD keep its matrix and vector units busy at
+// once.  Per chunk c, both halves:
+//   barrier; issue the loads of chunk c+2;
+//   half 0: PV(c-1), S^T(c)          | half 1: softmax(c-1), convert V(c)
+//   barrier;
+//   half 0: softmax(c), convert V(c) | half 1: PV(c-1), S^T(c)
+//   wait for chunk c+1's loads; note its V range.
+// K of chunk c is read in iteration c (three K stages), V of chunk c in
+// iteration c+1 (four V stages).  V goes to fp16 in place (fp16 P x fp16 V,
+// P <= 2^8 by the lazy rescale); a chunk holding a finite value of magnitude
+// 32768 or more is converted scaled by 2^-k (exact for the fp16 normal
+// range) and its PV product scaled back by 2^k in fp32.
+constexpr int PP_KC = 64;                               // keys per chunk
+constexpr int PP_THREADS = 512;
+constexpr int PP_WAVES = PP_THREADS / 64;
+constexpr int PP_KT = PP_KC / 16;                       // 16-key tiles per chunk
+constexpr int PP_K_LOADS = PP_KC * DQK / 8 / PP_THREADS;  // 3 per thread
+constexpr int PP_V_LOADS = PP_KC * DV / 8 / PP_THREADS;   // 2 per thread
+constexpr int PP_LOADS = PP_K_LOADS + PP_V_LOADS;
+constexpr int PP_KSTAGES = 3, PP_VSTAGES = 4;
+constexpr int PP_KSTAGE = PP_KC * DQK, PP_VSTAGE = PP_KC * DV;  // bf16 elements
+static_assert(PP_K_LOADS * PP_THREADS * 8 == PP_KSTAGE && PP_V_LOADS * PP_THREADS * 8 == PP_VSTAGE,
+              "chunk loads must cover the stages exactly");
+
+#define AI __attribute__((always_inline))
+
+
+// LDS of the G = 16 kernel, at namespace scope so that its two bodies (the
+// common one and the general one) share one allocation.
+__shared__ __attribute__((aligned(1024))) uint16_t pp_kst[PP_KSTAGES][PP_KSTAGE];
+__shared__ __attribute__((aligned(1024))) uint16_t pp_vst[PP_VSTAGES][PP_VSTAGE];
+// per V stage and wave: 1 if the wave's V pieces hold a finite value beyond
+// the fp16 range (the chunk then stays bf16), else 0
+__shared__ __attribute__((aligned(16))) int pp_vbig[PP_VSTAGES][PP_WAVES];
+
+// One workgroup's work.  GEN false: the common body, without the bf16 PV;
+// it returns false, having written nothing, at the first chunk that needs
+// that form (every wave at the same barrier, all loads landed).  GEN true:
+// the general body, either form per chunk.
+template <bool QROPE, bool GEN>
+__device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
+    constexpr int G = 16, BQ = 256 / G;
+    auto &kst = pp_kst;
+    auto &vst = pp_vst;
+    auto &vbig = pp_vbig;
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = w >> 2;
+    const int quad = lane >> 4, col = lane & 15;
+    const int total = a.n_seqs * a.hkv * nqb;
+    const int bid = xcd_remap((int)__builtin_amdgcn_workgroup_id_x(), total);
+    const int qb = bid % nqb;
+    const int g = (bid / nqb) % a.hkv;
+    const int s = bid / (nqb * a.hkv);
+
+    const int64_t tok0 = a.cu_seqlens[s];
+    const int len = (int)(a.cu_seqlens[s + 1] - tok0);
+    if (qb * BQ >= len) return true;
+    // Positions index pool rows (base + position < pool_rows < 2^31, checked
+    // on the host), so they fit in an int; an out-of-contract start is
+    // clamped into [0, pool_rows] and its keys to the pool below.
+    const int64_t start64 = a.start_pos[s];
+    const int start = (int)(start64 < 0 ? 0 : start64 > a.pool_rows ? a.pool_rows : start64);
+    const int p0 = start + qb * BQ;
+    const int plast = start + min(len, qb * BQ + BQ) - 1;
+    const int64_t base = a.seq_base[s];
+    int nkeys = plast + 1;
+    if (base + nkeys > a.pool_rows) nkeys = (int)(a.pool_rows - base);
+    if (base < 0 || nkeys < 0) nkeys = 0;
+    const int klast = max(nkeys - 1, 0);
+    const int nch = max((nkeys + PP_KC - 1) / PP_KC, 1);
+
+    const double invf = QROPE ? pin_loaded(a.inv_freq[lane & 31]) : 0.0;
+    // q of the wave's rows r = 32w + 16n + col (position r / 16, head r % 16)
+    u32x4 qv[2][STEPS];
+    const uint16_t *qg = (const uint16_t *)a.q;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int r = 32 * w + 16 * n + col;
+        const int local = min(qb * BQ + r / G, len - 1);
+        const uint16_t *qrow = qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+        }
+    }
+
+    // With no key in the pool (out of contract) every chunk is masked and
+    // the loads read the pool's first row (the launcher takes this kernel
+    // only for pools of at least one row).
+    const int64_t b0 = nkeys == 0 ? 0 : base;
+    const char *kseq = (const char *)a.k_main + (b0 * a.hkv + g) * (int64_t)(DQK * 2);
+    const char *vseq = (const char *)a.v_main + (b0 * a.hkv + g) * (int64_t)(DV * 2);
+    const int64_t krow = (int64_t)a.hkv * DQK * 2, vrow = (int64_t)a.hkv * DV * 2;
+
+    // LDS fragment order as in full_prefill_kernel, for 64 keys: K unit
+    // (kt * 6 + st) * 64 + lane (16 B) = K[16kt + col][pieces 4st + quad];
+    // V 8-byte unit (hh * 8 + dt) * 64 + lane, hh = 16-key tile.  The i-th
+    // 16-byte load of wave w fills 1 KB block j = 8i + w (j wave-uniform).
+    const int u = lane & 31;
+    const int vrow_l = 4 * (u >> 3) + ((u >> 1) & 3);
+    const uint32_t vbyte_l = 32 * (lane >> 5) + 16 * (u & 1), kbyte_l = 16 * quad;
+    // 32-bit per-lane offsets: 64 rows of either pool span less than 2^31
+    // bytes (the launcher checks).
+    const uint32_t krow32 = (uint32_t)krow, vrow32 = (uint32_t)vrow;
+    // Chunk c's loads into K stage c % 3 and V stage c % 4.  Rows past the
+    // last key are clamped to it (finite data, masked); past the band a
+    // dummy chunk (the first one again) keeps the count per iteration
+    // constant.
+    auto issue = [&](int c) AI {
+        uint16_t *ksd = kst[c % PP_KSTAGES], *vsd = vst[c % PP_VSTAGES];
+        const int kb0 = c < nch ? c * PP_KC : 0;
+        const int lim = klast - kb0;   // the chunk's last existing row, >= 0
+        const char *kb = kseq + (int64_t)kb0 * krow, *vb = vseq + (int64_t)kb0 * vrow;
+#pragma unroll
+        for (int i = 0; i < PP_V_LOADS; ++i) {
+            const int j = PP_WAVES * i + w;
+            const uint32_t row = (uint32_t)min(16 * (j / 4) + vrow_l, lim);
+            load_lds16_s(uniform_ptr(vb + 64 * (j % 4)), row * vrow32 + vbyte_l, (const char *)vsd + j * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < PP_K_LOADS; ++i) {
+            const int j = PP_WAVES * i + w;
+            const uint32_t row = (uint32_t)min(16 * (j / STEPS) + col, lim);
+            load_lds16_s(uniform_ptr(kb + 64 * (j % STEPS)), row * krow32 + kbyte_l, (const char *)ksd + j * 1024);
+        }
+    };
+
+    // Whether the wave's V pieces of chunk c (landed) hold a finite value of
+    // magnitude 65536 or more (bf16 magnitude bits 0x4780 up to, not
+    // including, the non-finite 0x7f80): the fp16 conversion would overflow.
+    // Non-finite values convert to themselves and do not count.
+    auto note_big = [&](int c) AI {
+        const char *vsd = (const char *)vst[c % PP_VSTAGES];
+        bool big = false;
+#pragma unroll
+        for (int i = 0; i < PP_V_LOADS; ++i) {
+            const u32x4 raw = *reinterpret_cast<const u32x4 *>(vsd + (PP_WAVES * i + w) * 1024 + lane * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = raw[e] & 0x7fffu, hi = (raw[e] >> 16) & 0x7fffu;
+                big |= (lo - 0x4780u < 0x7f80u - 0x4780u) || (hi - 0x4780u < 0x7f80u - 0x4780u);
+            }
+        }
+        const bool any = __any(big);
+        if (lane == 0) vbig[c % PP_VSTAGES][w] = any ? 1 : 0;
+    };
+    // Whether chunk c stays bf16 (every wave's note published by a barrier).
+    auto chunk_big = [&](int c) AI {
+        const u32x4 f0 = *reinterpret_cast<const u32x4 *>(&vbig[c % PP_VSTAGES][0]);
+        const u32x4 f1 = *reinterpret_cast<const u32x4 *>(&vbig[c % PP_VSTAGES][4]);
+        // the same in every lane: said so, so that a branch on it is scalar
+        return __builtin_amdgcn_readfirstlane((f0[0] | f0[1] | f0[2] | f0[3]) | (f1[0] | f1[1] | f1[2] | f1[3])) != 0;
+    };
+    // Convert the wave's V pieces of chunk c to fp16 in place (exact for
+    // bf16 values from 2^-14 up to 65536; smaller ones are rounded to fp16's
+    // absolute step 2^-24).  A chunk that stays bf16 is left as loaded.
+    auto convert_v = [&](int c, bool big) AI {
+        if (big) return;
+        char *vsd = (char *)vst[c % PP_VSTAGES];
+#pragma unroll
+        for (int i = 0; i < PP_V_LOADS; ++i) {
+            u32x4 *pp = reinterpret_cast<u32x4 *>(vsd + (PP_WAVES * i + w) * 1024 + lane * 16);
+            const u32x4 raw = *pp;
+            u32x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(raw[e]);
+            *pp = h;
+        }
+    };
+    // P (packed fp16) as bf16 hi + lo with hi + lo == P exactly: fp16's 11
+    // significant bits are bf16's 8 plus at most 3.
+    auto split_p = [&](const u32x4 &p, u32x4 &hi, u32x4 &lo) AI {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // (the element through a scalar: a bit cast of a vector element
+            // taken in place reads element 0 whatever the index)
+            const uint32_t word = p[e];
+            const f16x2 v = __builtin_bit_cast(f16x2, word);
+            const float x = (float)v[0], y = (float)v[1];
+            const uint32_t xh = __float_as_uint(x) & 0xffff0000u, yh = __float_as_uint(y) & 0xffff0000u;
+            hi[e] = (xh >> 16) | yh;
+            lo[e] = pack_bf16x2(x - __uint_as_float(xh), y - __uint_as_float(yh));
+        }
+    };
+
+    const float scale2 = a.scale * kLog2e;
+    f32x4 oacc[2][DT];
+    float m[2], l[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        m[n] = -INFINITY;
+        l[n] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
+    }
+    const int wpos_lo = p0 + (32 * w) / G, wpos_hi = p0 + (32 * w + 31) / G;
+    const int vis_hi = min(wpos_hi, nkeys - 1), vis_lo = min(wpos_lo, nkeys - 1);
+    auto visible = [&](int c) AI { return c >= 0 && c < nch && c * PP_KC <= vis_hi; };
+
+    // S^T of chunk c (accumulators), P of the chunk before (fp16, per row
+    // tile and 32-key half)
+    f32x4 sacc[PP_KT][2];
+    u32x4 pf[2][2];
+    // a rescale of O the softmax found needed, applied before the next PV
+    bool rs_pend = false;
+    float rs_f[2] = {1.0f, 1.0f};
+#pragma unroll
+    for (int n = 0; n < 2; ++n) pf[n][0] = pf[n][1] = u32x4{0, 0, 0, 0};
+
+    // MFMA phase: PV of chunk c-1 (V stage, P from the softmax), then S^T of c.
+    auto mfma_phase = [&](int c, bool bigprev) AI {
+        if (visible(c - 1)) {
+            const uint16_t *vsc = vst[(c - 1) % PP_VSTAGES];
+            if (rs_pend) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= rs_f[n];
+            }
+            if (!bigprev) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const u32x2 a0 = ds_read_tr16(vsc + ((2 * kh * 8 + dt) * 64 + lane) * 4);
+                        const u32x2 a1 = ds_read_tr16(vsc + (((2 * kh + 1) * 8 + dt) * 64 + lane) * 4);
+                        const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+                        for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf[n][kh], oacc[n][dt]);
+                    }
+            } else {
+                // bf16 V times P split exactly into bf16 hi + lo
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    u32x4 ph[2], pl[2];
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) split_p(pf[n][kh], ph[n], pl[n]);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const u32x2 a0 = ds_read_tr16(vsc + ((2 * kh * 8 + dt) * 64 + lane) * 4);
+                        const u32x2 a1 = ds_read_tr16(vsc + (((2 * kh + 1) * 8 + dt) * 64 + lane) * 4);
+                        const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+                        for (int n = 0; n < 2; ++n) {
+                            oacc[n][dt] = mfma_16x16x32_bf16(av, ph[n], oacc[n][dt]);
+                            oacc[n][dt] = mfma_16x16x32_bf16(av, pl[n], oacc[n][dt]);
+                        }
+                    }
+                }
+            }
+        }
+        if (visible(c)) {
+            const uint16_t *ksc = kst[c % PP_KSTAGES];
+#pragma unroll
+            for (int kt = 0; kt < PP_KT; ++kt)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) sacc[kt][n] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                for (int kt = 0; kt < PP_KT; ++kt) {
+                    const u32x4 ak = *reinterpret_cast<const u32x4 *>(ksc + ((kt * STEPS + st) * 64 + lane) * 8);
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) sacc[kt][n] = mfma_16x16x32_bf16(ak, qv[n][st], sacc[kt][n]);
+                }
+        }
+    };
+    // VALU phase: online softmax of chunk c's S^T into P (fp16).
+    auto softmax = [&](int c) AI {
+        if (!visible(c)) return;
+        const int k0 = c * PP_KC;
+        if (k0 + PP_KC - 1 > vis_lo) {
+            // key 16 kt + 4 quad + j of the chunk is visible to row r iff it
+            // is at most min(position of r, nkeys - 1)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int d = min(p0 + (32 * w + 16 * n + col) / G, nkeys - 1) - (k0 + 4 * quad);
+#pragma unroll
+                for (int kt = 0; kt < PP_KT; ++kt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (16 * kt + j > d) sacc[kt][n][j] = -INFINITY;
+            }
+        }
+        // New reference maxima first; the O rescale (rare) after P, so that
+        // it does not overlap the exponentials.
+        float fr[2] = {1.0f, 1.0f};
+        bool resc = false;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float cm = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < PP_KT; ++kt)
+                cm = fmaxf(cm, fmaxf(fmaxf(sacc[kt][n][0], sacc[kt][n][1]), fmaxf(sacc[kt][n][2], sacc[kt][n][3])));
+            cm = quad_max_swap(cm) * scale2;
+            const bool raise = cm > m[n] + kRescale;
+            if (__any(raise)) {
+                const float mn = raise ? cm : m[n];
+                if (__any(raise && m[n] != -INFINITY)) {
+                    fr[n] = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
+                    l[n] *= fr[n];
+                    resc = true;
+                }
+                m[n] = mn;
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const float mu = m[n] == -INFINITY ? 0.0f : -m[n];
+            float pv[PP_KT][4];
+#pragma unroll
+            for (int kt = 0; kt < PP_KT; ++kt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pv[kt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][n][j], scale2, mu));
+                    l[n] += pv[kt][j];
+                }
+            // P <= 2^8: fp16 keeps 11 significant bits.  32-key half kh takes
+            // tiles 2kh (slots 0-3) and 2kh + 1 (slots 4-7).
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+                pf[n][kh] = u32x4{pack_f16x2(pv[2 * kh][0], pv[2 * kh][1]), pack_f16x2(pv[2 * kh][2], pv[2 * kh][3]),
+                                  pack_f16x2(pv[2 * kh + 1][0], pv[2 * kh + 1][1]),
+                                  pack_f16x2(pv[2 * kh + 1][2], pv[2 * kh + 1][3])};
+        }
+        rs_pend = resc;
+        rs_f[0] = fr[0];
+        rs_f[1] = fr[1];
+    };
+    auto barrier = [&]() AI {
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+
+    // Epilogue: an optional sink joins the denominator once; scale; bf16.
+    // Each wave turns its 32 x 128 output tile around in LDS (8 KB of the K
+    // stages each) so that the stores cover whole 256-byte rows.
+    auto finish = [&]() AI {
+        uint16_t *ep = &kst[0][0] + w * (32 * DV);
+    #pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int r = 32 * w + 16 * n + col;
+            float ll = quad_sum_swap(l[n]);
+            const int head = r % G;
+            float mm = m[n], fac = 1.0f;
+            if (a.sinks) {
+                float sk = a.sinks[g * G + head] * kLog2e;
+                float mf = fmaxf(mm, sk);
+                fac = exp2f(mm - mf);
+                ll = ll * fac + exp2f(sk - mf);
+            }
+            const float rs = a.value_scale * fac / ll;
+            const int row = 16 * n + col;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o = oacc[n][dt];
+                const u32x2 pk = u32x2{pack_bf16x2(o[0] * rs, o[1] * rs), pack_bf16x2(o[2] * rs, o[3] * rs)};
+                const int unit = (2 * dt + (quad >> 1)) ^ (row & 15);
+                *reinterpret_cast<u32x2 *>(ep + row * DV + unit * 8 + 4 * (quad & 1)) = pk;
+            }
+        }
+        uint16_t *outg = (uint16_t *)a.out;
+    #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4), c = lane & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * DV + ((c ^ (row & 15)) * 8));
+            const int r = 32 * w + row;
+            const int local = qb * BQ + r / G;
+            if (local < len)
+                st16(outg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DV + 8 * c, v);
+        }
+    };
+
+    {
+        issue(0);
+        issue(1);
+        if constexpr (QROPE) {
+            // Rotate q in registers with the RoPE kernel's helpers (bit for
+            // bit RoPE then this kernel).  The wave's 32 rows cover 2
+            // positions; table entry e = 32 i + f is frequency f at position
+            // pw + i, cos then sin, in V stage 3 (first loaded in iteration 1).
+            float *tc = reinterpret_cast<float *>(vst[3]) + w * 64;
+            float *ts = reinterpret_cast<float *>(vst[3]) + PP_WAVES * 64 + w * 64;
+            const int pw = p0 + (32 * w) / G;
+            {
+                float cv, sv;
+                rope_cos_sin((int64_t)(pw + lane / 32), invf, cv, sv);
+                tc[lane] = cv;
+                ts[lane] = sv;
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int pi = (16 * n + col) / G;
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad);
+                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad + 4);
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad);
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad + 4);
+                const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                rope_rotate_bf16x8(qv[n][0], qv[n][1], cc, ss);
+            }
+            settle_q(qv);
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+            __asm__ volatile("" ::: "memory");
+        } else {
+            // q landed here once (the compiler's wait for it, counting only
+            // its own loads, is for everything: chunks 0 and 1 too), not at
+            // first use inside the loop
+            settle_q(qv);
+        }
+        // The chunk loop, one copy per half.  Half 0 runs the MFMA phase of
+        // chunk c first, half 1 its VALU phase; half 1's loop is rotated to
+        // start at the second barrier, so that in both copies only P (not
+        // S^T) is live across an iteration.
+        auto mfma_hi = [&](int c, bool bigprev) AI {
+            __builtin_amdgcn_s_setprio(1);
+            mfma_phase(c, bigprev);
+            __builtin_amdgcn_s_setprio(0);
+        };
+        auto await_next = [&](int c) AI {   // chunk c+1 landed; its V noted
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+            __asm__ volatile("" ::: "memory");
+            if (c + 1 < nch) note_big(c + 1);
+        };
+        auto leave = [&]() AI {   // every load landed and every wave here
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __asm__ volatile("" ::: "memory");
+            barrier();
+        };
+        // Without GEN the loops leave at the first chunk that needs the
+        // bf16 PV (known to every wave after the same barrier).
+        note_big(0);
+        bool bailed = false;
+        if (half == 0) {
+            bool big_this = false;
+#pragma clang loop unroll(disable)
+            for (int c = 0; c <= nch; ++c) {
+                barrier();                     // chunk c's K, V and V note visible; iteration c-1 done
+                issue(c + 2);
+                const bool big_prev = big_this;  // chunk c-1, whose PV runs now
+                if (c < nch) big_this = chunk_big(c);
+                if (!GEN && big_this) {
+                    bailed = true;
+                    break;
+                }
+                mfma_hi(c, GEN && big_prev);
+                barrier();
+                softmax(c);
+                if (c < nch) {
+                    convert_v(c, GEN && big_this);
+                    await_next(c);
+                }
+            }
+        } else {
+            barrier();
+            issue(2);
+            bool big_this = chunk_big(0), big_prev = false;
+            if (!GEN && big_this) {
+                leave();
+                return false;
+            }
+            convert_v(0, GEN && big_this);
+#pragma clang loop unroll(disable)
+            for (int c = 0;; ++c) {
+                barrier();
+                mfma_hi(c, GEN && big_prev);
+                if (c == nch) break;
+                await_next(c);
+                barrier();                     // chunk c+1's K, V and V note visible
+                issue(c + 3);
+                big_prev = big_this;
+                if (c + 1 < nch) big_this = chunk_big(c + 1);
+                if (!GEN && big_this) {
+                    bailed = true;
+                    break;
+                }
+                softmax(c);
+                if (c + 1 < nch) convert_v(c + 1, GEN && big_this);
+            }
+        }
+        leave();   // every load landed (the dummy ones too) before LDS is reused
+        if (!GEN && bailed) return false;
+        finish();
+        return true;
+    }
+}
+
+template <bool QROPE>
+__global__ __launch_bounds__(PP_THREADS, 1) void full_prefill_pp_kernel(AttnArgs a, int nqb) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
+    // The common body; a workgroup that met a chunk needing the bf16 PV
+    // starts over in the general one (its loop comes after the common loop
+    // and shares none of its registers).
+    if (pp_body<QROPE, false>(a, nqb)) return;
+    pp_body<QROPE, true>(a, nqb);
+}
+
 }  // namespace
 
 bool full_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
@@ -583,6 +1109,15 @@ bool full_qrope_ok(const AttnArgs &a, int dtype, int out_dtype, bool prefill) {
 
 hipError_t launch_full_prefill(const AttnArgs &a, hipStream_t s) {
     const int G = a.hq / a.hkv;
+    if (G == 16 && a.pool_rows > 0 && (int64_t)a.hkv * DQK * 2 * PP_KC < (int64_t(1) << 31)) {
+        const int64_t nqb = (a.max_seqlen + 15) / 16;
+        dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(PP_THREADS);
+        if (a.qrope)
+            hipLaunchKernelGGL((full_prefill_pp_kernel<true>), grid, block, 0, s, a, (int)nqb);
+        else
+            hipLaunchKernelGGL((full_prefill_pp_kernel<false>), grid, block, 0, s, a, (int)nqb);
+        return hipGetLastError();
+    }
     const int BQ = 128 / G;
     const int64_t nqb = (a.max_seqlen + BQ - 1) / BQ;
     dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(kThreads);

@@ -597,9 +597,9 @@ def test_full_prefill_values_beyond_fp16_range():
 
 
 def test_full_prefill_values_beyond_fp16_range_in_some_columns():
-    """Out-of-fp16-range V confined to a few columns (inside one or two of
-    the four 32-column blocks of a 32-key chunk): those blocks keep bf16 while
-    the rest of the chunk goes through fp16, and the result still matches."""
+    """Out-of-fp16-range V confined to a few columns of some rows: the keys
+    around them keep bf16 while the rest go through fp16, and the result
+    still matches."""
     note("full_prefill large V in some columns")
     batch = wl.full_prefill_batch(seed=74, n_seqs=2, seqlens=(150, 90), start_pos=(250, 60))
     rows = batch["vpool"].shape[0]
@@ -614,6 +614,30 @@ def test_full_prefill_values_beyond_fp16_range_in_some_columns():
     ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * float(np.abs(ref).max()),
                           what="full_prefill large V in some columns")
     print(f"full_prefill large V in some columns: max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+@pytest.mark.parametrize("model", ["flash", "pro"])
+def test_full_prefill_values_beyond_fp16_range_late_chunk(model):
+    """Out-of-fp16-range V only in keys well past the first ones: query
+    blocks meet it after many ordinary 64-key chunks (some only in their
+    last one, some in a chunk of new rows), others never."""
+    note(f"full_prefill large V in a late chunk {model}")
+    batch = wl.full_prefill_batch(seed=75, n_seqs=3, seqlens=(300, 100, 40), start_pos=(500, 0, 64),
+                                  **wl.model_kw(wl.MODELS[model], "full"))
+    base = batch["seq_base"].tolist()
+    vp = batch["vpool"].float()
+    vp[base[0] + 431] *= 2.5e5          # a prior row of sequence 0
+    vp[base[2] + 63, 1] *= -4.0e5       # the last prior row of sequence 2, one KV head
+    batch["vpool"] = vp.to(torch.bfloat16)
+    v = batch["v"].float()
+    v[250] *= 3.0e5                     # a new row of sequence 0 (position 750)
+    batch["v"] = v.to(torch.bfloat16)
+    q_rot, kpool, vpool, out = run_full_prefill(batch)
+    cu = batch["cu_seqlens"].tolist()
+    idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, [np.arange(cu[s], cu[s + 1]) for s in range(3)])
+    ma, mr = assert_close(f64(out)[idx], ref, max_abs=2e-2 * float(np.abs(ref).max()),
+                          what="full_prefill large V late chunk")
+    print(f"full_prefill large V late chunk {model}: max_abs={ma:.2e} mean_rel={mr:.2e}")
 
 
 # ------------------------------------------------------- degenerate cases
@@ -856,7 +880,7 @@ def run_full_prefill_qrope(batch, kpool, vpool):
 
 
 @pytest.mark.parametrize("model", ["flash", "pro"])
-@pytest.mark.parametrize("case", ["ragged", "8192_after_131072"])
+@pytest.mark.parametrize("case", ["ragged", "large_v", "8192_after_131072"])
 def test_full_prefill_qrope_bitwise_equals_rope_then_prefill(case, model):
     """The fused chunked prefill rotates q with the RoPE call's arithmetic and
     stores it as bf16 in the same registers the unfused kernel loads q_rot
@@ -866,9 +890,18 @@ def test_full_prefill_qrope_bitwise_equals_rope_then_prefill(case, model):
     call's q_rot and pool rows."""
     note(f"full_prefill_qrope bitwise {case} {model}")
     kw = wl.model_kw(wl.MODELS[model], "full")
-    if case == "ragged":
+    if case in ("ragged", "large_v"):
         batch = wl.full_prefill_batch(seed=73, n_seqs=4, seqlens=(300, 77, 129, 1),
                                       start_pos=(3000, 100, 0, 40000), **kw)
+        if case == "large_v":
+            # out-of-fp16-range values in a late chunk of sequence 0 and in
+            # the first chunk of sequence 2: their query blocks take the
+            # kernel's general path, fused or not
+            base = batch["seq_base"].tolist()
+            vp = batch["vpool"].float()
+            vp[base[0] + 2500] *= 2.0e5
+            vp[base[2] + 10] *= -3.0e5
+            batch["vpool"] = vp.to(torch.bfloat16)
     else:
         batch = wl.full_prefill_batch(seed=5, device=DEV, **kw)
     kpool0, vpool0 = dev(batch["kpool"]).clone(), dev(batch["vpool"]).clone()
@@ -880,13 +913,14 @@ def test_full_prefill_qrope_bitwise_equals_rope_then_prefill(case, model):
     # and pool rows (all rows of the ragged chunks; 256 rows of the full one,
     # drawn apart from the unfused test's sample)
     cu = batch["cu_seqlens"].tolist()
-    if case == "ragged":
+    if case != "8192_after_131072":
         rows = [np.arange(cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
     else:
         rows = [sampled_chunk_rows(8192, seed=6)]
     idx, ref = oracle_full_prefill(batch, q_rot, kpool, vpool, rows)
+    bar = dict(max_abs=2e-2 * float(np.abs(ref).max())) if case == "large_v" else {}
     ma, mr = assert_close(f64(out2[torch.from_numpy(idx).to(out2.device)]), ref,
-                          what=f"full_prefill_qrope {case} {model}")
+                          what=f"full_prefill_qrope {case} {model}", **bar)
     print(f"full_prefill_qrope {case} {model}: bitwise equal to RoPE + prefill over {out.shape[0]} rows; "
           f"{len(idx)} rows against the oracle: max_abs={ma:.2e} mean_rel={mr:.2e}")
 

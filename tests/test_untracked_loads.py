@@ -97,3 +97,45 @@ def test_prefill_q_loads_are_never_touched_in_flight(src, kernel, n):
     assert len(kernels) == n
     for name, body in kernels.items():
         assert avc.check(body) == [], name
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
+def test_full_prefill_g16_kernel_keeps_its_loop_registers():
+    """The G = 16 full-attention kernel (common and general bodies, with and
+    without the fused q-RoPE) touches no register an untracked load may still
+    be writing, and its common loop neither spills nor waits for every load
+    in flight (a spill reload there is followed by vmcnt(0), which would also
+    wait for the chunk loads the pipeline keeps in flight)."""
+    asm = avc.compile_to_asm(os.path.join(CSRC, "full_prefill.hip"))
+    kernels = {k: v for k, v in avc.kernel_functions(asm).items() if "full_prefill_pp_kernel" in k}
+    assert len(kernels) == 2
+    for name, body in kernels.items():
+        assert avc.check(body) == [], name
+        loops = loop_bodies(body)
+        common = [b for b in loops.values() if not any("v_cvt_f32_f16" in l for l in b)]
+        assert len(common) == 2, f"{name}: expected one common chunk loop per half"
+        for b in common:
+            assert not any("scratch_" in l for l in b), f"{name}: the common loop spills"
+            assert not any("vmcnt(0)" in l for l in b), f"{name}: the common loop waits for every load"
+
+
+def loop_bodies(body):
+    """Outermost loops of a function's assembly, by the compiler's block
+    annotations ("Loop Header: Depth=1", "in Loop: Header=BBn_m"): header
+    label -> the lines of the blocks in that loop.  (The P split of the
+    general body converts fp16 to fp32 with v_cvt_f32_f16; the common body
+    never does.)"""
+    import re
+    out, cur = {}, None
+    for line in body:
+        m = re.match(r"^\.?(LBB\w+|; %bb\.\d+):?", line)
+        if m or line.startswith("; %bb."):
+            h = re.search(r"Header=(BB\w+)", line)
+            if "Loop Header: Depth=1" in line:
+                cur = line.split(":")[0].lstrip(".").lstrip("L")
+            else:
+                cur = h.group(1) if h else None
+            continue
+        if cur is not None:
+            out.setdefault(cur, []).append(line)
+    return out
