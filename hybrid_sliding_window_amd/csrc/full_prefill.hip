@@ -69,6 +69,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) alone
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
 // lds_wave_base + 16 i (lds_wave_base is wave-uniform, passed in m0; said
@@ -721,17 +722,19 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
     // Non-finite values convert to themselves and do not count.
     auto note_big = [&](int c) AI {
         const char *vsd = (const char *)vst[c % PP_VSTAGES];
-        bool big = false;
+        // per 16-bit half: magnitude - 0x4780 (wrapping) < 0x3800 is the
+        // range test; the minimum over the pieces decides it
+        u16x2 mn = u16x2{0xffff, 0xffff};
 #pragma unroll
         for (int i = 0; i < PP_V_LOADS; ++i) {
             const u32x4 raw = *reinterpret_cast<const u32x4 *>(vsd + (PP_WAVES * i + w) * 1024 + lane * 16);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = raw[e] & 0x7fffu, hi = (raw[e] >> 16) & 0x7fffu;
-                big |= (lo - 0x4780u < 0x7f80u - 0x4780u) || (hi - 0x4780u < 0x7f80u - 0x4780u);
+                const uint32_t mag = raw[e] & 0x7fff7fffu;
+                mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2, mag) - u16x2{0x4780, 0x4780});
             }
         }
-        const bool any = __any(big);
+        const bool any = __any(mn[0] < 0x3800 || mn[1] < 0x3800);
         if (lane == 0) vbig[c % PP_VSTAGES][w] = any ? 1 : 0;
     };
     // Whether chunk c stays bf16 (every wave's note published by a barrier).
@@ -775,14 +778,19 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
 
     const float scale2 = a.scale * kLog2e;
     f32x4 oacc[2][DT];
-    float m[2], l[2];
+    // m: reference max per row; lacc: the row sums of the fp16 P the PV
+    // products take, formed by the same MFMA with an all-ones V^T operand
+    // (every element of a row's lacc holds the sum)
+    float m[2];
+    f32x4 lacc[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         m[n] = -INFINITY;
-        l[n] = 0.0f;
+        lacc[n] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
     }
+    const u32x4 ones_f16 = u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
     const int wpos_lo = p0 + (32 * w) / G, wpos_hi = p0 + (32 * w + 31) / G;
     const int vis_hi = min(wpos_hi, nkeys - 1), vis_lo = min(wpos_lo, nkeys - 1);
     auto visible = [&](int c) AI { return c >= 0 && c < nch && c * PP_KC <= vis_hi; };
@@ -803,21 +811,45 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
             const uint16_t *vsc = vst[(c - 1) % PP_VSTAGES];
             if (rs_pend) {
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < 2; ++n) {
+                    lacc[n] *= rs_f[n];
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= rs_f[n];
+                }
             }
+            // row sums of P (both forms of the PV take the same fp16 P)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(ones_f16, pf[n][kh], lacc[n]);
             if (!bigprev) {
+                // 16 tiles (kh, dt) in 4 groups of 4; the V^T reads of group
+                // g+1 are issued before the MFMAs of group g (fenced, so the
+                // scheduler keeps them a group ahead of their use)
+                u32x2 vb[2][4][2];
+                auto vread = [&](int g, u32x2 (&d)[4][2]) AI {
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+                    for (int i = 0; i < 4; ++i) {
+                        const int kh = (4 * g + i) / DT, dt = (4 * g + i) % DT;
+                        d[i][0] = ds_read_tr16(vsc + ((2 * kh * 8 + dt) * 64 + lane) * 4);
+                        d[i][1] = ds_read_tr16(vsc + (((2 * kh + 1) * 8 + dt) * 64 + lane) * 4);
+                    }
+                };
+                vread(0, vb[0]);
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const u32x2 a0 = ds_read_tr16(vsc + ((2 * kh * 8 + dt) * 64 + lane) * 4);
-                        const u32x2 a1 = ds_read_tr16(vsc + (((2 * kh + 1) * 8 + dt) * 64 + lane) * 4);
-                        const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                for (int g = 0; g < 4; ++g) {
+                    if (g + 1 < 4) vread(g + 1, vb[(g + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kh = (4 * g + i) / DT, dt = (4 * g + i) % DT;
+                        const u32x4 av = u32x4{vb[g & 1][i][0][0], vb[g & 1][i][0][1], vb[g & 1][i][1][0],
+                                               vb[g & 1][i][1][1]};
 #pragma unroll
                         for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pf[n][kh], oacc[n][dt]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             } else {
                 // bf16 V times P split exactly into bf16 hi + lo
 #pragma unroll
@@ -845,14 +877,24 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
             for (int kt = 0; kt < PP_KT; ++kt)
 #pragma unroll
                 for (int n = 0; n < 2; ++n) sacc[kt][n] = f32x4{0, 0, 0, 0};
+            // the K reads of step st+1 are issued before the MFMAs of step st
+            u32x4 kb[2][PP_KT];
+            auto kread = [&](int st, u32x4 (&d)[PP_KT]) AI {
 #pragma unroll
-            for (int st = 0; st < STEPS; ++st)
+                for (int kt = 0; kt < PP_KT; ++kt)
+                    d[kt] = *reinterpret_cast<const u32x4 *>(ksc + ((kt * STEPS + st) * 64 + lane) * 8);
+            };
+            kread(0, kb[0]);
 #pragma unroll
-                for (int kt = 0; kt < PP_KT; ++kt) {
-                    const u32x4 ak = *reinterpret_cast<const u32x4 *>(ksc + ((kt * STEPS + st) * 64 + lane) * 8);
+            for (int st = 0; st < STEPS; ++st) {
+                if (st + 1 < STEPS) kread(st + 1, kb[(st + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) sacc[kt][n] = mfma_16x16x32_bf16(ak, qv[n][st], sacc[kt][n]);
-                }
+                for (int kt = 0; kt < PP_KT; ++kt)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) sacc[kt][n] = mfma_16x16x32_bf16(kb[st & 1][kt], qv[n][st], sacc[kt][n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
     // VALU phase: online softmax of chunk c's S^T into P (fp16).
@@ -888,7 +930,6 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
                 const float mn = raise ? cm : m[n];
                 if (__any(raise && m[n] != -INFINITY)) {
                     fr[n] = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
-                    l[n] *= fr[n];
                     resc = true;
                 }
                 m[n] = mn;
@@ -901,10 +942,8 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
 #pragma unroll
             for (int kt = 0; kt < PP_KT; ++kt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j)
                     pv[kt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][n][j], scale2, mu));
-                    l[n] += pv[kt][j];
-                }
             // P <= 2^8: fp16 keeps 11 significant bits.  32-key half kh takes
             // tiles 2kh (slots 0-3) and 2kh + 1 (slots 4-7).
 #pragma unroll
@@ -932,7 +971,7 @@ __device__ __forceinline__ bool pp_body(const AttnArgs &a, int nqb) {
     #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int r = 32 * w + 16 * n + col;
-            float ll = quad_sum_swap(l[n]);
+            float ll = lacc[n][0];
             const int head = r % G;
             float mm = m[n], fac = 1.0f;
             if (a.sinks) {
