@@ -17,7 +17,13 @@ scale 0.612, 70 layers of which 10 full).
 
 Inputs are resident in HBM before each timed region.  Timed regions cycle
 over enough replicas of the inputs that every launch reads HBM rather than
-the 256 MB Infinity Cache.
+the 256 MB Infinity Cache.  Every call is timed as 5 runs of N back-to-back
+launches between two HIP events (N >= 200 for the windowed calls, >= 20 for
+the full decode, >= 3 hybrid steps) and reported as the median run; the
+runs themselves are kept for the headline call.  The GPU's clocks and power
+(rocm-smi; clocks are not locked) and the host CPU model are recorded, and
+the fp64 oracle is timed on workloads 1-4 in full and on a sample of the
+hybrid step, extrapolated by row count and labelled so.
 """
 from __future__ import annotations
 
@@ -25,6 +31,8 @@ import argparse
 import json
 import math
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -80,16 +88,73 @@ def warm(fn, stream, seconds=0.3):
     stream.synchronize()
 
 
-def ev_time(fn, n, stream):
-    """Mean ms per call of fn() over n back-to-back calls, HIP events on `stream`."""
+RUNS = 5   # timed runs per call; the median is reported
+
+
+def ev_time(fn, n, stream, runs=None, reps=None):
+    """Median over RUNS (or `reps`) runs of the mean ms per call of fn() over
+    n back-to-back calls, each run bracketed by HIP events on `stream`.  The
+    per-run means are appended to `runs` when given."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(n):
-        fn(i)
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / n
+    per = []
+    k = 0
+    for r in range(reps or RUNS):
+        start.record(stream)
+        for i in range(n):
+            fn(k)
+            k += 1
+        end.record(stream)
+        end.synchronize()
+        per.append(start.elapsed_time(end) / n)
+    if runs is not None:
+        runs.extend(per)
+    return statistics.median(per)
+
+
+def gpu_clocks_power():
+    """The GPU's current clocks and power as rocm-smi reports them (a child
+    process; clocks are not locked), or the error that prevented it."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=60)
+        d = json.loads(r.stdout)
+    except Exception as e:  # noqa: BLE001 - recorded, never fatal
+        return {"error": f"rocm-smi: {type(e).__name__}: {str(e)[:160]}"}
+    out = {}
+    for card, vals in d.items():
+        if isinstance(vals, dict):
+            out[card] = {k: v for k, v in vals.items() if "clock" in k.lower() or "power" in k.lower()
+                         or k.lower().startswith(("sclk", "mclk", "fclk", "socclk"))}
+    if not any("power" in k.lower() for v in out.values() for k in v):
+        # rocm-smi printed no power: the driver's hwmon average power, if readable
+        import glob
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_average")
+                        + glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")):
+            try:
+                with open(f) as fh:
+                    out.setdefault("hwmon", {})[f.split("/device/")[0].rsplit("/", 1)[1] + " " +
+                                             os.path.basename(f)] = f"{int(fh.read()) / 1e6:.1f} W"
+            except (OSError, ValueError):
+                pass
+        if "hwmon" not in out:
+            out["power"] = "not reported by rocm-smi or hwmon on this machine"
+    return out
+
+
+def host_cpu():
+    """CPU model name (/proc/cpuinfo) and the cores this process sees."""
+    name = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": name, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def swa_prefill_pairs(lens, starts, window=128):
@@ -132,8 +197,10 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
         call(i)
         rope(i)
     warm(call, stream)
-    t_call = ev_time(call, steps, stream)
-    t_rope = ev_time(rope, max(steps, 20), stream)
+    runs = []
+    n = max(steps, 200)
+    t_call = ev_time(call, n, stream, runs)
+    t_rope = ev_time(rope, n, stream)
 
     # the fused chain: K/V-only RoPE into staging, then the prefill that
     # rotates q itself (no q_rot written or read)
@@ -146,8 +213,8 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
                                   d["vring"], d["sinks"], out, stream)
     fused(0)
     warm(fused, stream)
-    t_fused = ev_time(fused, steps, stream)
-    t_rope_kv = ev_time(rope_kv, max(steps, 20), stream)
+    t_fused = ev_time(fused, n, stream)
+    t_rope_kv = ev_time(rope_kv, n, stream)
     pairs = swa_prefill_pairs([T1] * S, [0] * S)
     flops = pairs * hq * 2 * (192 + 128)
     # algorithmic bytes: q_rot, staged K/V read once, out written once, the
@@ -163,12 +230,44 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
                               "RoPE + hsw_swa_prefill, same workload")
     return dict(
         fused=fused_res,
-        ms=t_call, flops=flops, bytes=bytes_, tokens=T, tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
+        ms=t_call, runs_ms=runs, launches_per_run=n, flops=flops, bytes=bytes_, tokens=T,
+        tflops=flops / t_call / 1e9, gbs=bytes_ / t_call / 1e6,
         frac_mfma_peak=flops / t_call / 1e9 / BF16_PEAK_TFLOPS, frac_hbm_peak=bytes_ / t_call / 1e6 / HBM_PEAK_GBS,
         workload=f"windowed prefill, 4 x 8192 tokens from position 0, {heads(model)}, window 128",
         rope=dict(ms=t_rope, bytes=rope_bytes, tokens=T, gbs=rope_bytes / t_rope / 1e6,
                   frac_hbm_peak=rope_bytes / t_rope / 1e6 / HBM_PEAK_GBS,
                   workload=f"RoPE + staging write of 32768 tokens ({heads(model)})"))
+
+
+def bench_c1(hsw, wl, steps, stream):
+    """The fp32 windowed layer (1 x 512 tokens, 4 q / 1 KV head, logits near
+    -25, sinks near +1): RoPE + staging write, then the windowed prefill.
+    Launch-bound: the time is reported with no roofline claim."""
+    d = wl.logit_shift_layer()
+    sh = d["shape"]
+    T = 512
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q_rot, kst, vst = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    kring = torch.zeros((1, 1, 128, 192), dtype=torch.float32, device=DEV)
+    vring = torch.zeros((1, 1, 128, 128), dtype=torch.float32, device=DEV)
+    out = torch.empty((T, 4, 128), dtype=torch.float32, device=DEV)
+
+    def rope(i):
+        hsw.hsw_rope_partial_kv_write(sh, T, g["q"], g["k"], g["v"], g["pos"], None, hsw.HSW_DST_STAGING,
+                                      kst, vst, T, None, q_rot, None, stream)
+
+    def prefill(i):
+        hsw.hsw_swa_prefill(sh, 1, T, g["cu_seqlens"], g["start_pos"], q_rot, kst, vst, kring, vring, g["sinks"],
+                            out, stream)
+    for i in range(10):
+        rope(i)
+        prefill(i)
+    n = max(steps, 200)
+    t_rope = ev_time(rope, n, stream)
+    t_pre = ev_time(prefill, n, stream)
+    return dict(rope_ms=t_rope, swa_prefill_ms=t_pre, chain_ms=t_rope + t_pre, launches_per_run=n, tokens=T,
+                roofline=None, workload="one windowed layer in fp32: 1 x 512 tokens, 4 q / 1 KV head, window 128, "
+                                        "sinks, logits near -25 (launch-bound; no roofline claim)")
 
 
 def bench_copy(steps, stream, nbytes=1 << 30):
@@ -264,7 +363,8 @@ def bench_full_decode(hsw, wl, steps, stream, model=None):
     for i in range(3):
         call(i)
     torch.cuda.synchronize()
-    t = ev_time(call, max(steps // 2, 10), stream)
+    n = max(steps // 2, 20)
+    t = ev_time(call, n, stream)
 
     # the fused chain: K/V-only RoPE into the pool, then the decode that
     # rotates q itself (fp32 rotated dims, no q_rot written or read)
@@ -282,7 +382,7 @@ def bench_full_decode(hsw, wl, steps, stream, model=None):
     for i in range(3):
         fused(i)
     torch.cuda.synchronize()
-    t_fused = ev_time(fused, max(steps // 2, 10), stream)
+    t_fused = ev_time(fused, n, stream)
     t_rope = ev_time(rope, max(steps, 20), stream)
     t_rope_kv = ev_time(rope_kv, max(steps, 20), stream)
     L = int(b["ctx_len"].sum())
@@ -294,7 +394,7 @@ def bench_full_decode(hsw, wl, steps, stream, model=None):
                      workload="K/V-only RoPE into the pool + hsw_full_decode_splitk_qrope (q rotated in the "
                               "kernel, kept in fp32) against RoPE + hsw_full_decode_splitk, same workload")
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
-                tflops=flops / t / 1e9, flops=flops, tokens=S, fused=fused_res,
+                tflops=flops / t / 1e9, flops=flops, tokens=S, launches_per_run=n, fused=fused_res,
                 workload=f"full-attention decode, 64 sequences, contexts U{{32768..131072}}, {hq} q / {hkv} KV "
                          "heads, split-K 2048")
 
@@ -318,7 +418,8 @@ def bench_full_prefill(hsw, wl, steps, stream, model=None):
                                    d["vpool"], rows, None, out, stream)
     call(0)
     torch.cuda.synchronize()
-    t = ev_time(call, max(2, steps // 10), stream)
+    n = max(3, steps // 10)
+    t = ev_time(call, n, stream)
 
     # the fused chain: K/V-only RoPE into the pool, then the prefill that
     # rotates q itself (no q_rot written or read)
@@ -335,7 +436,7 @@ def bench_full_prefill(hsw, wl, steps, stream, model=None):
                                       d["kpool"], d["vpool"], rows, d["seq_base"], None, None, stream)
     fused(0)
     torch.cuda.synchronize()
-    t_fused = ev_time(fused, max(2, steps // 10), stream)
+    t_fused = ev_time(fused, n, stream)
     t_rope = ev_time(rope, max(steps, 20), stream)
     t_rope_kv = ev_time(rope_kv, max(steps, 20), stream)
     pairs = T * 131072 + T * (T + 1) // 2
@@ -345,7 +446,7 @@ def bench_full_prefill(hsw, wl, steps, stream, model=None):
                      workload="K/V-only RoPE into the pool + hsw_full_prefill_chunk_qrope (q rotated in the "
                               "kernel) against RoPE + hsw_full_prefill_chunk, same workload")
     return dict(ms=t, flops=flops, tflops=flops / t / 1e9, frac_mfma_peak=flops / t / 1e9 / BF16_PEAK_TFLOPS,
-                tokens=T, fused=fused_res,
+                tokens=T, launches_per_run=n, fused=fused_res,
                 workload=f"full-attention prefill, 8192 tokens after 131072 prior rows, {hq} q / {hkv} KV heads")
 
 
@@ -465,22 +566,24 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
     hs = HybridStep(hsw, device=DEV, model=model)
     hs.step(stream)
     torch.cuda.synchronize()
-    n = max(1, steps)
-    t = ev_time(lambda i: hs.step(stream), n, stream)
-    # the same step with every attention call rotating q itself
+    # the step as the metric defines it: 5 runs of n >= 3 steps, median
+    n = max(3, steps)
+    runs = []
+    t = ev_time(lambda i: hs.step(stream), n, stream, runs)
+    # variants, 3 runs of one step each: every attention call rotating q
+    # itself; decode calls on a second stream beside the prefill calls
+    # (fused q-RoPE on, then off)
     hs.qrope = True
     hs.step(stream)
     torch.cuda.synchronize()
-    t_q = ev_time(lambda i: hs.step(stream), n, stream)
-    # decode calls on a second stream beside the prefill calls (fused q-RoPE
-    # still on), then the same with the plain calls
+    t_q = ev_time(lambda i: hs.step(stream), 1, stream, reps=3)
     hs.step(stream, overlap=True)
     torch.cuda.synchronize()
-    t_qo = ev_time(lambda i: hs.step(stream, overlap=True), n, stream)
+    t_qo = ev_time(lambda i: hs.step(stream, overlap=True), 1, stream, reps=3)
     hs.qrope = False
     hs.step(stream, overlap=True)
     torch.cuda.synchronize()
-    t_o = ev_time(lambda i: hs.step(stream, overlap=True), n, stream)
+    t_o = ev_time(lambda i: hs.step(stream, overlap=True), 1, stream, reps=3)
     timer = []
     hs.step(stream, timer)
     torch.cuda.synchronize()
@@ -489,7 +592,8 @@ def bench_hybrid(hsw, wl, steps, stream, model=None):
         kinds[kind] += e0.elapsed_time(e1)
     T, S = hs.T, hs.S
     nl, nf = len(hs.pattern), len(hs.pattern) - sum(hs.pattern)
-    res = dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps=n, per_call_ms={k: round(v, 3) for k, v in kinds.items()},
+    res = dict(ms=t, tokens_per_s=(T + S) / (t / 1e3), steps_per_run=n, runs_ms=runs,
+               per_call_ms={k: round(v, 3) for k, v in kinds.items()},
                qrope_ms=t_q, qrope_tokens_per_s=(T + S) / (t_q / 1e3),
                overlap_ms=t_o, overlap_tokens_per_s=(T + S) / (t_o / 1e3),
                qrope_overlap_ms=t_qo, qrope_overlap_tokens_per_s=(T + S) / (t_qo / 1e3),
@@ -552,7 +656,7 @@ def bench_pro(hsw, wl, args, stream):
     out["full_prefill_chunk_qrope"] = rounded(fp.pop("fused"))
     out["full_prefill_chunk"] = rounded(fp)
     torch.cuda.empty_cache()
-    hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m)
+    hy = bench_hybrid(hsw, wl, args.steps // 25, stream, m)
     print(f"[bench] pro hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "
           f"fused q-RoPE step {hy['qrope_ms']:.1f} ms; decode on a second stream {hy['overlap_ms']:.1f} ms "
           f"(fused {hy['qrope_overlap_ms']:.1f} ms)",
@@ -562,30 +666,101 @@ def bench_pro(hsw, wl, args, stream):
     return out
 
 
-def cpu_baseline(target_s=15.0, max_seqs=64):
-    """The fp64 oracle on a bounded sample of the windowed-prefill workload:
-    one whole 8192-token sequence (all 64 heads, window 128, sinks), run
-    repeatedly until about target_s seconds of oracle time (at most max_seqs
-    runs), scaled to algorithmic TFLOP/s (the headline unit).  Input
-    generation is untimed."""
+def cpu_oracle_protocol(seed=2024):
+    """The fp64 oracle on the host cores (attention only; input generation,
+    seeded and synthetic, is untimed): workloads 1-4 in full, and the hybrid
+    step on a sample (32 chunk rows of one full layer, 256 of one windowed
+    layer, 8 of the 128 decodes of each kind) extrapolated linearly by row
+    count to its 39 + 9 layers and labelled "extrapolated".  Reported as a
+    baseline only."""
     import oracle
     from hybrid_sliding_window_amd import workloads as wl
-    kw = dict(window=128, tau=1 / math.sqrt(192), lam=0.707)
-    pos = np.arange(8192)
-    pairs_per_seq = int(np.minimum(pos + 1, 128).sum())
-    b = wl.swa_prefill_batch(seed=2, n_seqs=1, seqlens=(8192,))
-    q, k, v = (b[x].double().numpy() for x in "qkv")
-    spent, n = 0.0, 0
-    while n < max_seqs and spent < target_s:
+    rng = np.random.default_rng(seed)
+    tau, lam = 1 / math.sqrt(192), 0.707
+    gen_s = [0.0]
+
+    def normal(*shape, out=None):
+        """N(0, 1) in fp64, drawn into `out` when given (large arrays are
+        allocated once and redrawn in place)."""
         t0 = time.perf_counter()
-        oracle.attn_linear(q, pos, k, v, 0, sinks=b["sinks"].double().numpy(), **kw)
-        spent += time.perf_counter() - t0
-        n += 1
-    flops = n * pairs_per_seq * 64 * 2 * (192 + 128)
-    return dict(value=flops / spent / 1e12, unit="TFLOP/s", cores=oracle.num_threads(), kind="oracle",
-                seconds=round(spent, 2),
-                sample=f"{n} run(s) of one windowed-prefill sequence of 8192 tokens (all 64 heads, window 128, "
-                       f"sinks) through the fp64 oracle; algorithmic in-window flops per second")
+        a = rng.standard_normal(None if out is not None else shape, dtype=np.float64, out=out)
+        gen_s[0] += time.perf_counter() - t0
+        return a
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def entry(sec, flops, what):
+        print(f"[bench] cpu oracle: {what}: {sec:.2f} s", file=sys.stderr, flush=True)
+        return dict(seconds=round(sec, 3), flops=flops, tflops=flops / sec / 1e12, workload=what)
+
+    res = {}
+    # 1: the fp32 windowed layer, RoPE + windowed attention
+    d = wl.logit_shift_layer()
+    P1 = d["pos"].numpy()
+    q1, k1, v1, s1 = (d[x].double().numpy() for x in ("q", "k", "v", "sinks"))
+    sec = timed(lambda: oracle.attn_linear(oracle.rope(q1, P1, 1e4), P1, oracle.rope(k1, P1, 1e4), v1, 0,
+                                           window=128, tau=tau, lam=lam, sinks=s1))
+    res["c1"] = entry(sec, swa_prefill_pairs([512], [0]) * 4 * 2 * 320, "1 x 512 tokens, 4 q / 1 KV head, window 128")
+    # 2: windowed prefill, 4 x 8192 tokens, 64 q / 8 KV heads
+    sinks = 1.0 + 0.25 * normal(64)
+    pos = np.arange(8192)
+    sec = 0.0
+    q, k, v = np.empty((8192, 64, 192)), np.empty((8192, 8, 192)), np.empty((8192, 8, 128))
+    for _ in range(4):
+        normal(out=q), normal(out=k), normal(out=v)
+        sec += timed(lambda: oracle.attn_linear(q, pos, k, v, 0, window=128, tau=tau, lam=lam, sinks=sinks))
+    del q, k, v
+    res["c2"] = entry(sec, 4 * swa_prefill_pairs([8192], [0]) * 64 * 2 * 320,
+                      "4 x 8192 tokens from position 0, 64 q / 8 KV heads, window 128, sinks")
+    # 3: windowed decode, 256 sequences over full 128-slot rings
+    P3 = rng.integers(128, 524289, size=256)
+    q, kr, vr = normal(256, 64, 192), normal(256, 8, 128, 192), normal(256, 8, 128, 128)
+    sec = timed(lambda: oracle.ring_decode(q, P3, kr, vr, tau=tau, lam=lam, sinks=sinks))
+    del kr, vr
+    res["c3"] = entry(sec, 256 * 64 * 128 * 2 * 320, "256 sequences at positions U{128..524288}, 64 q / 8 KV heads")
+    # one pool of 262144 rows (4 KV heads) serves the full-attention contexts:
+    # each sequence reads its own prefix of it (the work depends only on the
+    # lengths)
+    kp, vp = normal(262144, 4, 192), normal(262144, 4, 128)
+    # 4: full decode, 64 sequences, contexts U{32768..131072}
+    L4 = rng.integers(32768, 131073, size=64)
+    q = normal(64, 64, 192)
+    sec = sum(timed(lambda s=s: oracle.attn_linear(q[s:s + 1], np.array([L4[s] - 1]), kp[:L4[s]], vp[:L4[s]], 0,
+                                                   window=0, tau=tau, lam=lam)) for s in range(64))
+    res["c4"] = entry(sec, int(L4.sum()) * 64 * 2 * 320, "64 sequences, contexts U{32768..131072}, 64 q / 4 KV heads")
+    # 5: sampled, then extrapolated by row count
+    rows = np.sort(rng.choice(8192, 32, replace=False))
+    qf = normal(32, 64, 192)
+    t_fp = timed(lambda: oracle.attn_linear(qf, 131072 + rows, kp[:139264], vp[:139264], 0, window=0, tau=tau,
+                                            lam=lam))
+    qw, kw, vw = normal(256, 64, 192), normal(256 + 127, 8, 192), normal(256 + 127, 8, 128)
+    t_wp = timed(lambda: oracle.attn_linear(qw, 131072 + np.arange(256), kw, vw, 131072 - 127, window=128, tau=tau,
+                                            lam=lam, sinks=sinks))
+    L5 = rng.integers(4096, 262145, size=8)
+    qd = normal(8, 64, 192)
+    t_fd = sum(timed(lambda s=s: oracle.attn_linear(qd[s:s + 1], np.array([L5[s] - 1]), kp[:L5[s]], vp[:L5[s]], 0,
+                                                    window=0, tau=tau, lam=lam)) for s in range(8))
+    qr_, kr_, vr_ = normal(8, 64, 192), normal(8, 8, 128, 192), normal(8, 8, 128, 128)
+    t_wd = timed(lambda: oracle.ring_decode(qr_, rng.integers(4096, 262145, size=8), kr_, vr_, tau=tau, lam=lam,
+                                            sinks=sinks))
+    del kp, vp
+    print(f"[bench] cpu oracle: hybrid-step sample {t_fp + t_wp + t_fd + t_wd:.2f} s", file=sys.stderr, flush=True)
+    ext = t_fp * (8192 / 32) * 9 + t_wp * (8192 / 256) * 39 + t_fd * (128 / 8) * 9 + t_wd * (128 / 8) * 39
+    res["c5"] = dict(label="extrapolated", seconds=round(ext, 1),
+                     sampled_seconds=round(t_fp + t_wp + t_fd + t_wd, 3),
+                     sample="32 of the 8192 chunk rows of one full layer (131072 prior rows), 256 of one windowed "
+                            "layer, 8 of the 128 decode sequences of each kind; scaled by row count to 9 full + 39 "
+                            "windowed layers",
+                     workload="hybrid step, 48 layers: 8192-token chunk at 131072 + 128 decode sequences")
+    for v in res.values():
+        if "tflops" in v:
+            v["tflops"] = round(v["tflops"], 6)
+    return dict(configs=res, cores=oracle.num_threads(), host=host_cpu(), kind="oracle",
+                input_generation_seconds=round(gen_s[0], 1),
+                note="fp64 oracle, attention only (input generation untimed); a baseline, not a target")
 
 
 def main():
@@ -618,7 +793,7 @@ def main():
               "swa_decode": lambda: bench_swa_decode(hsw, wl, args.steps, stream, model=m),
               "full_decode": lambda: bench_full_decode(hsw, wl, args.steps, stream, m),
               "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream, m),
-              "hybrid": lambda: bench_hybrid(hsw, wl, max(1, args.steps // 25), stream, m),
+              "hybrid": lambda: bench_hybrid(hsw, wl, args.steps // 25, stream, m),
               "copy": lambda: bench_copy(args.steps, stream),
               "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m),
               "vit": lambda: bench_vit(hsw, wl, args.steps, stream,
@@ -631,6 +806,7 @@ def main():
         return
 
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
+    clocks = {"after_windowed_prefill": gpu_clocks_power()}
     print(f"[bench] swa_prefill {pre['ms']:.3f} ms {pre['tflops']:.1f} TFLOP/s {pre['gbs']:.0f} GB/s; fused q-RoPE "
           f"{pre['fused']['ms']:.3f} ms, chain {pre['fused']['chain_ms']:.3f} vs {pre['fused']['unfused_chain_ms']:.3f} ms",
           file=sys.stderr, flush=True)
@@ -640,7 +816,8 @@ def main():
           f"{dec['fused']['unfused_chain_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
     calls = {"rope_partial_kv_write": pre.pop("rope"), "swa_prefill_qrope": pre.pop("fused"),
-             "swa_decode_qrope": dec.pop("fused"), "swa_decode": dec}
+             "swa_decode_qrope": dec.pop("fused"), "swa_decode": dec,
+             "fp32_windowed_layer": bench_c1(hsw, wl, args.steps, stream)}
     if not args.quick:
         fd = bench_full_decode(hsw, wl, args.steps, stream)
         print(f"[bench] full_decode {fd['ms']:.3f} ms {fd['gbs']:.0f} GB/s; fused q-RoPE {fd['fused']['ms']:.3f} ms, "
@@ -668,14 +845,16 @@ def main():
               f"{vit['rope']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
         calls["vit"] = vit
         torch.cuda.empty_cache()
-        hy = bench_hybrid(hsw, wl, max(1, args.steps // 25), stream)
+        hy = bench_hybrid(hsw, wl, args.steps // 25, stream)
         print(f"[bench] hybrid step {hy['ms']:.1f} ms {hy['tokens_per_s']:.0f} tok/s {hy['per_call_ms']}; "
               f"fused q-RoPE step {hy['qrope_ms']:.1f} ms; decode on a second stream {hy['overlap_ms']:.1f} ms "
               f"(fused {hy['qrope_overlap_ms']:.1f} ms)",
               file=sys.stderr, flush=True)
         calls["hybrid_step"] = hy
+        clocks["after_hybrid_step"] = gpu_clocks_power()
         torch.cuda.empty_cache()
-    calls["swa_prefill"] = dict(ms=pre["ms"], tflops=pre["tflops"], gbs=pre["gbs"],
+    calls["swa_prefill"] = dict(ms=pre["ms"], runs_ms=pre["runs_ms"], launches_per_run=pre["launches_per_run"],
+                                tflops=pre["tflops"], gbs=pre["gbs"],
                                 frac_mfma_peak=pre["tflops"] / BF16_PEAK_TFLOPS,
                                 frac_hbm_peak=pre["gbs"] / HBM_PEAK_GBS, flops=pre["flops"], bytes=pre["bytes"],
                                 tokens=4 * 8192)
@@ -708,13 +887,24 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic("swa_prefill"),
                      "kernel": "hsw_swa_prefill call (band kernel + ring commit), 1.513 GB algorithmic per call"},
+        "timing": {"statistic": f"median of {RUNS} runs, each of N back-to-back launches between two HIP events",
+                   "runs_ms": [round(x, 5) for x in pre["runs_ms"]], "launches_per_run": pre["launches_per_run"]},
         "calls": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in calls.items()},
+        "gpu_clocks_power": clocks,
+        "host_cpu": host_cpu(),
     }
     if not args.quick and not args.no_pro:
         line["pro"] = bench_pro(hsw, wl, args, stream)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline()
+        prot = cpu_oracle_protocol()
+        c2 = prot["configs"]["c2"]
+        line["cpu_baseline"] = dict(value=c2["tflops"], unit="TFLOP/s", cores=prot["cores"], kind="oracle",
+                                    seconds=c2["seconds"],
+                                    sample="the windowed-prefill workload in full (4 x 8192 tokens, 64 q / 8 KV "
+                                           "heads, window 128, sinks) through the fp64 oracle; algorithmic "
+                                           "in-window flops per second")
+        line["cpu_oracle"] = prot
     print(json.dumps(line))
 
 
