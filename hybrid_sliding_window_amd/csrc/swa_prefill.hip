@@ -11,10 +11,12 @@
 // fp32 output); "System One mode and prompt reuse": keys before the chunk
 // start come from ring slot p mod 128.
 //
-// One workgroup (4 waves) per query block: 128 rows = 128/G positions x the G
-// query heads of one KV head (the heads are the 16-wide MFMA columns), two
-// column tiles per wave.  The block's band (positions max(0, p0-127) .. its
-// last position, <= 143 keys for G = 8) streams through LDS in 32-key chunks
+// 8 or 16 query heads per KV head take swa_sweep_kernel (end of file), which
+// sweeps consecutive query blocks with the window's keys held in LDS.  For
+// 1, 2 or 4 heads, one workgroup (4 waves) per query block: 128 rows = 128/G
+// positions x the G query heads of one KV head (the heads are the 16-wide
+// MFMA columns), two column tiles per wave.  The block's band (positions
+// max(0, p0-127) .. its last position) streams through LDS in 32-key chunks
 // with a three-stage pipeline: chunk c+2 is fetched by direct global->LDS
 // 16-byte loads (no VGPR staging) while chunk c is computed, one barrier per
 // chunk; each wave skips chunks outside its rows' windows.  Per chunk:
@@ -46,6 +48,8 @@
 // reaches before the first step's barrier.
 #include "hsw_device.h"
 #include "hsw_launch.h"
+
+#include <algorithm>
 
 namespace hsw {
 namespace {
@@ -549,6 +553,524 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
     }
 }
 
+// ---------------------------------------------------------------------
+// 8 or 16 query heads per KV head (both models' windowed layers): a
+// workgroup sweeps a segment of consecutive query blocks of one (sequence,
+// KV head) and keeps the keys of the moving window in two LDS rings of six
+// 32-key chunks (relative keys 32c .. 32c+31 in slot c mod 6), one for K and
+// one for V, so each key's K/V is loaded, and its V converted to fp16, once
+// per segment rather than once for every block whose window holds it.  A
+// block is 128 rows = 128/G positions x G heads, 32 rows per wave; the
+// windows of a wave's rows lie in the 5 chunks ending with the one holding
+// the block's last position, which the wave takes whole:
+//   S^T = K Q^T (v_mfma_f32_16x16x32_bf16), the exact row max over the 5
+//   chunks (so no online rescale), P = exp2 relative to it (P <= 1, fp16),
+//   its row sums by an MFMA with an all-ones operand, and O^T += V^T P^T
+//   (v_mfma_f32_16x16x32_f16 with V in fp16; a column block holding a finite
+//   V beyond the fp16 range stays bf16 and takes P split exactly into bf16
+//   hi + lo).
+// The waves are software-pipelined over blocks: block b+1's S^T (matrix
+// cores, K from LDS) runs in the same straight-line code as block b's
+// exponentials and P V (VALU and matrix cores), so neither unit waits for
+// the other.  Hence K runs two blocks ahead (a K chunk is loaded while the
+// block before the one that first needs it computes) and V one block ahead.
+// Keys outside a row's window are masked; a slot holding another chunk (or
+// none yet: the rings start zeroed) only ever meets a mask, so its finite
+// contents never count, and no slot a block reads is being loaded.  The
+// next block's q loads as soon as S^T has read each step of it; a block's
+// output is staged in LDS and stored at the start of the next block, so the
+// wait there never covers a store issued just before it.
+#define AI __attribute__((always_inline))  // lambdas called from two sites stay inline
+constexpr int kSweepGroups = 256;  // workgroups the sweep aims for (one per CU)
+constexpr int SW_SLOTS = 6;        // chunk slots of each ring: a band's 5 and the one loading
+constexpr int SW_WIN = 5;          // chunks a wave reads per block
+
+__device__ __forceinline__ float pin_f(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <int G, bool QROPE>
+__global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int nbw, int nseg) {
+    if (checks_failed(a.dev_flag)) return;  // (checked builds only)
+    constexpr int BQ = 128 / G;
+    // a block's band p0-127 .. p0+BQ-1 (p0 a multiple of BQ, which divides
+    // 16) lies in chunks (p0>>5)-4 .. p0>>5, and every row of a wave (4 or 2
+    // consecutive positions, aligned) in chunk p0>>5
+    static_assert(16 % BQ == 0 && W % 32 == 0 && W / 32 + 1 == SW_WIN && SW_WIN < SW_SLOTS, "band and ring");
+    __shared__ __attribute__((aligned(1024))) uint16_t kr[SW_SLOTS][KC * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t vr[SW_SLOTS][KC * DV];
+    // per wave: the output tile of the block before (32 rows x 128), and the
+    // cos/sin table of the fused q-RoPE once that tile has been stored
+    __shared__ __attribute__((aligned(1024))) uint16_t stg[4][32 * DV];
+    // per V slot and wave: 1 if the wave's column block of the chunk's V
+    // (dims 32w .. 32w+31) stayed bf16
+    __shared__ __attribute__((aligned(16))) int vbig[SW_SLOTS][4];
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int quad = lane >> 4, col = lane & 15;
+    const int bid = (int)__builtin_amdgcn_workgroup_id_x();
+    const int seg = bid % nseg;
+    const int g = (bid / nseg) % a.hkv;
+    const int s = bid / (nseg * a.hkv);
+
+    const int64_t tok0 = a.cu_seqlens[s];
+    const int len = (int)(a.cu_seqlens[s + 1] - tok0);
+    const int b_begin = seg * nbw, b_end = min((len + BQ - 1) / BQ, b_begin + nbw);
+    if (b_begin >= b_end) return;
+    // Relative positions (the chunk's first token is 0): key kp < 0 is
+    // absolute position start + kp, which exists iff kp >= kmin, and lives in
+    // ring slot (start + kp) mod W.
+    const int64_t start = a.start_pos[s];
+    const int kmin = start < W - 1 ? -(int)start : -(W - 1);
+    const int smod = (int)(start & (W - 1));
+    const int plast = len - 1;
+    auto band_lo = [&](int b) AI { return max(kmin, b * BQ - (W - 1)); };
+    auto band_hi = [&](int b) AI { return min(plast, b * BQ + BQ - 1); };
+    // the last chunk of block b's window (it holds the block's stored rows)
+    auto top_chunk = [&](int b) AI { return band_hi(b) >> 5; };
+
+    const double invf = QROPE ? pin_loaded(a.inv_freq[lane & 31]) : 0.0;
+    float sk2[2] = {0.0f, 0.0f};  // the rows' sink logits in log2 units
+    if (a.sinks) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) sk2[n] = pin_f(a.sinks[g * G + (32 * w + 16 * n + col) % G] * kLog2e);
+    }
+
+    const uint16_t *qg = (const uint16_t *)a.q;
+    // q step st of the wave's rows r = 32w + 16n + col (position r / G,
+    // head r % G) of block b; rows past the sequence read its last row
+    // (their outputs are not stored).  Ordinary loads: the first use follows
+    // the wait at the next block's start, where the compiler's wait costs
+    // nothing.
+    auto load_q_step = [&](int b, int st, u32x4 (&qv)[2][STEPS]) AI {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int r = 32 * w + 16 * n + col;
+            const int local = min(b * BQ + r / G, plast);
+            qv[n][st] = ld16(qg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DQK + 32 * st + 8 * quad);
+        }
+    };
+
+    const char *kst = (const char *)a.k_main + (tok0 * a.hkv + g) * (int64_t)(DQK * 2);
+    const char *vst = (const char *)a.v_main + (tok0 * a.hkv + g) * (int64_t)(DV * 2);
+    const char *kring = (const char *)a.k_ring + ((int64_t)(s * a.hkv + g) * W) * (DQK * 2);
+    const char *vring = (const char *)a.v_ring + ((int64_t)(s * a.hkv + g) * W) * (DV * 2);
+    const int64_t krow = (int64_t)a.hkv * DQK * 2, vrow = (int64_t)a.hkv * DV * 2;
+    // A chunk's LDS layout is the fragment order of swa_prefill_kernel: K
+    // 16-byte unit (h * 6 + st) * 64 + lane, V 8-byte unit (hh * 8 + dt) *
+    // 64 + lane; the i-th load of wave w fills 1 KB unit group 4i + w, so
+    // wave w's V pieces are the chunk's column block w (tiles 2w, 2w+1).
+    const int u = lane & 31;
+    const int vrow_l = 4 * (u >> 3) + ((u >> 1) & 3);
+    const int vbyte_l = 32 * (lane >> 5) + 16 * (u & 1);
+    auto slot_of = [&](int c) AI { return (c + 8 * SW_SLOTS) % SW_SLOTS; };  // c >= -48
+    // K or V of chunk c (relative keys 32c .. 32c+31, each clamped into
+    // kmin .. plast: finite data, masked where outside a window) into its slot
+    auto issue_k = [&](int c) AI {
+        const int k0 = 32 * c;
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) {
+            const int j = 4 * i + w, h = j / STEPS, st = j % STEPS;
+            const int kp = min(max(k0 + 16 * h + col, kmin), plast);
+            const char *src = kp >= 0 ? kst + (int64_t)kp * krow : kring + (int64_t)((smod + kp) & (W - 1)) * (DQK * 2);
+            load_lds16(src + 64 * st + 16 * quad, (const char *)kr[slot_of(c)] + j * 1024);
+        }
+    };
+    auto issue_v = [&](int c) AI {
+        const int k0 = 32 * c;
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) {
+            const int j = 4 * i + w, hh = j / 4;
+            const int kp = min(max(k0 + 16 * hh + vrow_l, kmin), plast);
+            const char *src = kp >= 0 ? vst + (int64_t)kp * vrow : vring + (int64_t)((smod + kp) & (W - 1)) * (DV * 2);
+            load_lds16(src + 64 * (j % 4) + vbyte_l, (const char *)vr[slot_of(c)] + j * 1024);
+        }
+    };
+    // The wave's column block of chunk c's V (landed) to fp16 in place, or,
+    // if it holds a finite value of magnitude 65536 or more (bf16 magnitude
+    // bits 0x4780 up to, not including, 0x7f80), left bf16 and flagged.  fp16
+    // holds every other bf16 value exactly from 2^-14 up, smaller magnitudes
+    // to its absolute step 2^-24.
+    auto settle_v = [&](int c) AI {
+        char *vsd = (char *)vr[slot_of(c)];
+        u32x4 raw[V_LOADS];
+        bool big = false;
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) {
+            raw[i] = *reinterpret_cast<const u32x4 *>(vsd + (4 * i + w) * 1024 + lane * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t word = raw[i][e];
+                const uint32_t lo = word & 0x7fffu, hi = (word >> 16) & 0x7fffu;
+                big |= (lo - 0x4780u < 0x3800u) || (hi - 0x4780u < 0x3800u);
+            }
+        }
+        const bool keep = __any(big);
+        if (!keep) {
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                u32x4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(raw[i][e]);
+                *reinterpret_cast<u32x4 *>(vsd + (4 * i + w) * 1024 + lane * 16) = h;
+            }
+        }
+        if (lane == 0) vbig[slot_of(c)][w] = keep ? 1 : 0;
+    };
+    auto barrier = [&]() AI {
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+
+    uint16_t *ep = &stg[w][0];
+    uint16_t *outg = (uint16_t *)a.out;
+    // Store the wave's rows of block b staged in ep (rows past the sequence
+    // not).  Tile row stride 256 B, 16-byte units xor-swizzled by row & 15.
+    auto store_out = [&](int b) AI {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4), c = lane & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * DV + ((c ^ (row & 15)) * 8));
+            const int r = 32 * w + row;
+            const int local = b * BQ + r / G;
+            if (local < len) st16(outg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DV + 8 * c, v);
+        }
+    };
+    // The fused q-RoPE of block b's q: cos/sin of the wave's NP positions in
+    // its staging tile (free: its tile was stored before, and a wave's LDS
+    // operations run in order), then rotate-half of dims 0 .. 63.
+    auto rope_q = [&](int b, u32x4 (&qv)[2][STEPS]) AI {
+        constexpr int NP = 32 / G;
+        float *tc = reinterpret_cast<float *>(ep);
+        float *ts = tc + NP * 32;
+        const int pw = b * BQ + (32 * w) / G;
+#pragma unroll
+        for (int e = lane; e < NP * 32; e += 64) {
+            float cv, sv;
+            rope_cos_sin(start + pw + e / 32, invf, cv, sv);
+            tc[e] = cv;
+            ts[e] = sv;
+        }
+        // lane (quad, col) holds dims 8 quad .. +7 (step 0) and their
+        // rotation partners 32 + 8 quad .. (step 1) of row 32w + 16n + col
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int pi = (16 * n + col) / G;
+            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad);
+            const f32x4 c1 = *reinterpret_cast<const f32x4 *>(tc + 32 * pi + 8 * quad + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(ts + 32 * pi + 8 * quad + 4);
+            const float cc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            const float ss[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            rope_rotate_bf16x8(qv[n][0], qv[n][1], cc, ss);
+        }
+    };
+
+    // the rings start zeroed: a slot not loaded yet holds finite values
+    {
+        constexpr int KU = SW_SLOTS * KC * DQK / 8, VU = SW_SLOTS * KC * DV / 8;
+        for (int i = tid; i < KU; i += kThreads) reinterpret_cast<u32x4 *>(&kr[0][0])[i] = u32x4{0, 0, 0, 0};
+        for (int i = tid; i < VU; i += kThreads) reinterpret_cast<u32x4 *>(&vr[0][0])[i] = u32x4{0, 0, 0, 0};
+        barrier();
+    }
+
+    const float scale2 = a.scale * kLog2e;
+    const u32x4 ones = u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+    int ck_next = band_lo(b_begin) >> 5;  // next K chunk to load
+    int cv_next = ck_next;                // next V chunk to load
+    int cv_conv = cv_next;                // next landed V chunk to settle
+    int slotkept = 0;                     // 4 bits per V slot: column blocks kept bf16
+    u32x4 qv[2][STEPS];
+
+    // S^T = K Q^T of block b (q in qv, landed): lane (quad, col) gets keys
+    // 4 quad .. +3 of each 16-key half of each window chunk against row
+    // 32w + 16n + col.  Step-major, so each step's q registers are free
+    // early: block b+1's q for that step loads right away (its rows clamped
+    // into the sequence, so past the segment it loads rows it does not use).
+    // Then the cut at kmin, which only blocks near the start of a sequence
+    // with fewer than W-1 earlier positions meet inside chunks 1 .. 3.
+    auto s_phase = [&](int b, f32x4 (&sacc)[SW_WIN][2][2]) AI {
+        const int ct = top_chunk(b);
+#pragma unroll
+        for (int i = 0; i < SW_WIN; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) sacc[i][h][n] = f32x4{0, 0, 0, 0};
+        // K operands one step ahead of the MFMAs that take them (a fence per
+        // step keeps that order, so each read has a step's MFMAs to land)
+        u32x4 kb[2][SW_WIN][2];
+        auto read_k = [&](int st, u32x4 (&dst)[SW_WIN][2]) AI {
+#pragma unroll
+            for (int i = 0; i < SW_WIN; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    dst[i][h] = *reinterpret_cast<const u32x4 *>(kr[slot_of(ct - (SW_WIN - 1) + i)] +
+                                                                 ((h * STEPS + st) * 64 + lane) * 8);
+        };
+        read_k(0, kb[0]);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            if (st + 1 < STEPS) read_k(st + 1, kb[(st + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < SW_WIN; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) sacc[i][h][n] = mfma_16x16x32_bf16(kb[st & 1][i][h], qv[n][st], sacc[i][h][n]);
+            load_q_step(b + 1, st, qv);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (32 * (ct - (SW_WIN - 2)) < kmin) {
+#pragma unroll
+            for (int i = 1; i < SW_WIN - 1; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kk = 32 * (ct - (SW_WIN - 1) + i) + 16 * h + 4 * quad;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (kk + j < kmin) sacc[i][h][n][j] = -INFINITY;
+                }
+        }
+    };
+    // Softmax numerators of block b from its S^T: every stored row's
+    // position lies in chunk ct (a wave's rows are 4 or 2 aligned positions
+    // of one block), so chunks 1 .. 3 of the window are inside each row's
+    // window (up to the cut at kmin, applied above) and only chunk 0 (keys
+    // below pos - 127, or below kmin) and chunk 4 (keys past pos) take a
+    // mask.  Then the exact row max m (in log2 units) and P = exp2(s scale2
+    // - m) <= 1 in fp16 (slots 0-3: keys 4 quad.. of the first 16-key half,
+    // 4-7 of the second, as V^T's slots).  In pieces, to interleave with
+    // other work: t = 0 .. 9 mask and max of chunk t % 5 for rows n = t / 5;
+    // t = 10, 11 the row max of n = t - 10; t = 12 .. 21 the numerators of
+    // chunk (t - 12) % 5 for n = (t - 12) / 5.
+    constexpr int SM_PIECES = 4 * SW_WIN + 2;
+    auto softmax_piece = [&](int t, int b, f32x4 (&sacc)[SW_WIN][2][2], u32x4 (&pf)[SW_WIN][2], float (&mx)[2],
+                             float (&mrow)[2]) AI {
+        if (t < 2 * SW_WIN) {
+            const int i = t % SW_WIN, n = t / SW_WIN;
+            const int pos = b * BQ + (32 * w + 16 * n + col) / G;
+            const int klo = max(pos - (W - 1), kmin);
+            const int ct = top_chunk(b);
+            if (i == 0) mx[n] = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kk = 32 * (ct - (SW_WIN - 1) + i) + 16 * h + 4 * quad;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (i == 0) sacc[i][h][n][j] = kk + j >= klo ? sacc[i][h][n][j] : -INFINITY;
+                    if (i == SW_WIN - 1) sacc[i][h][n][j] = kk + j <= pos ? sacc[i][h][n][j] : -INFINITY;
+                    mx[n] = fmaxf(mx[n], sacc[i][h][n][j]);
+                }
+            }
+        } else if (t < 2 * SW_WIN + 2) {
+            const int n = t - 2 * SW_WIN;
+            // (every row sees at least key min(pos, plast): finite)
+            mrow[n] = quad_max_swap(mx[n]) * scale2;
+        } else {
+            const int i = (t - 2 * SW_WIN - 2) % SW_WIN, n = (t - 2 * SW_WIN - 2) / SW_WIN;
+            float pv[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pv[4 * h + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i][h][n][j], scale2, -mrow[n]));
+            pf[i][n] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
+                             pack_f16x2(pv[6], pv[7])};
+        }
+    };
+    auto softmax = [&](int b, f32x4 (&sacc)[SW_WIN][2][2], u32x4 (&pf)[SW_WIN][2], float (&mrow)[2]) AI {
+        float mx[2];
+#pragma unroll
+        for (int t = 0; t < SM_PIECES; ++t) softmax_piece(t, b, sacc, pf, mx, mrow);
+    };
+
+    // Block b, whose P is in pcur: block b+1's S^T, then block b+1's softmax
+    // (VALU) alongside block b's P V (matrix cores), then block b's output.
+    auto block = [&](int b, u32x4 (&pcur)[SW_WIN][2], float (&mcur)[2], u32x4 (&pnext)[SW_WIN][2],
+                     float (&mnext)[2]) AI {
+        // every load and store of this wave done: q of b+1, the K chunk for
+        // block b+1's band, the V chunk for block b's, the stores of b-2
+        wait_vmcnt_q<0>(qv);
+        for (int c = cv_conv; c < cv_next; ++c) settle_v(c);
+        // every wave's chunks, conversions and flags in; every wave past block b-1
+        barrier();
+        for (int c = cv_conv; c < cv_next; ++c) {
+            const u32x4 f = *reinterpret_cast<const u32x4 *>(&vbig[slot_of(c)][0]);
+            const int bits = (f[0] ? 1 : 0) | (f[1] ? 2 : 0) | (f[2] ? 4 : 0) | (f[3] ? 8 : 0);
+            const int sh = 4 * slot_of(c);
+            slotkept = (slotkept & ~(15 << sh)) | (__builtin_amdgcn_readfirstlane(bits) << sh);
+        }
+        cv_conv = cv_next;
+        if (b > b_begin) store_out(b - 1);
+        // The slot a new chunk goes to last held the chunk 6 before it: for
+        // K, below block b+1's window (the one read now); for V, below block
+        // b's.
+        if (b + 2 < b_end && ck_next <= top_chunk(b + 2)) {
+            issue_k(ck_next);
+            ++ck_next;
+        }
+        if (b + 1 < b_end && cv_next <= top_chunk(b + 1)) {
+            issue_v(cv_next);
+            ++cv_next;
+        }
+        if constexpr (QROPE) rope_q(b + 1, qv);
+        f32x4 sacc[SW_WIN][2][2];
+        s_phase(b + 1, sacc);
+
+        // O^T = V^T P^T; the row sums of the fp16 P by an MFMA with an
+        // all-ones operand (every element of lacc[n]'s column is row col's sum)
+        const int ct = top_chunk(b);
+        f32x4 oacc[2][DT], lacc[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            lacc[n] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
+        }
+        int kept_any = 0;
+#pragma unroll
+        for (int i = 0; i < SW_WIN; ++i) kept_any |= (slotkept >> (4 * slot_of(ct - (SW_WIN - 1) + i))) & 15;
+        if (kept_any == 0) {
+            // 20 groups: each issues the V^T reads of the P V units two
+            // groups on (unit u: chunk u / 8, tile u % 8), takes two units'
+            // MFMAs and one piece of block b+1's softmax; a fence per group
+            // keeps the interleave
+            constexpr int UNITS = SW_WIN * DT, GROUPS = UNITS / 2;
+            static_assert(GROUPS + 2 == SM_PIECES, "one softmax piece per group, two after");
+            u32x4 vb[6];
+            auto read_v = [&](int u2) AI {
+                const uint16_t *vsc = vr[slot_of(ct - (SW_WIN - 1) + u2 / DT)];
+                const int dt = u2 % DT;
+                const u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+                const u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
+                vb[u2 % 6] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            };
+            float mx[2];
+#pragma unroll
+            for (int u2 = 0; u2 < 4; ++u2) read_v(u2);
+#pragma unroll
+            for (int gi = 0; gi < GROUPS; ++gi) {
+                if (2 * gi + 4 < UNITS) read_v(2 * gi + 4);
+                if (2 * gi + 5 < UNITS) read_v(2 * gi + 5);
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    const int u2 = 2 * gi + uu, i = u2 / DT, dt = u2 % DT;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(vb[u2 % 6], pcur[i][n], oacc[n][dt]);
+                }
+                if (gi % 4 == 0) {
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(ones, pcur[gi / 4][n], lacc[n]);
+                }
+                softmax_piece(gi, b + 1, sacc, pnext, mx, mnext);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            softmax_piece(GROUPS, b + 1, sacc, pnext, mx, mnext);
+            softmax_piece(GROUPS + 1, b + 1, sacc, pnext, mx, mnext);
+        } else {
+            softmax(b + 1, sacc, pnext, mnext);
+#pragma unroll
+            for (int i = 0; i < SW_WIN; ++i) {
+                const int sl = slot_of(ct - (SW_WIN - 1) + i);
+                const uint16_t *vsc = vr[sl];
+                const int kept = (slotkept >> (4 * sl)) & 15;
+#pragma unroll
+                for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(ones, pcur[i][n], lacc[n]);
+                // a kept column block's tiles take the fp16-rounded P split
+                // exactly into bf16 hi + lo (11 significant bits fit in two
+                // bf16) times its raw bf16 V
+                u32x4 ph[2], pl[2];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    float pr[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // (copied out first: a bit cast of a vector element in
+                        // place reads element 0 with this compiler)
+                        const uint32_t word = pcur[i][n][e];
+                        const f16x2 hp = __builtin_bit_cast(f16x2, word);
+                        pr[2 * e] = (float)hp[0];
+                        pr[2 * e + 1] = (float)hp[1];
+                    }
+                    u32x2 h0, l0, h1, l1;
+                    split_hi_lo(pr, h0, l0);
+                    split_hi_lo(pr + 4, h1, l1);
+                    ph[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+                    pl[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x2 a0 = ds_read_tr16(vsc + (dt * 64 + lane) * 4);
+                    const u32x2 a1 = ds_read_tr16(vsc + ((DT + dt) * 64 + lane) * 4);
+                    const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    if ((kept >> (dt / 2)) & 1) {
+#pragma unroll
+                        for (int n = 0; n < 2; ++n) {
+                            oacc[n][dt] = mfma_16x16x32_bf16(av, ph[n], oacc[n][dt]);
+                            oacc[n][dt] = mfma_16x16x32_bf16(av, pl[n], oacc[n][dt]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int n = 0; n < 2; ++n) oacc[n][dt] = mfma_16x16x32_f16(av, pcur[i][n], oacc[n][dt]);
+                    }
+                }
+            }
+        }
+        // Epilogue: the sink joins the denominator once; value scale; bf16
+        // into the staging tile, stored at the start of the next block.
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float ll = lacc[n][0], fac = 1.0f;
+            if (a.sinks) {
+                const float mf = fmaxf(mcur[n], sk2[n]);
+                fac = exp2f(mcur[n] - mf);
+                ll = ll * fac + exp2f(sk2[n] - mf);
+            }
+            const float rs = a.value_scale * fac / ll;
+            const int row = 16 * n + col;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o = oacc[n][dt];
+                const u32x2 pk = u32x2{pack_bf16x2(o[0] * rs, o[1] * rs), pack_bf16x2(o[2] * rs, o[3] * rs)};
+                const int unit = (2 * dt + (quad >> 1)) ^ (row & 15);
+                *reinterpret_cast<u32x2 *>(ep + row * DV + unit * 8 + 4 * (quad & 1)) = pk;
+            }
+        }
+    };
+
+    // Prologue: q of the first block; K of the first two blocks' bands (at
+    // most 6 chunks), V of the first's; the first block's S^T and softmax.
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) load_q_step(b_begin, st, qv);
+    for (; ck_next <= top_chunk(min(b_begin + 1, b_end - 1)); ++ck_next) issue_k(ck_next);
+    for (; cv_next <= top_chunk(b_begin); ++cv_next) issue_v(cv_next);
+    wait_vmcnt_q<0>(qv);
+    barrier();
+    if constexpr (QROPE) rope_q(b_begin, qv);
+    u32x4 pa[SW_WIN][2], pb[SW_WIN][2];
+    float ma[2], mb[2];
+    {
+        f32x4 sacc[SW_WIN][2][2];
+        s_phase(b_begin, sacc);
+        softmax(b_begin, sacc, pa, ma);
+    }
+#pragma unroll 1
+    for (int b = b_begin; b < b_end; b += 2) {
+        block(b, pa, ma, pb, mb);
+        if (b + 1 < b_end) block(b + 1, pb, mb, pa, ma);
+    }
+    wait_vmcnt_q<0>(qv);
+    store_out(b_end - 1);
+}
+
 }  // namespace
 
 bool swa_prefill_fast_ok(const AttnArgs &a, int dtype, int out_dtype) {
@@ -570,23 +1092,34 @@ hipError_t launch_swa_prefill(const AttnArgs &a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int BQ = 128 / G;
     const int64_t nqb = (a.max_seqlen + BQ - 1) / BQ;
+    if (G >= 8) {
+        // segments of nbw query blocks: about one workgroup per CU
+        const int64_t pairs = (int64_t)a.n_seqs * a.hkv;
+        const int64_t want = std::max<int64_t>(1, std::min<int64_t>(nqb, (kSweepGroups + pairs - 1) / pairs));
+        const int nbw = (int)((nqb + want - 1) / want);
+        const int nseg = (int)((nqb + nbw - 1) / nbw);
+        dim3 grid((unsigned)(pairs * nseg)), block(kThreads);
+        if (G == 8) {
+            if (a.qrope) hipLaunchKernelGGL((swa_sweep_kernel<8, true>), grid, block, 0, s, a, nbw, nseg);
+            else hipLaunchKernelGGL((swa_sweep_kernel<8, false>), grid, block, 0, s, a, nbw, nseg);
+        } else {
+            if (a.qrope) hipLaunchKernelGGL((swa_sweep_kernel<16, true>), grid, block, 0, s, a, nbw, nseg);
+            else hipLaunchKernelGGL((swa_sweep_kernel<16, false>), grid, block, 0, s, a, nbw, nseg);
+        }
+        return hipGetLastError();
+    }
+    // 1, 2 or 4 query heads per KV head: a workgroup per query block
     dim3 grid((unsigned)((int64_t)a.n_seqs * a.hkv * nqb)), block(kThreads);
     const int nq = (int)nqb;
     if (a.qrope) {
-        switch (G) {
-            case 2: hipLaunchKernelGGL((swa_prefill_kernel<2, true>), grid, block, 0, s, a, nq); break;
-            case 4: hipLaunchKernelGGL((swa_prefill_kernel<4, true>), grid, block, 0, s, a, nq); break;
-            case 8: hipLaunchKernelGGL((swa_prefill_kernel<8, true>), grid, block, 0, s, a, nq); break;
-            default: hipLaunchKernelGGL((swa_prefill_kernel<16, true>), grid, block, 0, s, a, nq); break;
-        }
+        if (G == 2) hipLaunchKernelGGL((swa_prefill_kernel<2, true>), grid, block, 0, s, a, nq);
+        else hipLaunchKernelGGL((swa_prefill_kernel<4, true>), grid, block, 0, s, a, nq);
         return hipGetLastError();
     }
     switch (G) {
         case 1: hipLaunchKernelGGL((swa_prefill_kernel<1, false>), grid, block, 0, s, a, nq); break;
         case 2: hipLaunchKernelGGL((swa_prefill_kernel<2, false>), grid, block, 0, s, a, nq); break;
-        case 4: hipLaunchKernelGGL((swa_prefill_kernel<4, false>), grid, block, 0, s, a, nq); break;
-        case 8: hipLaunchKernelGGL((swa_prefill_kernel<8, false>), grid, block, 0, s, a, nq); break;
-        default: hipLaunchKernelGGL((swa_prefill_kernel<16, false>), grid, block, 0, s, a, nq); break;
+        default: hipLaunchKernelGGL((swa_prefill_kernel<4, false>), grid, block, 0, s, a, nq); break;
     }
     return hipGetLastError();
 }
