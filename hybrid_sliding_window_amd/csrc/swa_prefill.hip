@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(AttnArgs a, in
 // the block's last position, which the wave takes whole:
 //   S^T = K Q^T (v_mfma_f32_16x16x32_bf16), the exact row max over the 5
 //   chunks (so no online rescale), P = exp2 relative to it (P <= 1, fp16),
-//   its row sums by an MFMA with an all-ones operand, and O^T += V^T P^T
+//   its row sums by an MFMA with a 1.0 operand per existing key, and O^T += V^T P^T
 //   (v_mfma_f32_16x16x32_f16 with V in fp16; a column block holding a finite
 //   V beyond the fp16 range stays bf16 and takes P split exactly into bf16
 //   hi + lo).
@@ -600,12 +600,16 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
     static_assert(16 % BQ == 0 && W % 32 == 0 && W / 32 + 1 == SW_WIN && SW_WIN < SW_SLOTS, "band and ring");
     __shared__ __attribute__((aligned(1024))) uint16_t kr[SW_SLOTS][KC * DQK];
     __shared__ __attribute__((aligned(1024))) uint16_t vr[SW_SLOTS][KC * DV];
-    // per wave: the output tile of the block before (32 rows x 128), and the
-    // cos/sin table of the fused q-RoPE once that tile has been stored
+    // per wave: the output tile of the block before (32 rows x 128)
     __shared__ __attribute__((aligned(1024))) uint16_t stg[4][32 * DV];
+    // per wave: the cos/sin table of the fused q-RoPE (32 / G positions)
+    __shared__ __attribute__((aligned(16))) float rtab[4][QROPE ? 2 * (32 / G) * 32 : 4];
     // per V slot and wave: 1 if the wave's column block of the chunk's V
     // (dims 32w .. 32w+31) stayed bf16
     __shared__ __attribute__((aligned(16))) int vbig[SW_SLOTS][4];
+    // per V slot: the fp16 A operand of the row-sum MFMA for each quad, 1.0
+    // for a key of the chunk that exists (>= kmin), 0 for one that does not
+    __shared__ __attribute__((aligned(16))) uint32_t vvalid[SW_SLOTS][4][4];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
@@ -701,6 +705,11 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
 #pragma unroll
         for (int i = 0; i < V_LOADS; ++i) {
             raw[i] = *reinterpret_cast<const u32x4 *>(vsd + (4 * i + w) * 1024 + lane * 16);
+            // (a key that does not exist: V row zero; the piece is one key's)
+            if (32 * c + 16 * i + vrow_l < kmin) {
+                raw[i] = u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4 *>(vsd + (4 * i + w) * 1024 + lane * 16) = raw[i];
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t word = raw[i][e];
@@ -719,6 +728,13 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
             }
         }
         if (lane == 0) vbig[slot_of(c)][w] = keep ? 1 : 0;
+        // slots 0-3 of quad q: keys 4q .. 4q+3 of the first 16-key half,
+        // slots 4-7 the same keys of the second half (P's slot order)
+        if (w == 0 && lane < 16) {
+            const int q = lane >> 2, e = lane & 3;
+            const int k0 = 32 * c + 4 * q + (e < 2 ? 2 * e : 16 + 2 * (e - 2));
+            vvalid[slot_of(c)][q][e] = (k0 >= kmin ? 0x3c00u : 0u) | (k0 + 1 >= kmin ? 0x3c000000u : 0u);
+        }
     };
     auto barrier = [&]() AI {
         __asm__ volatile("" ::: "memory");
@@ -728,25 +744,35 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
     };
 
     uint16_t *ep = &stg[w][0];
-    uint16_t *outg = (uint16_t *)a.out;
-    // Store the wave's rows of block b staged in ep (rows past the sequence
-    // not).  Tile row stride 256 B, 16-byte units xor-swizzled by row & 15.
+    uint16_t *obase = (uint16_t *)a.out + (tok0 * a.hq + g * G) * (int64_t)DV;
+    // Store the wave's rows of block b staged in ep, in 8 parts: in part i,
+    // lane (lane >> 4, c) stores 16 bytes c of tile row 4i + (lane >> 4), i.e.
+    // wave row r = 32w + 4i + (lane >> 4), at position (32w + 4i) / G of the
+    // block (the same for the part's 4 rows: G is 8 or 16), head (4i) % G +
+    // (lane >> 4); rows past the sequence not.  Tile row stride 256 B,
+    // 16-byte units xor-swizzled by row & 15.
+    // (all eight parts read first, so their LDS latency is paid once)
     auto store_out = [&](int b) AI {
+        u32x4 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 4 * i + (lane >> 4), c = lane & 15;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(ep + row * DV + ((c ^ (row & 15)) * 8));
-            const int r = 32 * w + row;
-            const int local = b * BQ + r / G;
-            if (local < len) st16(outg + ((tok0 + local) * a.hq + g * G + r % G) * (int64_t)DV + 8 * c, v);
+            v[i] = *reinterpret_cast<const u32x4 *>(ep + row * DV + ((c ^ (row & 15)) * 8));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rq = (32 * w + 4 * i) / G;
+            if (b * BQ + rq < len) {
+                uint16_t *ob = obase + (int64_t)(b * BQ + rq) * a.hq * DV;
+                st16(ob + (uint32_t)((((4 * i) % G) + (lane >> 4)) * DV + 8 * (lane & 15)), v[i]);
+            }
         }
     };
     // The fused q-RoPE of block b's q: cos/sin of the wave's NP positions in
-    // its staging tile (free: its tile was stored before, and a wave's LDS
-    // operations run in order), then rotate-half of dims 0 .. 63.
+    // its table, then rotate-half of dims 0 .. 63.
     auto rope_q = [&](int b, u32x4 (&qv)[2][STEPS]) AI {
         constexpr int NP = 32 / G;
-        float *tc = reinterpret_cast<float *>(ep);
+        float *tc = &rtab[w][0];
         float *ts = tc + NP * 32;
         const int pw = b * BQ + (32 * w) / G;
 #pragma unroll
@@ -776,11 +802,11 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
         constexpr int KU = SW_SLOTS * KC * DQK / 8, VU = SW_SLOTS * KC * DV / 8;
         for (int i = tid; i < KU; i += kThreads) reinterpret_cast<u32x4 *>(&kr[0][0])[i] = u32x4{0, 0, 0, 0};
         for (int i = tid; i < VU; i += kThreads) reinterpret_cast<u32x4 *>(&vr[0][0])[i] = u32x4{0, 0, 0, 0};
+        if (tid < SW_SLOTS * 4) reinterpret_cast<u32x4 *>(&vvalid[0][0][0])[tid] = u32x4{0, 0, 0, 0};
         barrier();
     }
 
     const float scale2 = a.scale * kLog2e;
-    const u32x4 ones = u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     int ck_next = band_lo(b_begin) >> 5;  // next K chunk to load
     int cv_next = ck_next;                // next V chunk to load
     int cv_conv = cv_next;                // next landed V chunk to settle
@@ -792,8 +818,6 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
     // 32w + 16n + col.  Step-major, so each step's q registers are free
     // early: block b+1's q for that step loads right away (its rows clamped
     // into the sequence, so past the segment it loads rows it does not use).
-    // Then the cut at kmin, which only blocks near the start of a sequence
-    // with fewer than W-1 earlier positions meet inside chunks 1 .. 3.
     auto s_phase = [&](int b, f32x4 (&sacc)[SW_WIN][2][2]) AI {
         const int ct = top_chunk(b);
 #pragma unroll
@@ -826,26 +850,16 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
             load_q_step(b + 1, st, qv);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (32 * (ct - (SW_WIN - 2)) < kmin) {
-#pragma unroll
-            for (int i = 1; i < SW_WIN - 1; ++i)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int kk = 32 * (ct - (SW_WIN - 1) + i) + 16 * h + 4 * quad;
-#pragma unroll
-                    for (int n = 0; n < 2; ++n)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            if (kk + j < kmin) sacc[i][h][n][j] = -INFINITY;
-                }
-        }
     };
     // Softmax numerators of block b from its S^T: every stored row's
     // position lies in chunk ct (a wave's rows are 4 or 2 aligned positions
     // of one block), so chunks 1 .. 3 of the window are inside each row's
-    // window (up to the cut at kmin, applied above) and only chunk 0 (keys
-    // below pos - 127, or below kmin) and chunk 4 (keys past pos) take a
-    // mask.  Then the exact row max m (in log2 units) and P = exp2(s scale2
+    // window and only chunk 0 (keys below pos - 127) and chunk 4 (keys past
+    // pos) take a mask.  A key below kmin does not exist; where it falls in
+    // chunks 1 .. 3 (a block near the start of a sequence with fewer than
+    // W-1 earlier positions) its K is key kmin's, which lies in every row's
+    // window, so it leaves the row max as it is; its V is zero and the row
+    // sums leave it out (vvalid), so it adds nothing.  Then the exact row max m (in log2 units) and P = exp2(s scale2
     // - m) <= 1 in fp16 (slots 0-3: keys 4 quad.. of the first 16-key half,
     // 4-7 of the second, as V^T's slots).  In pieces, to interleave with
     // other work: t = 0 .. 9 mask and max of chunk t % 5 for rows n = t / 5;
@@ -857,7 +871,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
         if (t < 2 * SW_WIN) {
             const int i = t % SW_WIN, n = t / SW_WIN;
             const int pos = b * BQ + (32 * w + 16 * n + col) / G;
-            const int klo = max(pos - (W - 1), kmin);
+            const int klo = pos - (W - 1);
             const int ct = top_chunk(b);
             if (i == 0) mx[n] = -INFINITY;
 #pragma unroll
@@ -925,8 +939,9 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
         f32x4 sacc[SW_WIN][2][2];
         s_phase(b + 1, sacc);
 
-        // O^T = V^T P^T; the row sums of the fp16 P by an MFMA with an
-        // all-ones operand (every element of lacc[n]'s column is row col's sum)
+        // O^T = V^T P^T; the row sums of the fp16 P by an MFMA whose A
+        // operand is 1.0 for each key that exists (every element of
+        // lacc[n]'s column is row col's sum)
         const int ct = top_chunk(b);
         f32x4 oacc[2][DT], lacc[2];
 #pragma unroll
@@ -935,6 +950,10 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[n][dt] = f32x4{0, 0, 0, 0};
         }
+        // the row-sum operand of window chunk i (all 1.0 where every key exists)
+        auto valid_op = [&](int i) AI {
+            return *reinterpret_cast<const u32x4 *>(&vvalid[slot_of(ct - (SW_WIN - 1) + i)][quad][0]);
+        };
         int kept_any = 0;
 #pragma unroll
         for (int i = 0; i < SW_WIN; ++i) kept_any |= (slotkept >> (4 * slot_of(ct - (SW_WIN - 1) + i))) & 15;
@@ -968,7 +987,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
                 }
                 if (gi % 4 == 0) {
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(ones, pcur[gi / 4][n], lacc[n]);
+                    for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(valid_op(gi / 4), pcur[gi / 4][n], lacc[n]);
                 }
                 softmax_piece(gi, b + 1, sacc, pnext, mx, mnext);
                 __builtin_amdgcn_sched_barrier(0);
@@ -983,7 +1002,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
                 const uint16_t *vsc = vr[sl];
                 const int kept = (slotkept >> (4 * sl)) & 15;
 #pragma unroll
-                for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(ones, pcur[i][n], lacc[n]);
+                for (int n = 0; n < 2; ++n) lacc[n] = mfma_16x16x32_f16(valid_op(i), pcur[i][n], lacc[n]);
                 // a kept column block's tiles take the fp16-rounded P split
                 // exactly into bf16 hi + lo (11 significant bits fit in two
                 // bf16) times its raw bf16 V
@@ -1031,10 +1050,10 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
             float ll = lacc[n][0], fac = 1.0f;
             if (a.sinks) {
                 const float mf = fmaxf(mcur[n], sk2[n]);
-                fac = exp2f(mcur[n] - mf);
-                ll = ll * fac + exp2f(sk2[n] - mf);
+                fac = __builtin_amdgcn_exp2f(mcur[n] - mf);
+                ll = ll * fac + __builtin_amdgcn_exp2f(sk2[n] - mf);
             }
-            const float rs = a.value_scale * fac / ll;
+            const float rs = a.value_scale * fac * __builtin_amdgcn_rcpf(ll);
             const int row = 16 * n + col;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
