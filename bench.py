@@ -56,8 +56,8 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_
 # profiles/vit_window_16x4096_hbm_traffic.md hold the runs.  Reported as null
 # once those sources differ from the ones measured.
 MEASURED_TRAFFIC = {
-    # band kernel 1510.3 MB + ring commit 2.7 MB read / 2.6 MB written
-    "swa_prefill": (1515.6e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "8baa3af85ddcd646"),
+    # sweep kernel 1014.0 MB read / 536.9 MB written + ring commit 2.7 / 2.6 MB
+    "swa_prefill": (1556.1e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "f92dff93c81c05b1"),
     "swa_decode": (178.45e6, ("swa_decode.hip", "hsw_device.h"), "83186c6fe6ff93f0"),
     # ViT window block: 201.8 MB read, 134.2 MB written
     "vit_window": (336.0e6, ("vit.hip", "hsw_device.h"), "3c7858915bd096a0"),
@@ -886,7 +886,7 @@ def main():
         "swa_prefill_frac_mfma_peak": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic("swa_prefill"),
-                     "kernel": "hsw_swa_prefill call (band kernel + ring commit), 1.513 GB algorithmic per call"},
+                     "kernel": "hsw_swa_prefill call (sweep kernel + ring commit), 1.513 GB algorithmic per call"},
         "timing": {"statistic": f"median of {RUNS} runs, each of N back-to-back launches between two HIP events",
                    "runs_ms": [round(x, 5) for x in pre["runs_ms"]], "launches_per_run": pre["launches_per_run"]},
         "calls": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
