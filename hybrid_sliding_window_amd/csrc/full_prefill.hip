@@ -595,9 +595,11 @@ __global__ __launch_bounds__(kThreads, 2) void full_prefill_kernel(AttnArgs a, i
 //   wait for chunk c+1's loads; note its V range.
 // K of chunk c is read in iteration c (three K stages), V of chunk c in
 // iteration c+1 (four V stages).  V goes to fp16 in place (fp16 P x fp16 V,
-// P <= 2^8 by the lazy rescale); a chunk holding a finite value of magnitude
-// 32768 or more is converted scaled by 2^-k (exact for the fp16 normal
-// range) and its PV product scaled back by 2^k in fp32.
+// P <= 2^8 by the lazy rescale).  A chunk holding a finite value of
+// magnitude 65536 or more (fp16 cannot hold it) sends the workgroup, before
+// it has written anything, to a second pass over its keys in which such a
+// chunk keeps bf16 V and takes P split exactly into bf16 hi + lo; the common
+// loop carries no code for that form.
 constexpr int PP_KC = 64;                               // keys per chunk
 constexpr int PP_THREADS = 512;
 constexpr int PP_WAVES = PP_THREADS / 64;
