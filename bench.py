@@ -334,10 +334,60 @@ def bench_swa_decode(hsw, wl, steps, stream, replicas=8, model=None):
                      chain_ms=t_rope_kv + t_fused, unfused_chain_ms=t_rope + t,
                      workload="K/V-only RoPE into the rings + hsw_swa_decode_qrope (q rotated in the "
                               "kernel, kept in fp32) against RoPE + hsw_swa_decode, same workload")
+    floor = bench_stream_floor(steps, stream, model, replicas)
     return dict(ms=t, bytes=bytes_, gbs=bytes_ / t / 1e6, frac_hbm_peak=bytes_ / t / 1e6 / HBM_PEAK_GBS,
                 flops=flops, tokens=S, launches=n, replicas=replicas, fused=fused_res,
+                stream_floor_ms=floor["ms"], stream_floor_gbs=floor["gbs"],
+                time_vs_stream_floor=floor["ms"] / t,
                 workload=f"windowed decode, 256 sequences at positions U{{128..524288}}, {heads(model)}, "
                          "128-slot ring")
+
+
+def measure_lib():
+    """libhsw_measure.so: measurement-only kernels (not the attention path)."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_window_amd",
+                        "libhsw_measure.so")
+    lib = ctypes.CDLL(path)
+    f = lib.hsw_measure_read_items
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    return lib
+
+
+def bench_stream_floor(steps, stream, model=None, replicas=8):
+    """A plain read (loads only, nothing computed) of the windowed decode's
+    input bytes in the decode's layout: per (sequence, KV head) item its 48 KiB
+    K ring, 32 KiB V ring and the 3 KiB (Flash; 6 KiB Pro) of its query heads,
+    256 sequences, 8 replicas as in the decode's timing.  What the memory
+    system delivers for these bytes to the simplest kernel: the decode
+    kernel's time is set beside it."""
+    from hybrid_sliding_window_amd import workloads as wl
+    model = model or wl.FLASH
+    hq, hkv = model.n_q_heads, model.swa_kv_heads
+    items = 256 * hkv
+    kb, vb, qb = 128 * 192 * 2, 128 * 128 * 2, (hq // hkv) * 192 * 2
+    lib = measure_lib()
+    reps = [tuple(torch.ones(items * n, dtype=torch.uint8, device=DEV) for n in (kb, vb, qb))
+            for _ in range(replicas)]
+    sink = torch.zeros(1024, dtype=torch.int32, device=DEV)
+    sp = stream.cuda_stream
+
+    def call(i):
+        k, v, q = reps[i % replicas]
+        rc = lib.hsw_measure_read_items(k.data_ptr(), v.data_ptr(), q.data_ptr(), items, kb, vb, qb,
+                                        sink.data_ptr(), sp)
+        if rc:
+            raise RuntimeError(f"hsw_measure_read_items failed ({rc})")
+    for i in range(2 * replicas):
+        call(i)
+    warm(call, stream)
+    t = ev_time(call, max(steps, 25) * replicas, stream)
+    nbytes = items * (kb + vb + qb)
+    return dict(ms=t, bytes=nbytes, gbs=nbytes / t / 1e6, frac_hbm_peak=nbytes / t / 1e6 / HBM_PEAK_GBS,
+                workload=f"plain read of the windowed decode's inputs ({items} items of K {kb} B, V {vb} B, "
+                         f"q {qb} B), one workgroup per item, loads only")
 
 
 def bench_full_decode(hsw, wl, steps, stream, model=None):
@@ -535,7 +585,6 @@ def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
     win_flops = win_pairs * hq * 64 * 4
     full_flops = full_pairs * hq * 64 * 4
     rope_bytes = T * (hq + hkv) * 64 * 2 * 2
-    del reps
     return dict(window=dict(ms=res["window"], bytes=win_bytes, gbs=win_bytes / res["window"] / 1e6,
                             traffic=measured_traffic("vit_window"),
                             frac_hbm_peak=win_bytes / res["window"] / 1e6 / HBM_PEAK_GBS,
@@ -771,7 +820,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="only the two metric calls")
     ap.add_argument("--only", choices=["swa_prefill", "swa_decode", "full_decode", "full_prefill", "hybrid", "copy",
-                                       "kvm_snapshot", "vit"],
+                                       "kvm_snapshot", "vit", "stream"],
                     help="run one call's timing only (for profiling) and print its numbers")
     ap.add_argument("--model", choices=["flash", "pro"], default="flash", help="shapes for --only")
     ap.add_argument("--vit-part", choices=["all", "window", "full", "rope"], default="all",
@@ -795,6 +844,7 @@ def main():
               "full_prefill": lambda: bench_full_prefill(hsw, wl, args.steps, stream, m),
               "hybrid": lambda: bench_hybrid(hsw, wl, args.steps // 25, stream, m),
               "copy": lambda: bench_copy(args.steps, stream),
+              "stream": lambda: bench_stream_floor(args.steps, stream, m),
               "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m),
               "vit": lambda: bench_vit(hsw, wl, args.steps, stream,
                                        ("window", "full", "rope") if args.vit_part == "all" else (args.vit_part,))}[
@@ -811,7 +861,8 @@ def main():
           f"{pre['fused']['ms']:.3f} ms, chain {pre['fused']['chain_ms']:.3f} vs {pre['fused']['unfused_chain_ms']:.3f} ms",
           file=sys.stderr, flush=True)
     dec = bench_swa_decode(hsw, wl, args.steps, stream)
-    print(f"[bench] swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s; fused q-RoPE "
+    print(f"[bench] swa_decode {dec['ms'] * 1e3:.1f} us {dec['gbs']:.0f} GB/s (a plain read of its inputs: "
+          f"{dec['stream_floor_ms'] * 1e3:.1f} us); fused q-RoPE "
           f"{dec['fused']['ms'] * 1e3:.1f} us, chain {dec['fused']['chain_ms'] * 1e3:.1f} vs "
           f"{dec['fused']['unfused_chain_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
@@ -881,6 +932,8 @@ def main():
                    "global_batch": 4, "seq_len": 8192, "parallelism": "single GPU"},
         "swa_decode": {"value": round(dec["gbs"], 1), "unit": "GB/s",
                        "frac_hbm_peak": round(dec["frac_hbm_peak"], 4), "us_per_call": round(dec["ms"] * 1e3, 2),
+                       "stream_floor_us": round(dec["stream_floor_ms"] * 1e3, 2),
+                       "time_vs_stream_floor": round(dec["time_vs_stream_floor"], 4),
                        "traffic": measured_traffic("swa_decode"),
                        "workload": dec["workload"]},
         "swa_prefill_frac_mfma_peak": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),

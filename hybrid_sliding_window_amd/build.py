@@ -1,7 +1,9 @@
 """Build libhsw.so (the C-ABI library of hand-written gfx950 HIP kernels) in
 place, next to this file, and libhsw_checked.so, the same sources built with
 HSW_CHECK_DEVICE=1 (device-resident arguments checked on the device before
-each call's kernels run).
+each call's kernels run).  libhsw_measure.so holds measurement-only kernels
+(measure/*.hip) that bench.py times beside the path's own; nothing of the
+path uses it.
 
     python -m hybrid_sliding_window_amd.build
 
@@ -25,6 +27,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libhsw.so")
 CHECKED_LIB = os.path.join(HERE, "libhsw_checked.so")
+MEASURE_LIB = os.path.join(HERE, "libhsw_measure.so")
+MEASURE_SRC = os.path.join(HERE, "measure")
 BUILD_DIR = os.path.join(HERE, "_build")
 CHECKED_BUILD_DIR = os.path.join(HERE, "_build_checked")
 
@@ -71,13 +75,16 @@ def _link(objs, lib):
 
 
 def build(verbose: bool = False, checked: bool = True) -> str:
-    """Compile and link libhsw.so, and (checked=True) libhsw_checked.so."""
+    """Compile and link libhsw.so, (checked=True) libhsw_checked.so, and
+    libhsw_measure.so."""
     builds = [(BUILD_DIR, LIB, False)] + ([(CHECKED_BUILD_DIR, CHECKED_LIB, True)] if checked else [])
     srcs = sources()
+    msrcs = sorted(glob.glob(os.path.join(MEASURE_SRC, "*.hip")))
     jobs = []
     for d, _, chk in builds:
         os.makedirs(d, exist_ok=True)
         jobs += [(src, d, chk) for src in srcs]
+    jobs += [(src, BUILD_DIR, False) for src in msrcs]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
     n = len(srcs)
@@ -85,6 +92,10 @@ def build(verbose: bool = False, checked: bool = True) -> str:
         _link(objs[i * n:(i + 1) * n], lib)
         if verbose:
             print("built", lib)
+    if msrcs:
+        _link(objs[len(builds) * n:], MEASURE_LIB)
+        if verbose:
+            print("built", MEASURE_LIB)
     return LIB
 
 
