@@ -103,12 +103,13 @@ template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
     if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     // V of the current and the next item, each wave's 32 slots in its own
-    // 8 KiB; after a wave's PV it holds that wave's O partial [G][PS] fp32.
+    // 8 KiB; after a wave's PV it holds that wave's O partial [G][DV] fp32,
+    // 16-byte unit u of head row h stored at unit u ^ (h & 15), so the 16
+    // lanes of a quad (16 heads, one unit) write 16 different bank groups.
     __shared__ __attribute__((aligned(1024))) uint16_t vb0[VBUF], vb1[VBUF];
     __shared__ float ml[2][4][16][2];  // (max, sum) per buffer, wave, head
     __shared__ float sk[MAX_HQ];       // sinks in log2 units
     __shared__ float qcs[QROPE ? 4 : 1][64];  // per wave: cos, sin of the item's 32 angles
-    constexpr int PS = G * (DV + 4) * 4 <= KEYS * DV * 2 ? DV + 4 : DV;  // partial row stride (floats)
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
         if (col < G) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4 *>(part + col * PS + 16 * dt + 4 * quad) = oacc[dt];
+                *reinterpret_cast<f32x4 *>(part + col * DV + 4 * ((4 * dt + quad) ^ col)) = oacc[dt];
             if (quad == 0) {
                 mlb[w][col][0] = mx;
                 mlb[w][col][1] = lsum;
@@ -278,7 +279,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_kernel(AttnArgs a) {
             for (int ww = 0; ww < 4; ++ww) {
                 const float f = __builtin_amdgcn_exp2f(mw[ww] - M);
                 L += f * mlb[ww][hd][1];
-                o += f * *reinterpret_cast<const f32x4 *>(pbase + ww * (KEYS * DV / 2) + hd * PS + d4);
+                o += f * *reinterpret_cast<const f32x4 *>(pbase + ww * (KEYS * DV / 2) + hd * DV +
+                                                          4 * ((d4 / 4) ^ (hd & 15)));
             }
             const float r = a.value_scale / L;
             const u32x2 pk = u32x2{pack_bf16x2(o[0] * r, o[1] * r), pack_bf16x2(o[2] * r, o[3] * r)};
