@@ -58,7 +58,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hybrid_sliding_
 MEASURED_TRAFFIC = {
     # sweep kernel 1014.0 MB read / 536.9 MB written + ring commit 2.7 / 2.6 MB
     "swa_prefill": (1556.1e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "f92dff93c81c05b1"),
-    "swa_decode": (178.45e6, ("swa_decode.hip", "hsw_device.h"), "83186c6fe6ff93f0"),
+    "swa_decode": (178.46e6, ("swa_decode.hip", "hsw_device.h"), "896eeabc5cd54b5f"),
     # ViT window block: 201.8 MB read, 134.2 MB written
     "vit_window": (336.0e6, ("vit.hip", "hsw_device.h"), "3c7858915bd096a0"),
 }
