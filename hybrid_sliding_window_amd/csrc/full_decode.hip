@@ -14,8 +14,10 @@
 // heads of the group are the 16 B columns of S^T = K Q^T
 // (v_mfma_f32_16x16x32_bf16, K rows loaded from HBM straight into the A
 // operand); an online softmax in log2 units; O^T += V^T P^T
-// (v_mfma_f32_16x16x16_bf16, P as bf16 hi + lo, V transposed through a
-// per-wave LDS tile).  The four waves merge in LDS and write one
+// (v_mfma_f32_16x16x32_bf16, P as bf16 hi + lo; V loaded in MFMA fragment
+// order, put in a per-wave LDS tile by 16-byte writes and read back
+// transposed by ds_read_b64_tr_b16, free of bank conflicts).  The four
+// waves merge in LDS and write one
 // (m, l, acc[128]) fp32 partial per (sequence, head, chunk).
 // Pass 2: one wave per (sequence, head) merges the chunks:
 //   M = max m_c,  Z = sum 2^(m_c - M) l_c (+ 2^(sink - M) once),
@@ -37,9 +39,16 @@ constexpr int DQK = 192, DV = 128;
 constexpr int STEPS = DQK / 32;
 constexpr int DT = DV / 16;
 constexpr int KS = 32;                 // keys per wave step
-constexpr int VT_STRIDE = KS + 4;      // bf16 per transposed V row
+constexpr int VSTEP = KS * DV;         // bf16 of one wave's V tile (8 KiB)
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
 
 struct StepRegs {
     u32x4 k[2][STEPS];
@@ -49,7 +58,7 @@ struct StepRegs {
 template <int G, bool QROPE>
 __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnArgs a) {
     if (checks_failed(a.dev_flag)) return;  // (checked builds only)
-    __shared__ __attribute__((aligned(16))) uint16_t vt[4 * DV * VT_STRIDE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vt[4 * VSTEP];
     __shared__ float red_m[4][16], red_l[4][16];
     __shared__ float qcs[QROPE ? 4 : 1][64];  // per wave: cos, sin of the 32 angles
 
@@ -121,6 +130,8 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
         }
     }
 
+    const int u = lane & 31;
+    const int vkey = 4 * (u >> 3) + ((u >> 1) & 3), vbyte = 32 * (lane >> 5) + 16 * (u & 1);
     auto load_step = [&](int i, StepRegs &r) {
         const int64_t k0 = w0 + (int64_t)i * KS;
 #pragma unroll
@@ -131,16 +142,20 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) r.k[kt][st] = ok ? ld16(src + 32 * st) : u32x4{0, 0, 0, 0};
         }
+        // V in the fragment order of the transposing reads: piece i of lane
+        // (u = lane & 31) is key 16 (i / 4) + 4 (u >> 3) + ((u >> 1) & 3) of
+        // the step, bytes 64 (i % 4) + 32 (lane >> 5) + 16 (u & 1) of its
+        // row, and goes to bytes 1024 i + 16 lane of the wave's tile.
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-            int cc = it * 64 + lane;
-            int64_t key = k0 + (cc >> 4);
-            r.v[it] = key < w1 ? ld16(Vp + ((base + key) * a.hkv + g) * (int64_t)DV + 8 * (cc & 15))
+            int64_t key = k0 + 16 * (it / 4) + vkey;
+            r.v[it] = key < w1 ? ld16((const char *)(Vp + ((base + key) * a.hkv + g) * (int64_t)DV) + 64 * (it % 4) +
+                                      vbyte)
                                : u32x4{0, 0, 0, 0};
         }
     };
 
-    uint16_t *vtw = vt + w * DV * VT_STRIDE;
+    uint16_t *vtw = vt + w * VSTEP;
     f32x4 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0, 0, 0, 0};
@@ -162,18 +177,11 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) sacc[kt] = mfma_16x16x32_bf16(cur.k[kt][st], ql[st], sacc[kt]);
         }
-        // V^T of this step into the wave's LDS tile (DS ops of one wave run
-        // in order, so the reads below see these writes and the writes of the
+        // V of this step into the wave's LDS tile (DS ops of one wave run in
+        // order, so the reads below see these writes and the writes of the
         // next step come after these reads).
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            int cc = it * 64 + lane, key = cc >> 4, dv0 = 8 * (cc & 15);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t word = cur.v[it][e >> 1];
-                vtw[(dv0 + e) * VT_STRIDE + key] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
-            }
-        }
+        for (int it = 0; it < 8; ++it) *reinterpret_cast<u32x4 *>(vtw + it * 512 + 8 * lane) = cur.v[it];
         __builtin_amdgcn_wave_barrier();
         float sv[8], mx = -INFINITY;
 #pragma unroll
@@ -200,16 +208,21 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
         m = mn;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= corr;
+        // O^T += V^T P^T over the step's 32 keys: operand slots 0-3 of a
+        // quad are keys 4quad.. of the first 16-key half, slots 4-7 of the
+        // second.
+        u32x2 h0, l0, h1, l1;
+        split_hi_lo(pv, h0, l0);
+        split_hi_lo(pv + 4, h1, l1);
+        const u32x4 bhi = u32x4{h0[0], h0[1], h1[0], h1[1]};
+        const u32x4 blo = u32x4{l0[0], l0[1], l1[0], l1[1]};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            u32x2 hi, lo;
-            split_hi_lo(pv + 4 * kt, hi, lo);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                u32x2 av = *reinterpret_cast<const u32x2 *>(vtw + (16 * dt + col) * VT_STRIDE + 16 * kt + 4 * quad);
-                oacc[dt] = mfma_16x16x16_bf16(av, hi, oacc[dt]);
-                oacc[dt] = mfma_16x16x16_bf16(av, lo, oacc[dt]);
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+            const u32x2 a0 = ds_read_tr16(vtw + (dt * 64 + lane) * 4);
+            const u32x2 a1 = ds_read_tr16(vtw + ((DT + dt) * 64 + lane) * 4);
+            const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            oacc[dt] = mfma_16x16x32_bf16(av, bhi, oacc[dt]);
+            oacc[dt] = mfma_16x16x32_bf16(av, blo, oacc[dt]);
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -220,10 +233,12 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
         red_l[w][col] = l;
     }
     __syncthreads();  // all waves done with their V tiles: reuse vt for partials
-    float *opart = reinterpret_cast<float *>(vt);  // [4][16][DV]
+    // [4][16][DV]; 16-byte unit u of head row h at unit u ^ h (the 16 lanes
+    // of a quad write 16 different bank groups)
+    float *opart = reinterpret_cast<float *>(vt);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4 *>(opart + (w * 16 + col) * DV + 16 * dt + 4 * quad) = oacc[dt];
+        *reinterpret_cast<f32x4 *>(opart + (w * 16 + col) * DV + 4 * ((4 * dt + quad) ^ col)) = oacc[dt];
     __syncthreads();
     float *ws_ml = (float *)a.ws;
     float *ws_acc = ws_ml + ((2 * (int64_t)a.n_seqs * a.hq * a.n_chunks + 3) & ~(int64_t)3);
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void full_decode_partial_kernel(AttnAr
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
             float f = exp2f(red_m[ww][h] - mu);
-            o += f * *reinterpret_cast<const f32x4 *>(opart + (ww * 16 + h) * DV + d4);
+            o += f * *reinterpret_cast<const f32x4 *>(opart + (ww * 16 + h) * DV + 4 * ((d4 / 4) ^ h));
             lc += f * red_l[ww][h];
         }
         int64_t slot = ((int64_t)s * a.hq + g * G + h) * a.n_chunks + c;
