@@ -177,15 +177,50 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     const uint16_t *vg = (const uint16_t *)a.v + g * D;
     const int64_t rs = (int64_t)a.hkv * D;   // elements per token row of k / v
 
-    // Thread tid moves pieces pi = tid + NT i: key pi / 8, 16-byte piece pi % 8.
+    // Load i of lane l in wave w moves 16-byte piece p of key `key` of the
+    // chunk, b = NW i + w.  Window blocks (HBM-bound): 8 keys x 8 pieces per
+    // load for K and V alike (key 8 b + l / 8, piece l % 8), whole 128-byte
+    // rows.  Full blocks (bound by issue, where LDS bank conflicts of the
+    // staging writes showed): for K, 16 keys x 4 pieces per load (key
+    // 16 (b >> 1) + l % 16, piece 4 (b & 1) + l / 16); for V, 8 keys x 8
+    // pieces (key 8 b + 4 ((l >> 3) & 1) + ((l >> 1) & 3), piece 2 (l >> 4) +
+    // (l & 1)), so the lanes of each 8- and 16-lane group write different LDS
+    // bank groups in put (a K unit's bank group is its key mod 16; a V unit's
+    // is 8 (key >> 2 & 1) + 2 (key & 3) + (piece & 1)).
+    auto k_piece = [&](int i, int &key, int &p) {
+        const int b = NW * i + w;
+        if constexpr (WIN) {
+            key = 8 * b + (lane >> 3);
+            p = lane & 7;
+        } else {
+            key = 16 * (b >> 1) + (lane & 15);
+            p = 4 * (b & 1) + (lane >> 4);
+        }
+    };
+    auto v_piece = [&](int i, int &key, int &p) {
+        const int b = NW * i + w;
+        if constexpr (WIN) {
+            key = 8 * b + (lane >> 3);
+            p = lane & 7;
+        } else {
+            key = 8 * b + 4 * ((lane >> 3) & 1) + ((lane >> 1) & 3);
+            p = 2 * (lane >> 4) + (lane & 1);
+        }
+    };
     u32x4 kr[LOADS], vr[LOADS];
     auto fetch = [&](int c) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int pi = tid + NT * i, key = pi >> 3, p = pi & 7;
+            int key, p;
+            k_piece(i, key, p);
             const int64_t r = row_of(min(klo + c * KCS + key, khi - 1));
             kr[i] = ld16(kg + r * rs + 8 * p);
-            vr[i] = ld16(vg + r * rs + 8 * p);
+            if constexpr (WIN) {
+                vr[i] = ld16(vg + r * rs + 8 * p);  // the same piece of V: one lookup of the order
+            } else {
+                v_piece(i, key, p);
+                vr[i] = ld16(vg + row_of(min(klo + c * KCS + key, khi - 1)) * rs + 8 * p);
+            }
         }
     };
     // any value of the thread's V pieces beyond fp16 (|v| >= 65536, the first
@@ -209,8 +244,10 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     auto put = [&](int stg, bool f16) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int pi = tid + NT * i, key = pi >> 3, p = pi & 7;
+            int key, p;
+            k_piece(i, key, p);
             *reinterpret_cast<u32x4 *>(&ks[stg][k_unit(key, p) * 8]) = kr[i];
+            v_piece(i, key, p);
             *reinterpret_cast<u32x4 *>(&vs[stg][v_unit(key, p) * 4]) = f16 ? to_f16(vr[i]) : vr[i];
         }
     };
