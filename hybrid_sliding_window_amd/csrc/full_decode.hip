@@ -276,19 +276,49 @@ __global__ __launch_bounds__(kThreads) void full_decode_combine_kernel(AttnArgs 
     const float *ws_ml = (const float *)a.ws;
     const float *ws_acc = ws_ml + ((2 * (int64_t)a.n_seqs * a.hq * a.n_chunks + 3) & ~(int64_t)3);
     const int64_t slot0 = wid * a.n_chunks;
+    // (m, l) of chunk c in lane c mod 64 of pass c / 64: the maximum and the
+    // factors come from one coalesced load per 64 chunks, then each chunk's
+    // accumulator loads are independent of one another (eight in flight).
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, ws_ml[2 * (slot0 + c)]);
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        if (c < nc) M = fmaxf(M, ws_ml[2 * (slot0 + c)]);
+    }
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
     M = fmaxf(M, sink2);
     const float mu = M == -INFINITY ? 0.0f : M;
     float z = a.sinks ? exp2f(sink2 - mu) : 0.0f;
     float o0 = 0.0f, o1 = 0.0f;
-    for (int c = 0; c < nc; ++c) {
-        float f = exp2f(ws_ml[2 * (slot0 + c)] - mu);
-        z += f * ws_ml[2 * (slot0 + c) + 1];
-        const float *acc = ws_acc + (slot0 + c) * DV + 2 * lane;
-        o0 += f * acc[0];
-        o1 += f * acc[1];
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        float f = 0.0f, lz = 0.0f;
+        if (c < nc) {
+            f = exp2f(ws_ml[2 * (slot0 + c)] - mu);
+            lz = f * ws_ml[2 * (slot0 + c) + 1];
+        }
+        for (int off = 32; off > 0; off >>= 1) lz += __shfl_xor(lz, off, 64);
+        z += lz;
+        const int n = min(64, nc - c0);
+        int j = 0;
+        for (; j + 8 <= n; j += 8) {
+            float2 v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = *reinterpret_cast<const float2 *>(ws_acc + (slot0 + c0 + j + e) * DV + 2 * lane);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float fe = __shfl(f, j + e, 64);
+                o0 += fe * v[e].x;
+                o1 += fe * v[e].y;
+            }
+        }
+        for (; j < n; ++j) {
+            const float2 v = *reinterpret_cast<const float2 *>(ws_acc + (slot0 + c0 + j) * DV + 2 * lane);
+            const float fe = __shfl(f, j, 64);
+            o0 += fe * v.x;
+            o1 += fe * v.y;
+        }
     }
     float r = z > 0.0f ? a.value_scale / z : 0.0f;
     uint16_t *out = (uint16_t *)a.out + wid * DV + 2 * lane;
