@@ -49,6 +49,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float quad_max_swap(float v) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -223,15 +224,18 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
             }
         }
     };
-    // any value of the thread's V pieces beyond fp16 (|v| >= 65536, the first
-    // bf16 value fp16 cannot hold, or not finite)
-    auto v_big = [&](const u32x4 &x) {
-        float m = 0.0f;
+    // Any value of V pieces beyond fp16: bf16 magnitude bits at or above
+    // 0x4780 (|v| >= 65536, the first bf16 value fp16 cannot hold; infinity
+    // and NaN above it), from a packed 16-bit maximum of the magnitude bits
+    // (two instructions per word).
+    auto mag_max = [&](u16x2 mx, const u32x4 &x) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            m = fmaxf(m, fmaxf(fabsf(__uint_as_float(x[e] << 16)), fabsf(__uint_as_float(x[e] & 0xffff0000u))));
-        return !(m < 65536.0f);
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, x[e] & 0x7fff7fffu));
+        return mx;
     };
+    auto beyond_f16 = [&](u16x2 mx) { return mx[0] >= 0x4780 || mx[1] >= 0x4780; };
+    auto v_big = [&](const u32x4 &x) { return beyond_f16(mag_max(u16x2{0, 0}, x)); };
     auto to_f16 = [&](u32x4 x) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
@@ -252,10 +256,10 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
         }
     };
     auto chunk_big = [&](bool extra) {
-        bool big = extra;
+        u16x2 mx = u16x2{0, 0};
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) big = big || v_big(vr[i]);
-        return big;
+        for (int i = 0; i < LOADS; ++i) mx = mag_max(mx, vr[i]);
+        return extra || beyond_f16(mx);
     };
 
     // First chunk (and, in a window after the first, the sink key: slot 64 =
@@ -283,6 +287,10 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     const float scale2 = a.scale * kLog2e;
     f32x4 oacc[2][DT];
     float m[2], l[2];
+    // full blocks: row sums of the same P the PV product takes, from an MFMA
+    // of P against an all-ones operand (every lane then holds its column's
+    // whole sum), instead of a VALU add per score
+    f32x4 lacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         m[n] = -INFINITY;
@@ -434,7 +442,7 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
                     const float f = (m[n] == -INFINITY) ? 0.0f : exp2f(m[n] - mn);
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) oacc[n][dt] *= f;
-                    l[n] *= f;
+                    lacc[n] *= f;
                 }
                 m[n] = mn;
             }
@@ -442,11 +450,9 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
 #pragma unroll
             for (int h = 0; h < NKT; ++h)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pv[n][h][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[n][h][j], scale2, mu));
-                    l[n] += pv[n][h][j];
-                }
+                for (int j = 0; j < 4; ++j) pv[n][h][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[n][h][j], scale2, mu));
         }
+        constexpr uint32_t kOnesF16 = 0x3c003c00u, kOnesBf16 = 0x3f803f80u;
 #pragma unroll
         for (int s2 = 0; s2 < NKT / 2; ++s2) {
             if (vf16) {
@@ -457,6 +463,9 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
                     pf[n] = u32x4{pack_f16x2(p0[0], p0[1]), pack_f16x2(p0[2], p0[3]), pack_f16x2(p1[0], p1[1]),
                                   pack_f16x2(p1[2], p1[3])};
                 }
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    lacc[n] = mfma_16x16x32_f16(u32x4{kOnesF16, kOnesF16, kOnesF16, kOnesF16}, pf[n], lacc[n]);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const u32x2 a0 = ds_read_tr16(vsc + ((2 * s2 * DT + dt) * 64 + lane) * 4);
@@ -474,6 +483,9 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
                     split_hi_lo(pv[n][2 * s2 + 1], h1, l1);
                     ph[n] = u32x4{h0[0], h0[1], h1[0], h1[1]};
                     pl[n] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+                    const u32x4 ones = u32x4{kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+                    lacc[n] = mfma_16x16x32_bf16(ones, ph[n], lacc[n]);
+                    lacc[n] = mfma_16x16x32_bf16(ones, pl[n], lacc[n]);
                 }
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
@@ -513,7 +525,7 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
         const int r = 32 * w + 16 * n + col;
         const int j = qb * BQ + r / G;
         const int head = r % G;
-        float ll = quad_sum_swap(l[n]);
+        float ll = WIN ? quad_sum_swap(l[n]) : lacc[n][0];
         float fac = 1.0f;
         if (a.sinks) {
             const float sk2 = a.sinks[g * G + head] * kLog2e;
