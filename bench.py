@@ -202,14 +202,15 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
     t_call = ev_time(call, n, stream, runs)
     t_rope = ev_time(rope, n, stream)
 
-    # the fused chain: K/V-only RoPE into staging, then the prefill that
-    # rotates q itself (no q_rot written or read)
+    # the fused chain: K-only RoPE into staging, then the prefill that
+    # rotates q itself (no q_rot written or read) and reads V in place (v's
+    # layout is the staging one, so no V copy is written or read)
     def rope_kv(i):
-        hsw.hsw_rope_partial_kv_write(sh, T, None, d["k"], d["v"], d["pos"], None, hsw.HSW_DST_STAGING,
-                                      kst, vst, T, None, None, None, stream)
+        hsw.hsw_rope_partial_kv_write(sh, T, None, d["k"], None, d["pos"], None, hsw.HSW_DST_STAGING,
+                                      kst, None, T, None, None, None, stream)
 
     def fused(i):
-        hsw.hsw_swa_prefill_qrope(sh, S, T1, d["cu_seqlens"], d["start_pos"], d["q"], kst, vst, d["kring"],
+        hsw.hsw_swa_prefill_qrope(sh, S, T1, d["cu_seqlens"], d["start_pos"], d["q"], kst, d["v"], d["kring"],
                                   d["vring"], d["sinks"], out, stream)
     fused(0)
     warm(fused, stream)
@@ -221,13 +222,13 @@ def bench_swa_prefill(hsw, wl, steps, warmup, stream, model=None):
     # ring commit (last 128 rows of K and V per sequence) written once
     bytes_ = T * hq * 192 * 2 + T * hkv * (192 + 128) * 2 + T * hq * 128 * 2 + S * hkv * 128 * (192 + 128) * 2
     rope_bytes = T * 2 * (hq * 192 + hkv * 192 + hkv * 128) * 2
-    rope_kv_bytes = T * 2 * (hkv * 192 + hkv * 128) * 2
+    rope_kv_bytes = T * 2 * hkv * 192 * 2
     fused_res = dict(ms=t_fused, gbs=bytes_ / t_fused / 1e6, tflops=flops / t_fused / 1e9,
                      rope_kv_ms=t_rope_kv, rope_kv_gbs=rope_kv_bytes / t_rope_kv / 1e6,
                      chain_ms=t_rope_kv + t_fused, unfused_chain_ms=t_rope + t_call,
                      chain_bytes=rope_kv_bytes + bytes_, unfused_chain_bytes=rope_bytes + bytes_,
-                     workload="K/V-only RoPE + hsw_swa_prefill_qrope (q rotated in the kernel) against "
-                              "RoPE + hsw_swa_prefill, same workload")
+                     workload="K-only RoPE into staging + hsw_swa_prefill_qrope (q rotated in the kernel, V "
+                              "read in place) against RoPE + hsw_swa_prefill, same workload")
     return dict(
         fused=fused_res,
         ms=t_call, runs_ms=runs, launches_per_run=n, flops=flops, bytes=bytes_, tokens=T,

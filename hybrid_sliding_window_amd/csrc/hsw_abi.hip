@@ -362,8 +362,14 @@ hsw_status hsw_rope_partial_kv_write(const hsw_attn_shape *sh, int64_t n_tokens,
     // themselves); one without the other is an error.
     if (!q != !q_rot) return fail(HSW_E_NULL, "%s is NULL (q and q_rot must both be given, or both NULL)",
                                   q ? "q_rot" : "q");
-    REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(pos);
-    REQUIRE_PTR(k_dst); REQUIRE_PTR(v_dst);
+    // v and v_dst both NULL (staging only): K alone is written; the windowed
+    // prefill then reads V from v itself, whose layout is the staging one.
+    if (dst_kind == HSW_DST_STAGING && !v && !v_dst) {
+    } else {
+        REQUIRE_PTR(v); REQUIRE_PTR(v_dst);
+    }
+    REQUIRE_PTR(k); REQUIRE_PTR(pos);
+    REQUIRE_PTR(k_dst);
     if (dst_kind != HSW_DST_STAGING) REQUIRE_PTR(seq);
     if (dst_kind == HSW_DST_POOL) REQUIRE_PTR(seq_base);
     REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(k_dst, 16);

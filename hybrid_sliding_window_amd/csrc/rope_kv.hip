@@ -98,8 +98,9 @@ __global__ __launch_bounds__(kThreads) void rope_kv_kernel(RopeArgs a) {
     const int pass = (a.dqk - a.rope_dim) / 8;       // pass-through items per q/k head
     const int per_qk = units + pass;
     const int per_v = a.dv / 8;
-    // q == NULL: K/V only (the attention call rotates q itself)
-    const int n_q = a.q ? a.hq * per_qk : 0, n_k = a.hkv * per_qk, n_v = a.hkv * per_v;
+    // q == NULL: K/V only (the attention call rotates q itself); v == NULL
+    // (staging only): K only (the windowed prefill reads V where it is)
+    const int n_q = a.q ? a.hq * per_qk : 0, n_k = a.hkv * per_qk, n_v = a.v ? a.hkv * per_v : 0;
     const int64_t row = dst_row;
     // K/V row stride between heads: ring rows interleave (head, slot).
     const int64_t head_stride = (a.dst_kind == 0) ? (int64_t)a.window : 1;

@@ -18,7 +18,8 @@ batch of decode sequences on every layer:
 
 With qrope=True the RoPE calls rotate and write K/V only and each attention
 call is its *_qrope form, which rotates the raw q itself (no q_rot round trip
-through HBM).
+through HBM); on windowed layers the chunk's RoPE call writes K alone and the
+prefill reads the chunk's V where it is (its layout is the staging one).
 
 step(overlap=True) issues each layer's decode calls on a second stream: the
 decode chain (RoPE + decode of the decode tokens, layer after layer) and the
@@ -142,11 +143,12 @@ class HybridStep:
         if self.pattern[li] == 1:
             swa = self.swa
             return [
-                ("rope", lambda: h.hsw_rope_partial_kv_write(swa, T, None, d["kc"], d["vc"], self.d_pos_c, None,
-                                                             h.HSW_DST_STAGING, self.kst, self.vst, T, None, None,
+                # K only into staging: the prefill reads the chunk's V in place
+                ("rope", lambda: h.hsw_rope_partial_kv_write(swa, T, None, d["kc"], None, self.d_pos_c, None,
+                                                             h.HSW_DST_STAGING, self.kst, None, T, None, None,
                                                              None, stream)),
                 ("swa_prefill", lambda: h.hsw_swa_prefill_qrope(swa, 1, T, self.d_cu, self.d_start, d["qc"],
-                                                                self.kst, self.vst, d["kring"][S:], d["vring"][S:],
+                                                                self.kst, d["vc"], d["kring"][S:], d["vring"][S:],
                                                                 self.sinks, self.out, stream)),
                 ("rope", lambda: h.hsw_rope_partial_kv_write(swa, S, None, d["kd"], d["vd"], self.d_pos_dec,
                                                              self.d_seq_dec, h.HSW_DST_RING, d["kring"], d["vring"],

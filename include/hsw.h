@@ -183,6 +183,10 @@ hsw_status hsw_device_check_status(hsw_stream_t stream, int32_t *code, int64_t *
  *   q_rot [n_tokens][Hq][d_qk] in dtype (written).  q and q_rot may both be
  *      NULL: then only K/V are rotated and written (for the *_qrope calls,
  *      which rotate q themselves); one of them NULL alone is HSW_E_NULL.
+ *   v and v_dst may both be NULL for HSW_DST_STAGING: then only K is
+ *      written (V staging has v's own layout [n_tokens][Hkv][d_v], so the
+ *      windowed prefill can take v itself as its V staging); one of them
+ *      NULL alone, or either NULL for RING / POOL, is HSW_E_NULL.
  *   dst_index_out [n_tokens] int64 or NULL: the slot / row written for each
  *      token, or -1 when its destination was outside dst_capacity.
  */

@@ -88,6 +88,20 @@ def test_rope_argument_errors():
     hsw.hsw_rope_partial_kv_write(sh, **{**args, "n_tokens": 0})
 
 
+def test_rope_k_only_staging_contract():
+    """v and v_dst both NULL is the K-only staging write; anything else
+    without V is refused before a launch."""
+    sh = swa()
+    args = dict(n_tokens=4, q=None, k=FAKE, v=None, pos=FAKE, seq=None, dst_kind=hsw.HSW_DST_STAGING,
+                k_dst=FAKE, v_dst=None, dst_capacity=4, seq_base=None, q_rot=None)
+    hsw.hsw_rope_partial_kv_write(sh, **{**args, "n_tokens": 0})  # accepted (empty: no launch)
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "v_dst": FAKE})  # v missing alone
+    expect(1, hsw.hsw_rope_partial_kv_write, sh, **{**args, "v": FAKE})      # v_dst missing alone
+    for kind in (hsw.HSW_DST_RING, hsw.HSW_DST_POOL):                       # caches always take V
+        expect(1, hsw.hsw_rope_partial_kv_write, sh,
+               **{**args, "dst_kind": kind, "seq": FAKE, "seq_base": FAKE})
+
+
 def test_attention_argument_errors():
     sh, fs = swa(), full()
     expect(2, hsw.hsw_swa_prefill, fs, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)

@@ -155,7 +155,8 @@ def test_hybrid_full_layer_sampled(hs):
 
 def test_hybrid_fused_qrope_calls(hs):
     """The same two layers through the driver's fused q-RoPE calls (K/V-only
-    RoPE, then the *_qrope attention calls on the raw q): both prefills
+    RoPE -- K alone for the windowed chunk, whose V the prefill reads in
+    place -- then the *_qrope attention calls on the raw q): both prefills
     byte-identical to the unfused calls on the same state and their sampled
     rows held to the oracle fed the bytes the unfused calls consumed, both
     decodes against the oracle fed the raw q rotated in fp64."""
@@ -182,10 +183,10 @@ def test_hybrid_fused_qrope_calls(hs):
     assert torch.equal(hs.out, out_u), "fused windowed prefill differs from the unfused call"
     del out_u, kst_u
     # gate: sampled fused rows against the oracle fed the unfused call's
-    # q_rot (the K/V-only RoPE leaves it in place), staging rows and the ring
-    # as it was before the commit
+    # q_rot (the K/V-only RoPE leaves it in place), staging K, the chunk's own
+    # V (what the fused prefill read) and the ring as it was before the commit
     rows = chunk_rows(T, seed=11)
-    k, v, kpos0 = linear_kv_from_ring(f64(kr0), f64(vr0), P0, f64(hs.kst), f64(hs.vst))
+    k, v, kpos0 = linear_kv_from_ring(f64(kr0), f64(vr0), P0, f64(hs.kst), f64(d0["vc"]))
     ref = oracle.attn_linear(f64(hs.q_rot[rows]), np.arange(P0, P0 + T)[rows], k, v, kpos0, window=128,
                              sinks=f64(hs.sinks), **shape_kw(hs.swa))
     ma, mr = assert_close(f64(hs.out[rows]), ref, what="hybrid swa_prefill_qrope")

@@ -768,16 +768,19 @@ def test_rope_cos_sin_fp32_against_fp64():
         print(f"rope cos/sin theta={theta:.0e}: max |err| {err.max():.2e}, mean {err.mean():.2e}")
 
 
-def run_swa_prefill_qrope(batch):
-    """K/V-only RoPE into staging, then the prefill that rotates q itself."""
+def run_swa_prefill_qrope(batch, v_in_place=False):
+    """K/V-only RoPE into staging, then the prefill that rotates q itself.
+    v_in_place: the RoPE call writes K only and the prefill takes v itself as
+    its V staging."""
     shape = batch["shape"]
     T = batch["q"].shape[0]
     S = batch["start_pos"].shape[0]
     lens = (batch["cu_seqlens"][1:] - batch["cu_seqlens"][:-1])
     kst = torch.empty_like(dev(batch["k"]))
-    vst = torch.empty_like(dev(batch["v"]))
-    hsw.hsw_rope_partial_kv_write(shape, T, None, dev(batch["k"]), dev(batch["v"]), dev(batch["pos"]), None,
-                                  STAGING, kst, vst, T, None, None)
+    v = dev(batch["v"])
+    vst = v if v_in_place else torch.empty_like(v)
+    hsw.hsw_rope_partial_kv_write(shape, T, None, dev(batch["k"]), None if v_in_place else v, dev(batch["pos"]),
+                                  None, STAGING, kst, None if v_in_place else vst, T, None, None)
     kring, vring = dev(batch["kring"]), dev(batch["vring"])
     out = torch.full((T, shape.n_q_heads, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
     hsw.hsw_swa_prefill_qrope(shape, S, int(lens.max()) + 3, dev(batch["cu_seqlens"]), dev(batch["start_pos"]),
@@ -823,6 +826,14 @@ def test_swa_prefill_qrope_bitwise_equals_rope_then_prefill(model):
     ma, mr = errors(f64(out2), np.concatenate(refs))
     print(f"swa_prefill_qrope {model}: bitwise equal to RoPE + prefill; bf16-in max_abs={gma:.2e} "
           f"mean_rel={gmr:.2e}; chain max_abs={ma:.2e} mean_rel={mr:.2e}")
+    # V read in place: the RoPE call writes K only and the prefill takes v
+    # itself as its V staging (the same layout): same output and ring bytes,
+    # and held to the oracle on its own
+    kst3, _, kring3, vring3, out3 = run_swa_prefill_qrope(batch, v_in_place=True)
+    assert torch.equal(kst3.cpu(), kst.cpu())
+    assert torch.equal(kring3.cpu(), kring.cpu()) and torch.equal(vring3.cpu(), vring.cpu())
+    assert torch.equal(out3.cpu(), out.cpu()), "prefill with V read in place differs"
+    assert_close(f64(out3), ref, what=f"swa_prefill_qrope V in place {model}")
 
 
 @pytest.mark.parametrize("model", ["flash", "pro"])
