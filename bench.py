@@ -531,7 +531,7 @@ def bench_kvm_snapshot(hsw, wl, steps, stream, model=None):
                          f"(192 + 128) bf16 ({sb / 1e6:.1f} MB each way)")
 
 
-def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
+def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope", "window_rope")):
     """Vision-encoder attention on 16 pictures of 64 x 64 patches (65536
     tokens, 16 q / 4 KV heads of width 64): a window block (column order of
     the merge units, the sink key), a full block, and the 2D RoPE of q and k.
@@ -565,9 +565,14 @@ def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
     def rope_call(i):
         b = reps[i % 2]
         hsw.hsw_vit_rope_2d(win, T, b["q"], b["k"], d_row, d_col, b["qr"], b["kr"], stream)
-    res = {"window": float("nan"), "full": float("nan"), "rope": float("nan")}
+
+    def window_rope_call(i):   # the 2D RoPE fused into the window block (unrotated q, k)
+        b = reps[i % 2]
+        hsw.hsw_vit_window_attention_rope(win, S, maxlen, b["cu"], d_order, 1, d_row, d_col, b["q"], b["k"],
+                                          b["v"], None, b["out"], stream)
+    res = {"window": float("nan"), "full": float("nan"), "rope": float("nan"), "window_rope": float("nan")}
     for name, fn, n in (("window", window_call, max(steps, 20) * 2), ("full", full_call, max(steps // 5, 4)),
-                        ("rope", rope_call, max(steps, 20) * 2)):
+                        ("rope", rope_call, max(steps, 20) * 2), ("window_rope", window_rope_call, max(steps, 20) * 2)):
         if name not in parts:
             continue
         fn(0)
@@ -597,6 +602,11 @@ def bench_vit(hsw, wl, steps, stream, parts=("window", "full", "rope")):
                           workload="full block: every picture attends to itself"),
                 rope=dict(ms=res["rope"], bytes=rope_bytes, gbs=rope_bytes / res["rope"] / 1e6, tokens=T,
                           workload="2D RoPE of q and k"),
+                window_rope=dict(ms=res["window_rope"], bytes=win_bytes, gbs=win_bytes / res["window_rope"] / 1e6,
+                                 frac_hbm_peak=win_bytes / res["window_rope"] / 1e6 / HBM_PEAK_GBS, tokens=T,
+                                 chain_ms=res["window_rope"], unfused_chain_ms=res["rope"] + res["window"],
+                                 workload="window block with the 2D RoPE fused (hsw_vit_window_attention_rope, "
+                                          "unrotated q and k) against 2D RoPE + window block"),
                 workload=f"vision encoder, {S} pictures of 64 x 64 patches ({T} tokens), {hq} q / {hkv} KV "
                          "heads of width 64")
 
@@ -824,7 +834,7 @@ def main():
                                        "kvm_snapshot", "vit", "stream"],
                     help="run one call's timing only (for profiling) and print its numbers")
     ap.add_argument("--model", choices=["flash", "pro"], default="flash", help="shapes for --only")
-    ap.add_argument("--vit-part", choices=["all", "window", "full", "rope"], default="all",
+    ap.add_argument("--vit-part", choices=["all", "window", "full", "rope", "window_rope"], default="all",
                     help="with --only vit: time one of the vision-encoder calls only (for profiling)")
     ap.add_argument("--no-pro", action="store_true", help="skip the MiMo-V2.6-Pro section")
     args = ap.parse_args()
@@ -848,12 +858,13 @@ def main():
               "stream": lambda: bench_stream_floor(args.steps, stream, m),
               "kvm_snapshot": lambda: bench_kvm_snapshot(hsw, wl, args.steps, stream, m),
               "vit": lambda: bench_vit(hsw, wl, args.steps, stream,
-                                       ("window", "full", "rope") if args.vit_part == "all" else (args.vit_part,))}[
+                                       ("window", "full", "rope", "window_rope") if args.vit_part == "all"
+                                       else (args.vit_part,))}[
             args.only]
         r = fn()
         print(json.dumps({"only": args.only, "model": m.name,
                           **{k: v for k, v in r.items() if not isinstance(v, dict) or k in ("fused", "window", "full",
-                                                                                            "rope")}}))
+                                                                                            "rope", "window_rope")}}))
         return
 
     pre = bench_swa_prefill(hsw, wl, args.steps, args.warmup, stream)
@@ -894,7 +905,8 @@ def main():
         vit = bench_vit(hsw, wl, args.steps, stream)
         print(f"[bench] vit window {vit['window']['ms'] * 1e3:.1f} us {vit['window']['gbs']:.0f} GB/s; full "
               f"{vit['full']['ms']:.3f} ms {vit['full']['tflops']:.1f} TFLOP/s; rope {vit['rope']['ms'] * 1e3:.1f} us "
-              f"{vit['rope']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+              f"{vit['rope']['gbs']:.0f} GB/s; window with the RoPE fused {vit['window_rope']['ms'] * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
         calls["vit"] = vit
         torch.cuda.empty_cache()
         hy = bench_hybrid(hsw, wl, args.steps // 25, stream)

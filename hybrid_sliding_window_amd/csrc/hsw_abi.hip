@@ -649,4 +649,41 @@ hsw_status hsw_vit_attention(const hsw_attn_shape *sh, int32_t n_images, int64_t
     return launched(hsw::launch_vit_attn(a, max_len, (hipStream_t)stream), "vit_attention");
 }
 
+hsw_status hsw_vit_window_attention_rope(const hsw_attn_shape *sh, int32_t n_images, int64_t max_len,
+                                         const int64_t *cu_seqlens, const int32_t *order, int32_t sink_key,
+                                         const int32_t *row, const int32_t *col, const void *q, const void *k,
+                                         const void *v, const float *sinks, void *out, hsw_stream_t stream) {
+    hsw_status st = check_shape(sh, -1);
+    if (st) return st;
+    hsw::VitArgs a;
+    memset(&a, 0, sizeof a);
+    a.hq = sh->n_q_heads; a.hkv = sh->n_kv_heads; a.window = sh->window; a.sink_key = sink_key ? 1 : 0;
+    a.scale = sh->softmax_scale;
+    if (sh->window != 64 || !hsw::vit_attn_ok(a, sh->d_qk, sh->d_v, sh->dtype, sh->out_dtype) ||
+        sh->rope_dim != sh->d_qk)
+        return fail(HSW_E_SHAPE, "vit_window_attention_rope needs window 64, bf16 in and out, d_qk = d_v = "
+                                 "rope_dim = 64 and 1, 2, 4, 8 or 16 query heads per KV head");
+    if (sh->value_scale != 1.0f) return fail(HSW_E_SHAPE, "vit_window_attention_rope has no value scale (must be 1)");
+    if (n_images < 0 || max_len < 0) return fail(HSW_E_SHAPE, "n_images and max_len must be >= 0");
+    if (max_len > 0x7fffffffLL) return fail(HSW_E_SHAPE, "max_len exceeds 2^31 - 1");
+    REQUIRE_PTR(cu_seqlens); REQUIRE_PTR(row); REQUIRE_PTR(col); REQUIRE_PTR(q); REQUIRE_PTR(k);
+    REQUIRE_PTR(v); REQUIRE_PTR(out);
+    REQUIRE_ALIGN(q, 16); REQUIRE_ALIGN(k, 16); REQUIRE_ALIGN(v, 16); REQUIRE_ALIGN(out, 16);
+    REQUIRE_ALIGN(cu_seqlens, 8); REQUIRE_ALIGN(order, 4); REQUIRE_ALIGN(sinks, 4);
+    REQUIRE_ALIGN(row, 4); REQUIRE_ALIGN(col, 4);
+    if (n_images == 0 || max_len == 0) return HSW_OK;
+    const int BQ = hsw::vit_block_tokens(sh->n_q_heads / sh->n_kv_heads);
+    if ((int64_t)n_images * sh->n_kv_heads * ((max_len + BQ - 1) / BQ) > 0x7fffffffLL)
+        return fail(HSW_E_SHAPE, "grid too large");
+    a.q = q; a.k = k; a.v = v; a.out = out; a.cu_seqlens = cu_seqlens; a.order = order; a.sinks = sinks;
+    a.n_images = n_images;
+    a.rope = 1; a.row = row; a.col = col;
+    const int quarter = sh->d_qk / 4;   // the frequencies of hsw_vit_rope_2d
+    for (int j = 0; j < quarter; ++j) a.rope_f[j] = pow(sh->rope_theta, -(double)j / (double)quarter);
+    dc::Inputs ci = check_inputs(dc::kVit, n_images);
+    ci.cu_seqlens = cu_seqlens; ci.order = order; ci.max_seqlen = max_len;
+    if ((st = device_checks(ci, (hipStream_t)stream, &a.dev_flag))) return st;
+    return launched(hsw::launch_vit_attn(a, max_len, (hipStream_t)stream), "vit_window_attention_rope");
+}
+
 }  // extern "C"

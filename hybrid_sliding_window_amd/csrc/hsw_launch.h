@@ -73,6 +73,11 @@ struct VitArgs {
     const unsigned long long *dev_flag;  // checked builds: nonzero once an argument broke the contract
     int n_images, hq, hkv, window, sink_key;
     float scale;
+    // fused 2D RoPE of q and k (window blocks): rope != 0, patch coordinates
+    // per token row, and the frequencies theta^(-j / 16), j < 16
+    int rope;
+    const int32_t *row, *col;
+    double rope_f[16];
 };
 struct VitRopeArgs {
     const void *q, *k;          // either may be null (then not rotated)

@@ -114,8 +114,9 @@ __global__ __launch_bounds__(256) void vit_rope_kernel(VitRopeArgs a) {
 // otherwise a full block (the picture in 128-key chunks, each computed as two
 // 64-key halves, two stages, the next chunk's loads in flight while one is
 // computed).
-template <int G, bool WIN>
+template <int G, bool WIN, bool ROPE = false>
 __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_kernel(VitArgs a, int nqb) {
+    static_assert(!ROPE || WIN, "the fused 2D RoPE is for window blocks");
     if (checks_failed(a.dev_flag)) return;  // (checked builds only)
     constexpr int NW = G == 1 ? 2 : 4;        // waves: 64 tokens per block at G = 1
     constexpr int NT = NW * 64;
@@ -135,6 +136,9 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     // lane order.
     __shared__ __attribute__((aligned(1024))) uint16_t ks[NSTG][KT * 16 * D];
     __shared__ __attribute__((aligned(1024))) uint16_t vs[NSTG][VH * 16 * D];
+    // ROPE: (cos, sin) of every rotary pair i < 32 of the window's 64 tokens
+    // and the sink token (slot 64), [slot][i][2]
+    __shared__ __attribute__((aligned(16))) float rtab[ROPE ? (KC + 1) * 32 * 2 : 2];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
@@ -160,6 +164,71 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     const int khi = WIN ? min(len, klo + KC) : len;
     const bool has_sink = WIN && a.sink_key && klo > 0;
     const int nch = WIN ? 1 : (len + KCS - 1) / KCS;
+
+    // ROPE: the angles of the window's tokens (slot t: position klo + t of
+    // the order, clamped into the picture as the K loads are; slot 64: the
+    // sink key at position 0).  Pair i (dims i, i + 32) turns by row * f(i)
+    // for i < 16 and by col * f(i - 16) above, formed and reduced as the
+    // 2D RoPE call does it, so the rotated bf16 q and k are the bytes that
+    // call writes.  Entry u = (slot, quarter qq) holds pairs 8 qq .. 8 qq + 7,
+    // which share one coordinate; thread tid takes entries tid + NT m.  The
+    // coordinates are loaded after q (table_coords) and the angles formed
+    // once the window's K/V loads are in flight (table_angles); the barrier
+    // before the first staging publishes them.
+    constexpr int TE = (KC + 1) * 4, TM = (TE + NT - 1) / NT;
+    int64_t tcoord[ROPE ? TM : 1];
+    auto table_coords = [&]() {
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            const int u = tid + NT * m;
+            if (u < TE) {
+                const int slot = u >> 2, qq = u & 3;
+                const int64_t t = row_of(slot < KC ? min(klo + slot, khi - 1) : 0);
+                tcoord[m] = qq < 2 ? (int64_t)a.row[t] : (int64_t)a.col[t];
+            }
+        }
+    };
+    auto table_angles = [&]() {
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            const int u = tid + NT * m;
+            if (u < TE) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 8 * (u & 3) + e;
+                    float c, sn;
+                    rope_cos_sin(tcoord[m], a.rope_f[i & 15], c, sn);
+                    rtab[2 * ((u >> 2) * 32 + i)] = c;
+                    rtab[2 * ((u >> 2) * 32 + i) + 1] = sn;
+                }
+            }
+        }
+    };
+    // ROPE: rotate a 16-byte piece of a head row of window slot `slot`:
+    // piece p < 4 holds dims 8p .. 8p+7 (the first of each pair), p >= 4 the
+    // partners 32 + 8(p - 4) ..; `other` is the partner piece.
+    auto rotate_piece = [&](u32x4 mine, u32x4 other, int p, int slot) {
+        const bool first = p < 4;
+        const u32x4 lo = first ? mine : other, hi = first ? other : mine;
+        const float *cs = &rtab[2 * (slot * 32 + 8 * (p & 3))];
+        u32x4 y;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            float yl0, yh0, yl1, yh1;
+            rope_rotate(__uint_as_float(lo[w2] << 16), __uint_as_float(hi[w2] << 16), cs[4 * w2], cs[4 * w2 + 1],
+                        yl0, yh0);
+            rope_rotate(__uint_as_float(lo[w2] & 0xffff0000u), __uint_as_float(hi[w2] & 0xffff0000u),
+                        cs[4 * w2 + 2], cs[4 * w2 + 3], yl1, yh1);
+            y[w2] = first ? pack_bf16x2(yl0, yl1) : pack_bf16x2(yh0, yh1);
+        }
+        return y;
+    };
+    auto partner = [&](const u32x4 &x) {   // the piece of lane ^ 4 (piece p ^ 4 of the same key)
+        u32x4 o;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) o[w2] = (uint32_t)__shfl_xor((int)x[w2], 4, 64);
+        return o;
+    };
 
     // q of this wave's rows: row r = 32w + 16n + col is token qb*BQ + r/G,
     // head g*G + r%G (rows past the picture read its last token, never stored)
@@ -250,6 +319,7 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
         for (int i = 0; i < LOADS; ++i) {
             int key, p;
             k_piece(i, key, p);
+            if constexpr (ROPE) kr[i] = rotate_piece(kr[i], partner(kr[i]), p, key);
             *reinterpret_cast<u32x4 *>(&ks[stg][k_unit(key, p) * 8]) = kr[i];
             v_piece(i, key, p);
             *reinterpret_cast<u32x4 *>(&vs[stg][v_unit(key, p) * 4]) = f16 ? to_f16(vr[i]) : vr[i];
@@ -265,6 +335,7 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     // First chunk (and, in a window after the first, the sink key: slot 64 =
     // the picture's first token in the block's order; slots 65..79 of K and
     // 65..95 of V zero).
+    if constexpr (ROPE) table_coords();
     u32x4 sk = u32x4{0, 0, 0, 0}, svv = u32x4{0, 0, 0, 0};
     if (has_sink && tid < 8) {
         const int64_t r0 = row_of(0);
@@ -272,7 +343,23 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
         svv = ld16(vg + r0 * rs + 8 * tid);
     }
     fetch(0);
+    if constexpr (ROPE) table_angles();
     bool f16 = !__syncthreads_or(chunk_big(has_sink && tid < 8 && v_big(svv)));
+    if constexpr (ROPE) {
+        // q: lane (quad, col) holds dims 8 quad .. (step 0) and their
+        // partners 32 + 8 quad .. (step 1) of its rows' tokens
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int r = 32 * w + 16 * n + col;
+            const int slot = min(qb * BQ + r / G, len - 1) - klo;
+            const u32x4 lo = qv[n][0];
+            qv[n][0] = rotate_piece(lo, qv[n][1], quad, slot);
+            qv[n][1] = rotate_piece(qv[n][1], lo, quad + 4, slot);
+        }
+        // the sink key's pieces (threads 0..7 of wave 0, piece tid)
+        const u32x4 sko = partner(sk);
+        if (has_sink && tid < 8) sk = rotate_piece(sk, sko, tid, KC);
+    }
     put(0, f16);
     if (WIN && has_sink) {
         for (int pi = tid; pi < 32 * 8; pi += NT) {
@@ -561,7 +648,15 @@ hipError_t launch_vit_attn(const VitArgs &a, int64_t max_len, hipStream_t s) {
     const int BQ = vit_block_tokens(G);
     const int nqb = (int)((max_len + BQ - 1) / BQ);
     dim3 grid((unsigned)((int64_t)a.n_images * a.hkv * nqb));
-    if (a.window > 0) {
+    if (a.rope) {   // window blocks only (the caller checks)
+        switch (G) {
+            case 1: hipLaunchKernelGGL((vit_attn_kernel<1, true, true>), grid, dim3(128), 0, s, a, nqb); break;
+            case 2: hipLaunchKernelGGL((vit_attn_kernel<2, true, true>), grid, dim3(256), 0, s, a, nqb); break;
+            case 4: hipLaunchKernelGGL((vit_attn_kernel<4, true, true>), grid, dim3(256), 0, s, a, nqb); break;
+            case 8: hipLaunchKernelGGL((vit_attn_kernel<8, true, true>), grid, dim3(256), 0, s, a, nqb); break;
+            default: hipLaunchKernelGGL((vit_attn_kernel<16, true, true>), grid, dim3(256), 0, s, a, nqb); break;
+        }
+    } else if (a.window > 0) {
         switch (G) {
             case 1: hipLaunchKernelGGL((vit_attn_kernel<1, true>), grid, dim3(128), 0, s, a, nqb); break;
             case 2: hipLaunchKernelGGL((vit_attn_kernel<2, true>), grid, dim3(256), 0, s, a, nqb); break;

@@ -94,6 +94,7 @@ def _load() -> ctypes.CDLL:
     lib.hsw_vit_layout.argtypes = [I32, I32, P, P, P]
     lib.hsw_vit_rope_2d.argtypes = [SH, I64, P, P, P, P, P, P, P]
     lib.hsw_vit_attention.argtypes = [SH, I32, I64, P, P, I32, P, P, P, P, P, P]
+    lib.hsw_vit_window_attention_rope.argtypes = [SH, I32, I64, P, P, I32, P, P, P, P, P, P, P, P]
     lib.hsw_kv_bytes.restype = I64
     KC = ctypes.POINTER(KvmConfig)
     PI32, PI64, PP = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(P)
@@ -121,7 +122,7 @@ def _load() -> ctypes.CDLL:
               "hsw_swa_decode_qrope", "hsw_full_decode_splitk", "hsw_full_decode_splitk_noalloc",
               "hsw_full_prefill_chunk",
               "hsw_full_decode_splitk_qrope", "hsw_full_prefill_chunk_qrope", "hsw_vit_layout",
-              "hsw_vit_rope_2d", "hsw_vit_attention"):
+              "hsw_vit_rope_2d", "hsw_vit_attention", "hsw_vit_window_attention_rope"):
         getattr(lib, f).restype = I32
     return lib
 
@@ -138,7 +139,7 @@ EXPORTED = ("hsw_status_str", "hsw_last_error", "hsw_version", "hsw_device_check
             "hsw_kvm_snapshot_bytes", "hsw_kvm_create", "hsw_kvm_destroy", "hsw_kvm_admit", "hsw_kvm_release",
             "hsw_kvm_append", "hsw_kvm_truncate", "hsw_kvm_info", "hsw_kvm_free_space", "hsw_kvm_snapshot",
             "hsw_kvm_restore", "hsw_kvm_drop_snapshot", "hsw_kvm_window_safe_length",
-            "hsw_vit_layout", "hsw_vit_rope_2d", "hsw_vit_attention")
+            "hsw_vit_layout", "hsw_vit_rope_2d", "hsw_vit_attention", "hsw_vit_window_attention_rope")
 
 
 def _ptr(t):
@@ -395,3 +396,11 @@ def hsw_vit_attention(shape, n_images, max_len, cu_seqlens, order, sink_key, q, 
     _check(lib.hsw_vit_attention(_sh(shape), int(n_images), int(max_len), _ptr(cu_seqlens), _ptr(order),
                                  int(sink_key), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out),
                                  _stream(stream)), "hsw_vit_attention")
+
+
+def hsw_vit_window_attention_rope(shape, n_images, max_len, cu_seqlens, order, sink_key, row, col, q, k, v,
+                                  sinks, out, stream=None):
+    _check(lib.hsw_vit_window_attention_rope(_sh(shape), int(n_images), int(max_len), _ptr(cu_seqlens),
+                                             _ptr(order), int(sink_key), _ptr(row), _ptr(col), _ptr(q), _ptr(k),
+                                             _ptr(v), _ptr(sinks), _ptr(out), _stream(stream)),
+           "hsw_vit_window_attention_rope")

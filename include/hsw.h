@@ -547,6 +547,30 @@ hsw_status hsw_vit_attention(const hsw_attn_shape *sh, int32_t n_images, int64_t
                              const int64_t *cu_seqlens, const int32_t *order, int32_t sink_key, const void *q,
                              const void *k, const void *v, const float *sinks, void *out, hsw_stream_t stream);
 
+/*
+ * A ViT window block with its 2D RoPE fused: hsw_vit_rope_2d of q and k
+ * (rope_theta of sh, row and col as there) followed by hsw_vit_attention with
+ * window 64, in one call that reads the unrotated q and k and writes only
+ * out -- no rotated copy of q or k goes through memory.  Follows colibri
+ * "MiMo-V2.6 (Xiaomi)", the model description's "vision" entry (2D RoPE;
+ * 64-token windows with a sink on the first key), read as for the two calls
+ * it joins.  Each workgroup forms the angles of its window's tokens once and
+ * rotates with the 2D RoPE call's own arithmetic, so out is bit-identical to
+ * the two calls made in turn.
+ *   Arguments as hsw_vit_attention, with q [T][Hq][64] and k [T][Hkv][64]
+ *   unrotated, and row, col [T] int32 patch coordinates by token row
+ *   (hsw_vit_layout).  Requires sh->window == 64 and d_qk == d_v ==
+ *   rope_dim == 64 (HSW_E_SHAPE otherwise); full blocks (window 0) rotate
+ *   once with hsw_vit_rope_2d instead, since every query block of a picture
+ *   reads every key.
+ * Errors: HSW_E_NULL (cu_seqlens, row, col, q, k, v, out), HSW_E_SHAPE,
+ * HSW_E_ALIGN (q, k, v, out 16 B; cu_seqlens 8 B; order, sinks, row, col 4 B).
+ */
+hsw_status hsw_vit_window_attention_rope(const hsw_attn_shape *sh, int32_t n_images, int64_t max_len,
+                                         const int64_t *cu_seqlens, const int32_t *order, int32_t sink_key,
+                                         const int32_t *row, const int32_t *col, const void *q, const void *k,
+                                         const void *v, const float *sinks, void *out, hsw_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,6 +102,19 @@ def test_rope_k_only_staging_contract():
                **{**args, "dst_kind": kind, "seq": FAKE, "seq_base": FAKE})
 
 
+def test_vit_window_attention_rope_argument_errors():
+    """Window 64 only (full blocks rotate once with the 2D RoPE call), the
+    coordinates required, nothing launched on an error or an empty call."""
+    sh = wl.vit_shape(16, 4, 64)
+    args = (1, 64, FAKE, None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    hsw.hsw_vit_window_attention_rope(sh, 0, 64, FAKE, None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)  # empty
+    expect(2, hsw.hsw_vit_window_attention_rope, wl.vit_shape(16, 4, 0), *args)           # full block
+    expect(1, hsw.hsw_vit_window_attention_rope, sh, 1, 64, FAKE, None, 1, None, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    expect(1, hsw.hsw_vit_window_attention_rope, sh, 1, 64, FAKE, None, 1, FAKE, None, FAKE, FAKE, FAKE, None, FAKE)
+    expect(3, hsw.hsw_vit_window_attention_rope, sh, 1, 64, FAKE, None, 1, FAKE + 2, FAKE, FAKE, FAKE, FAKE, None,
+           FAKE)                                                                               # row misaligned
+
+
 def test_attention_argument_errors():
     sh, fs = swa(), full()
     expect(2, hsw.hsw_swa_prefill, fs, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)

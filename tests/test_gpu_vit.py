@@ -275,3 +275,68 @@ def test_vit_attention_clamps_out_of_range_order_entries():
     sel = np.array([pos[int(r)] for r in once])
     ma, mr = assert_close(f64(out)[once], ref[sel], what="vit_attention clamped order")
     print(f"vit_attention clamped order ({len(once)} tokens checked): max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+# ------------------------------------------------ fused 2D RoPE (window blocks)
+def run_window_rope(batch, shape, row, col, order=None, sink_key=True):
+    T = batch["q"].shape[0]
+    out = torch.full((T, shape.n_q_heads, 64), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    od = None if order is None else torch.from_numpy(order).to(DEV)
+    hsw.hsw_vit_window_attention_rope(shape, len(batch["lens"]), max(batch["lens"]), dev(batch["cu_seqlens"]), od,
+                                      int(sink_key), torch.from_numpy(row).to(DEV), torch.from_numpy(col).to(DEV),
+                                      dev(batch["q"]), dev(batch["k"]), dev(batch["v"]), dev(batch["sinks"]), out)
+    torch.cuda.synchronize()
+    return out
+
+
+def rotated(batch, shape, row, col):
+    q, k = dev(batch["q"]), dev(batch["k"])
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    hsw.hsw_vit_rope_2d(shape, q.shape[0], q, k, torch.from_numpy(row).to(DEV), torch.from_numpy(col).to(DEV),
+                        qr, kr)
+    return qr, kr
+
+
+@pytest.mark.parametrize("case", ["col_sinkkey", "row_sinkkey", "col_learned_sinks"])
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (16, 16), (16, 8), (16, 2), (16, 1)])
+def test_vit_window_attention_rope_bitwise_equals_rope_then_attention(case, hq, hkv):
+    """The fused call forms each window token's angles and rotates q and k
+    with the 2D RoPE call's own arithmetic: its output is byte-identical to
+    hsw_vit_rope_2d then hsw_vit_attention (window 64), for every group size,
+    both orders, the sink key or learned sinks, and pictures whose last
+    window is partial; and it is held to the oracle fed the rotated bf16
+    tensors (the bytes both paths attend over)."""
+    note(f"vit window rope fused {case} {hq}/{hkv}")
+    grids = [wl.VIT_PAGE_GRID, (8, 6), (2, 2), (2, 66), (16, 10)]   # 1008, 48, 4, 132, 160 tokens
+    learned = case.endswith("learned_sinks")
+    b = wl.vit_batch(seed=41, grids=grids, hq=hq, hkv=hkv, with_sinks=learned)
+    shape = wl.vit_shape(hq, hkv, 64)
+    row, col, order = layouts(grids, lib=True)
+    use_col = case.startswith("col")
+    sink_key = case.endswith("sinkkey")
+    qr, kr = rotated(b, shape, row, col)
+    out_u = run_attention(b, shape, order if use_col else None, sink_key, q=qr, k=kr)
+    out_f = run_window_rope(b, shape, row, col, order if use_col else None, sink_key)
+    assert torch.equal(out_f, out_u), "fused window attention differs from RoPE + attention"
+    oorder = layouts(grids, lib=False)[2] if use_col else None
+    idx, ref = oracle_attention(b, shape, oorder, sink_key, q=qr.cpu(), k=kr.cpu())
+    ma, mr = assert_close(f64(out_f)[idx], ref, what=f"vit window rope fused {case} {hq}/{hkv}")
+    print(f"vit window rope fused {case} {hq}/{hkv}: bitwise equal; max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_vit_window_attention_rope_full_size():
+    """The bench workload (16 pictures of 64 x 64 patches, column order, the
+    sink key): the fused call byte-identical to the two calls, and sampled
+    windows held to the oracle."""
+    note("vit window rope fused, 16 x 4096 tokens")
+    grids = wl.VIT_BENCH_GRIDS
+    b = wl.vit_batch(seed=42, grids=grids)
+    shape = wl.vit_shape()
+    row, col, order = layouts(grids, lib=True)
+    qr, kr = rotated(b, shape, row, col)
+    out_u = run_attention(b, shape, order, True, q=qr, k=kr)
+    out_f = run_window_rope(b, shape, row, col, order, True)
+    assert torch.equal(out_f, out_u)
+    oorder = layouts(grids, lib=False)[2]
+    idx, ref = oracle_attention(b, shape, oorder, True, q=qr.cpu(), k=kr.cpu(), pictures=[0, 15])
+    assert_close(f64(out_f)[idx], ref, what="vit window rope fused full size")
