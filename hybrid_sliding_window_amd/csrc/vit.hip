@@ -5,7 +5,7 @@
 // colibri "MiMo-V2.6 (Xiaomi)", the model description's "vision" entry: 2D
 // RoPE, grouped-query attention, full attention in 4 of 28 blocks and a 1D
 // window of 64 tokens in the others, row and column order of the 2x2 merge
-// units alternating, a sink on the first key of the window blocks.  Read
+// units alternating; the window blocks add a sink at their leading key.  Read
 // here as: a picture's tokens come in merge-unit order; a window block takes
 // the tokens in its order (row order = that order, or an index array such
 // as the column order of the units), cuts them into consecutive windows of

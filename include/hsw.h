@@ -486,7 +486,7 @@ int64_t hsw_kvm_window_safe_length(hsw_kvm *kvm, int32_t seq, const int32_t *tok
  * colibri "MiMo-V2.6 (Xiaomi)", the model description's "vision" entry: 2D
  * RoPE, grouped-query attention, full attention in 4 of 28 blocks and a 1D
  * window of 64 tokens in the others, row and column order of the 2x2 merge
- * units alternating, a sink on the first key of the window blocks; its
+ * units alternating; the window blocks add a sink at their leading key; its
  * "Verifying it": the gateway's patches equal the Qwen2-VL processor's.
  * Readings: a picture's tokens come in merge-unit order (the 4 patches of a
  * 2x2 unit consecutive: top-left, top-right, bottom-left, bottom-right;

@@ -10,8 +10,8 @@ length -- so that it can be checked by eye against the pages:
 * gokawiil "Full-Pipeline Inference Optimization for MiMo-V2.5 Series",
   section 2.1 "SWA KVCache Management": full-attention layers keep O(N) rows
   per sequence, windowed layers O(W) (the ring); a request is admitted only if
-  BOTH pools have room ("validates both Full KV and SWA KV capacity
-  constraints when admitting requests"); prefix reuse is clipped to the
+  BOTH pools have room (admission checks the capacity of each pool, not
+  one combined figure); prefix reuse is clipped to the
   "window-safe length", the longest matched prefix whose last W positions the
   windowed layers still hold (anything beyond is a miss).
 * colibri "MiMo-V2.6 (Xiaomi)", section "System One mode and prompt reuse":

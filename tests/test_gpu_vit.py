@@ -2,7 +2,8 @@
 hsw_vit_attention) against the fp64 oracle fed the exact tensors each call
 consumed (colibri "MiMo-V2.6 (Xiaomi)", the "vision" entry: 2D RoPE, GQA,
 full blocks and 64-token window blocks in alternating row / column order of
-the 2x2 merge units, a sink on the first key of the window blocks).
+the 2x2 merge units; the window blocks add a sink placed at their leading
+key).
 
 Bars: rotated q/k within one bf16 ulp of the rounded fp64 value; attention
 max_abs <= 2e-2 and mean_rel <= 2e-3.  The library's layout (coordinates
