@@ -177,14 +177,14 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     // before the first staging publishes them.
     constexpr int TE = (KC + 1) * 4, TM = (TE + NT - 1) / NT;
     int64_t tcoord[ROPE ? TM : 1];
+    int tq[2], tkv[WIN ? LOADS : 1], tsk = 0, ttab[ROPE ? TM : 1];   // tokens by order position, below
     auto table_coords = [&]() {
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
             const int u = tid + NT * m;
             if (u < TE) {
-                const int slot = u >> 2, qq = u & 3;
-                const int64_t t = row_of(slot < KC ? min(klo + slot, khi - 1) : 0);
-                tcoord[m] = qq < 2 ? (int64_t)a.row[t] : (int64_t)a.col[t];
+                const int64_t t = tok0 + ttab[m];
+                tcoord[m] = (u & 3) < 2 ? (int64_t)a.row[t] : (int64_t)a.col[t];
             }
         }
     };
@@ -230,19 +230,6 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
         return o;
     };
 
-    // q of this wave's rows: row r = 32w + 16n + col is token qb*BQ + r/G,
-    // head g*G + r%G (rows past the picture read its last token, never stored)
-    u32x4 qv[2][STEPS];
-    const uint16_t *qg = (const uint16_t *)a.q;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int r = 32 * w + 16 * n + col;
-        const int j = min(qb * BQ + r / G, len - 1);
-        const uint16_t *qrow = qg + (row_of(j) * a.hq + g * G + r % G) * (int64_t)D;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
-    }
-
     const uint16_t *kg = (const uint16_t *)a.k + g * D;
     const uint16_t *vg = (const uint16_t *)a.v + g * D;
     const int64_t rs = (int64_t)a.hkv * D;   // elements per token row of k / v
@@ -277,13 +264,81 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
             p = 2 * (lane >> 4) + (lane & 1);
         }
     };
+    // The block's tokens by order position, every lookup issued before any
+    // is used: with an index array, a lookup whose row feeds a load at once
+    // makes the compiler wait for every load in flight after each one, so
+    // the block's q, K/V, sink and table loads would each wait a memory
+    // latency behind the one before.  tq: q / output rows (n = 0, 1);
+    // window blocks: tkv the K/V pieces of the window, tsk the sink (order
+    // position 0), ttab the RoPE table's entries (declared with tcoord).
+    {
+        int jq[2], jkv[WIN ? LOADS : 1], jt[ROPE ? TM : 1];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) jq[n] = min(qb * BQ + (32 * w + 16 * n + col) / G, len - 1);
+        if constexpr (WIN) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                int key, p;
+                k_piece(i, key, p);
+                jkv[i] = min(klo + key, khi - 1);
+            }
+        }
+        if constexpr (ROPE) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+                const int u = tid + NT * m, slot = u >> 2;
+                jt[m] = u < TE && slot < KC ? min(klo + slot, khi - 1) : 0;
+            }
+        }
+        auto clampt = [&](int t) { return min(max(t, 0), len - 1); };
+        if (ord) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) tq[n] = ord[jq[n]];
+            if constexpr (WIN) {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) tkv[i] = ord[jkv[i]];
+                tsk = ord[0];
+            }
+            if constexpr (ROPE) {
+#pragma unroll
+                for (int m = 0; m < TM; ++m) ttab[m] = ord[jt[m]];
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) tq[n] = clampt(tq[n]);
+#pragma unroll
+            for (int i = 0; i < (WIN ? LOADS : 0); ++i) tkv[i] = clampt(tkv[i]);
+            tsk = clampt(tsk);
+#pragma unroll
+            for (int m = 0; m < (ROPE ? TM : 0); ++m) ttab[m] = clampt(ttab[m]);
+        } else {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) tq[n] = jq[n];
+#pragma unroll
+            for (int i = 0; i < (WIN ? LOADS : 0); ++i) tkv[i] = jkv[i];
+#pragma unroll
+            for (int m = 0; m < (ROPE ? TM : 0); ++m) ttab[m] = jt[m];
+        }
+    }
+
+    // q of this wave's rows: row r = 32w + 16n + col is token qb*BQ + r/G,
+    // head g*G + r%G (rows past the picture read its last token, never stored)
+    u32x4 qv[2][STEPS];
+    const uint16_t *qg = (const uint16_t *)a.q;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int r = 32 * w + 16 * n + col;
+        const uint16_t *qrow = qg + ((tok0 + tq[n]) * a.hq + g * G + r % G) * (int64_t)D;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) qv[n][st] = ld16(qrow + 32 * st + 8 * quad);
+    }
+
     u32x4 kr[LOADS], vr[LOADS];
     auto fetch = [&](int c) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             int key, p;
             k_piece(i, key, p);
-            const int64_t r = row_of(min(klo + c * KCS + key, khi - 1));
+            const int64_t r = WIN ? tok0 + tkv[i] : row_of(min(klo + c * KCS + key, khi - 1));
             kr[i] = ld16(kg + r * rs + 8 * p);
             if constexpr (WIN) {
                 vr[i] = ld16(vg + r * rs + 8 * p);  // the same piece of V: one lookup of the order
@@ -338,7 +393,7 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     if constexpr (ROPE) table_coords();
     u32x4 sk = u32x4{0, 0, 0, 0}, svv = u32x4{0, 0, 0, 0};
     if (has_sink && tid < 8) {
-        const int64_t r0 = row_of(0);
+        const int64_t r0 = tok0 + tsk;
         sk = ld16(kg + r0 * rs + 8 * tid);
         svv = ld16(vg + r0 * rs + 8 * tid);
     }
@@ -622,7 +677,7 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
         }
         const float sc = fac / ll;
         if (j < len) {
-            uint16_t *orow = og + (row_of(j) * a.hq + g * G + head) * (int64_t)D;
+            uint16_t *orow = og + ((tok0 + tq[n]) * a.hq + g * G + head) * (int64_t)D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const f32x4 o = oacc[n][dt];
