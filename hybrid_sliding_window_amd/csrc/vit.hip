@@ -176,16 +176,18 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
     // once the window's K/V loads are in flight (table_angles); the barrier
     // before the first staging publishes them.
     constexpr int TE = (KC + 1) * 4, TM = (TE + NT - 1) / NT;
-    int64_t tcoord[ROPE ? TM : 1];
+    int32_t tcoord[ROPE ? TM : 1];   // (32-bit until used: no wait where it lands)
     int tq[2], tkv[WIN ? LOADS : 1], tsk = 0, ttab[ROPE ? TM : 1];   // tokens by order position, below
+    const int32_t *rowp = a.row, *colp = a.col;
     auto table_coords = [&]() {
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
-            const int u = tid + NT * m;
-            if (u < TE) {
-                const int64_t t = tok0 + ttab[m];
-                tcoord[m] = (u & 3) < 2 ? (int64_t)a.row[t] : (int64_t)a.col[t];
-            }
+            // (every thread loads, entries past the table too (token 0 of the
+            // order): a load under a branch is waited for where the branch
+            // ends; the array is picked as a value, since a pick between two
+            // fields of the argument block loads the pointer per lane first)
+            const int32_t *coords = ((tid + NT * m) & 3) < 2 ? rowp : colp;
+            tcoord[m] = coords[tok0 + ttab[m]];
         }
     };
     auto table_angles = [&]() {
@@ -196,8 +198,13 @@ __global__ __launch_bounds__((G == 1 ? 2 : 4) * 64, WIN ? 4 : 2) void vit_attn_k
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int i = 8 * (u & 3) + e;
+                    // f(i & 15) = f(8 (u & 1) + e): a pick between two
+                    // values the whole workgroup shares (an index per lane
+                    // would load from the argument block per lane, behind
+                    // the K/V loads)
+                    const double f_lo = a.rope_f[e], f_hi = a.rope_f[8 + e];
                     float c, sn;
-                    rope_cos_sin(tcoord[m], a.rope_f[i & 15], c, sn);
+                    rope_cos_sin((int64_t)tcoord[m], (u & 1) ? f_hi : f_lo, c, sn);
                     rtab[2 * ((u >> 2) * 32 + i)] = c;
                     rtab[2 * ((u >> 2) * 32 + i) + 1] = sn;
                 }
