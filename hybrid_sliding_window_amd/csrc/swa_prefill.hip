@@ -764,7 +764,9 @@ __global__ __launch_bounds__(kThreads, 1) void swa_sweep_kernel(AttnArgs a, int 
             const int rq = (32 * w + 4 * i) / G;
             if (b * BQ + rq < len) {
                 uint16_t *ob = obase + (int64_t)(b * BQ + rq) * a.hq * DV;
-                st16(ob + (uint32_t)((((4 * i) % G) + (lane >> 4)) * DV + 8 * (lane & 15)), v[i]);
+                // (non-temporal: nothing here reads the output again)
+                __builtin_nontemporal_store(
+                    v[i], reinterpret_cast<u32x4 *>(ob + (uint32_t)((((4 * i) % G) + (lane >> 4)) * DV + 8 * (lane & 15))));
             }
         }
     };
