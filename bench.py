@@ -60,7 +60,7 @@ MEASURED_TRAFFIC = {
     "swa_prefill": (1556.1e6, ("swa_prefill.hip", "generic_attn.hip", "hsw_device.h"), "f92dff93c81c05b1"),
     "swa_decode": (178.46e6, ("swa_decode.hip", "hsw_device.h"), "896eeabc5cd54b5f"),
     # ViT window block: 201.8 MB read, 134.2 MB written
-    "vit_window": (336.6e6, ("vit.hip", "hsw_device.h"), "cad8d173df28eb36"),
+    "vit_window": (336.6e6, ("vit.hip", "hsw_device.h"), "5d83105600c1bde9"),
 }
 
 

@@ -105,8 +105,10 @@ __global__ __launch_bounds__(256) void vit_rope_kernel(VitRopeArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) rope_cos_sin(coord, a.inv_freq[f0 + e], c[e], s[e]);
     rope_rotate_bf16x8(lo, hi, c, s);
-    st16(y + 8 * p, lo);
-    st16(y + half + 8 * p, hi);
+    // (non-temporal: the rotated q and k of a whole batch of pictures are
+    // larger than the last-level cache, so keeping them there buys nothing)
+    __builtin_nontemporal_store(lo, reinterpret_cast<u32x4 *>(y + 8 * p));
+    __builtin_nontemporal_store(hi, reinterpret_cast<u32x4 *>(y + half + 8 * p));
 }
 
 // -------------------------------------------------------------- attention
